@@ -1,0 +1,244 @@
+"""Masked-set attention, forward and backward, in float64 (oracle; test
+infrastructure only).
+
+Definition: "Story of Attention -- Part 4: Sparse Attention, Then and Now",
+section 1 (Sparse Transformer), the sparse-attention formula: for query i and
+its permitted key set S_i,
+
+    out_i = sum_{j in S_i} exp(q_i . k_j / sqrt(d_k)) / sum_{m in S_i} exp(q_i . k_m / sqrt(d_k)) * v_j
+
+i.e. ordinary attention whose softmax runs only over S_i.  SPAttention
+("Making Every Head Count", Figure 1 caption and abstract) gives head h the
+set S_i^h = { j : 0 <= j <= i, lo_h <= i - j <= hi_h }, one contiguous band of
+causal distances per head.
+
+Readings (pages silent): an empty S_i gives output 0 and LSE = -inf;
+LSE_i = ln sum_{j in S_i} exp(scaled score); the backward pass is the
+textbook derivative of the formula (D_i = dO_i . O_i, dS = P * (dP - D)).
+
+Three independent forms are kept so the tests can cross-check them:
+
+* ``masked_attention_literal`` -- a per-element Python loop over S_i, written
+  exactly as the formula reads (tiny shapes only);
+* ``masked_attention_dense`` / ``masked_attention_dense_bwd`` -- one head, a
+  full N x N score matrix with an explicit boolean mask;
+* ``band_attention_fwd`` / ``band_attention_bwd`` -- all of [B, H, N, d], per
+  (b, h) and per block of query rows, gathering only the key rows the band can
+  reach and masking element by element.  Used at full workload sizes.
+"""
+import math
+
+import numpy as np
+
+QUERY_BLOCK = 256
+
+
+def _default_scale(d, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def masked_attention_literal(q, k, v, allowed, scale=None):
+    """One head.  q, k: [N, d]; v: [N, dv]; allowed(i, j) -> bool.
+
+    Returns (out [N, dv], lse [N]).  Every sum is written out term by term.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape
+    dv = v.shape[1]
+    sc = _default_scale(d, scale)
+    out = np.zeros((n, dv))
+    lse = np.full(n, -np.inf)
+    for i in range(n):
+        s_i = [j for j in range(k.shape[0]) if allowed(i, j)]
+        if not s_i:
+            continue
+        scores = {}
+        for j in s_i:
+            dot = 0.0
+            for c in range(d):
+                dot += q[i, c] * k[j, c]
+            scores[j] = dot * sc
+        denom = 0.0
+        for m in s_i:
+            denom += math.exp(scores[m])
+        for j in s_i:
+            w = math.exp(scores[j]) / denom
+            for c in range(dv):
+                out[i, c] += w * v[j, c]
+        lse[i] = math.log(denom)
+    return out, lse
+
+
+def band_mask(n_q, n_k, lo, hi):
+    """Boolean [n_q, n_k] mask of head (lo, hi): j <= i and lo <= i - j <= hi."""
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    dist = i - j
+    return (j <= i) & (dist >= lo) & (dist <= hi)
+
+
+def masked_attention_dense(q, k, v, mask, scale=None):
+    """One head with an explicit [N, N] boolean mask.  Returns (out, lse, p)
+    where p is the [N, N] probability matrix (0 off the mask)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    sc = _default_scale(q.shape[1], scale)
+    s = (q @ k.T) * sc
+    s = np.where(mask, s, -np.inf)
+    row_max = s.max(axis=1)
+    nonempty = mask.any(axis=1)
+    shift = np.where(nonempty, row_max, 0.0)
+    e = np.where(mask, np.exp(s - shift[:, None]), 0.0)
+    denom = e.sum(axis=1)
+    safe = np.where(nonempty, denom, 1.0)
+    p = e / safe[:, None]
+    out = p @ v
+    lse = np.where(nonempty, shift + np.log(safe), -np.inf)
+    return out, lse, p
+
+
+def masked_attention_dense_bwd(q, k, v, dout, mask, scale=None):
+    """Textbook gradient of ``masked_attention_dense`` for one head.
+
+    Returns (dq, dk, dv).  P is recomputed here; D_i = dO_i . O_i uses the
+    float64 forward output of this same function.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    sc = _default_scale(q.shape[1], scale)
+    out, _, p = masked_attention_dense(q, k, v, mask, sc)
+    dv = p.T @ dout
+    dp = dout @ v.T
+    dcoef = (dout * out).sum(axis=1)
+    ds = p * (dp - dcoef[:, None])
+    dq = sc * (ds @ k)
+    dk = sc * (ds.T @ q)
+    return dq, dk, dv
+
+
+def _key_range(i0, i1, lo, hi):
+    """Keys a block of query rows [i0, i1) can reach in band [lo, hi]:
+    j from max(0, i0 - hi) to (i1 - 1) - lo inclusive (empty if it ends < 0)."""
+    return max(0, i0 - hi), (i1 - 1) - lo
+
+
+def _block_forward(qb, kb, vb, i0, j0, lo, hi, sc):
+    """Forward on one query block against the gathered key rows."""
+    n_q, n_k = qb.shape[0], kb.shape[0]
+    i = (i0 + np.arange(n_q))[:, None]
+    j = (j0 + np.arange(n_k))[None, :]
+    dist = i - j
+    mask = (dist >= max(lo, 0)) & (dist <= hi)
+    s = np.where(mask, (qb @ kb.T) * sc, -np.inf)
+    nonempty = mask.any(axis=1)
+    shift = np.where(nonempty, s.max(axis=1), 0.0)
+    e = np.where(mask, np.exp(s - shift[:, None]), 0.0)
+    denom = e.sum(axis=1)
+    safe = np.where(nonempty, denom, 1.0)
+    p = e / safe[:, None]
+    out = p @ vb
+    lse = np.where(nonempty, shift + np.log(safe), -np.inf)
+    return out, lse, p
+
+
+def band_attention_fwd(q, k, v, lo, hi, scale=None, heads=None):
+    """Band attention over [B, H, N, d] inputs.
+
+    lo, hi: per-head inclusive distance bounds (length H).  Returns
+    (out [B, H, N, dv] float64, lse [B, H, N] float64).  ``heads`` optionally
+    restricts the work to a subset of head indices (others are left 0/-inf).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, d = q.shape
+    sc = _default_scale(d, scale)
+    out = np.zeros(q.shape[:3] + (v.shape[3],))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in (range(H) if heads is None else heads):
+            l, u = int(lo[h]), int(hi[h])
+            if u < l:
+                continue
+            for i0 in range(0, N, QUERY_BLOCK):
+                i1 = min(N, i0 + QUERY_BLOCK)
+                j0, j1 = _key_range(i0, i1, l, u)
+                if j1 < j0:
+                    continue
+                o_blk, l_blk, _ = _block_forward(q[b, h, i0:i1], k[b, h, j0:j1 + 1],
+                                                 v[b, h, j0:j1 + 1], i0, j0, l, u, sc)
+                out[b, h, i0:i1] = o_blk
+                lse[b, h, i0:i1] = l_blk
+    return out, lse
+
+
+def band_attention_fwd_rows(q, k, v, lo, hi, b, h, rows, scale=None):
+    """Forward for selected query rows of one (b, h) only -- each row is
+    computed on its own from the definition.  Returns (out [len(rows), dv],
+    lse [len(rows)]).  Used to check sampled outputs at full sizes."""
+    d = q.shape[3]
+    sc = _default_scale(d, scale)
+    l, u = int(lo[h]), int(hi[h])
+    outs = np.zeros((len(rows), v.shape[3]))
+    lses = np.full(len(rows), -np.inf)
+    for r, i in enumerate(rows):
+        j0, j1 = _key_range(i, i + 1, l, u)
+        if u < l or j1 < j0:
+            continue
+        qb = np.asarray(q[b, h, i:i + 1], dtype=np.float64)
+        kb = np.asarray(k[b, h, j0:j1 + 1], dtype=np.float64)
+        vb = np.asarray(v[b, h, j0:j1 + 1], dtype=np.float64)
+        o_blk, l_blk, _ = _block_forward(qb, kb, vb, i, j0, l, u, sc)
+        outs[r] = o_blk[0]
+        lses[r] = l_blk[0]
+    return outs, lses
+
+
+def band_attention_bwd(q, k, v, dout, lo, hi, scale=None):
+    """Gradients of band attention over [B, H, N, d].
+
+    Recomputes the forward in float64 per query block, then per block:
+    dV_J += P^T dO, dP = dO V_J^T, dS = P * (dP - D) with D_i = dO_i . O_i,
+    dQ = scale * dS K_J, dK_J += scale * dS^T Q.  Rows with an empty key set
+    have P = 0 and contribute nothing.  Returns (dq, dk, dv, out, lse).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, H, N, d = q.shape
+    sc = _default_scale(d, scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    out = np.zeros(q.shape[:3] + (v.shape[3],))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            l, u = int(lo[h]), int(hi[h])
+            if u < l:
+                continue
+            for i0 in range(0, N, QUERY_BLOCK):
+                i1 = min(N, i0 + QUERY_BLOCK)
+                j0, j1 = _key_range(i0, i1, l, u)
+                if j1 < j0:
+                    continue
+                qb = q[b, h, i0:i1]
+                kb = k[b, h, j0:j1 + 1]
+                vb = v[b, h, j0:j1 + 1]
+                dob = dout[b, h, i0:i1]
+                o_blk, l_blk, p = _block_forward(qb, kb, vb, i0, j0, l, u, sc)
+                out[b, h, i0:i1] = o_blk
+                lse[b, h, i0:i1] = l_blk
+                dcoef = (dob * o_blk).sum(axis=1)
+                dv[b, h, j0:j1 + 1] += p.T @ dob
+                dp = dob @ vb.T
+                ds = p * (dp - dcoef[:, None])
+                dq[b, h, i0:i1] = sc * (ds @ kb)
+                dk[b, h, j0:j1 + 1] += sc * (ds.T @ qb)
+    return dq, dk, dv, out, lse
