@@ -1,0 +1,185 @@
+"""Benchmark of band-partitioned (SPAttention) attention on one MI355X.
+
+One step = the whole hot path over one batch: spattn_fwd (band table, band
+tile schedule, scores, masks, online softmax, P V, epilogue) followed by
+spattn_bwd (D = rowsum(dO * O), band-tiled dK / dV / dQ, dQ finalize), on
+B = 8, H = 16, N = 4096, d = 128, bfloat16 inputs resident in HBM.
+
+Prints ONE JSON line.  ``value`` is in-band TFLOP/s of fwd+bwd (14 d FLOP per
+attended pair; the heads together attend N(N+1)/2 pairs per sequence).
+Extra keys report the forward alone, the dense-causal kernel of the same
+library at the same shape, the roofline of the dominant kernel and the
+float64 CPU oracle timed on this host.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+B, H, N, D = 8, 16, 4096, 128
+SEED = 1005
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+
+
+def pairs_total(lo, hi):
+    tot = 0
+    for l, u in zip(lo, hi):
+        l, u = int(l), int(u)
+        if u >= l:
+            w = u - l + 1
+            tot += w * (2 * N - l - u) // 2
+    return tot * B
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal comparison")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the band kernels shard over "
+              "(batch, head) with no communication, so multi-GPU throughput is not measured here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from structured_sparse_attention_spattn_amd import ops
+    from structured_sparse_attention_spattn_amd.inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+    inp = make_inputs(B, H, N, D, dtype="bf16", seed=SEED, with_dout=True)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    lo, hi = ops.band_table(N, H)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(max(256, ops.bwd_workspace_bytes(B, H, N, D, torch.bfloat16, torch.bfloat16)),
+                     dtype=torch.uint8, device=dev)
+
+    def step(bands=None):
+        ops.fwd(q, k, v, bands=bands, out=o, lse=lse)
+        ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads)
+
+    def timed(bands, steps, warmup):
+        for _ in range(warmup):
+            step(bands)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1, e2 in ev:
+            e0.record()
+            ops.fwd(q, k, v, bands=bands, out=o, lse=lse)
+            e1.record()
+            ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads)
+            e2.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
+        bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
+        return wall, float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
+
+    wall, fwd_ms, bwd_ms = timed(None, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    pairs = pairs_total(lo, hi)
+    fl_fwd = 4 * D * pairs
+    fl_all = 14 * D * pairs
+    value = fl_all / (ms_per_step * 1e-3) / 1e12
+
+    # forward kernel: one launch per spattn_fwd call.  Algorithmic bytes:
+    # read Q, K, V, write O (bf16) and LSE (fp32).
+    fwd_bytes = 4 * B * H * N * D * 2 + B * H * N * 4
+    fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    roofline = {
+        "kernel": "fwd_bf16_kernel<128>",
+        "bound": "hbm",
+        "achieved": round(fwd_gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "avg_launch_ms": round(fwd_ms, 4),
+        "algorithmic_bytes_per_launch": fwd_bytes,
+    }
+
+    out = {
+        "metric": "in-band TFLOP/s (fwd+bwd) on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (iid N(0,1), seed 1005)",
+        "config": {"workload": "band attention fwd+bwd, bf16, B=8 H=16 N=4096 d=128, BDP bands width 256",
+                   "B": B, "H": H, "N": N, "d": D},
+        "pct_bf16_mfma_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "inband_pairs": pairs,
+        "pairs_per_s": round(pairs / (ms_per_step * 1e-3), 1),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(fl_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(10 * D * pairs / (bwd_ms * 1e-3) / 1e12, 2),
+        "roofline": roofline,
+    }
+
+    if not args.no_dense:
+        dlo, dhi = ops.dense_bands(N, H)
+        dwall, dfwd, dbwd = timed((dlo, dhi), max(2, args.steps // 5), 1)
+        dms = dwall * 1e3 / max(2, args.steps // 5)
+        out["dense_causal"] = {
+            "ms_per_step": round(dms, 4), "fwd_ms": round(dfwd, 4), "bwd_ms": round(dbwd, 4),
+            "speedup_fwdbwd": round(dms / ms_per_step, 3), "speedup_fwd": round(dfwd / fwd_ms, 3),
+            "dense_tflops_fwdbwd": round(14 * D * pairs_total(dlo, dhi) / (dms * 1e-3) / 1e12, 2),
+        }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp, lo, hi, fl_all)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(inp, lo, hi, flops_all):
+    """The float64 oracle (as is) on this host, fwd+bwd over the whole workload."""
+    import platform
+
+    import oracle
+    from structured_sparse_attention_spattn_amd.inputs import as_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    q, k, v, do = (as_f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    t0 = time.perf_counter()
+    oracle.band_attention_bwd(q, k, v, do, lo, hi)  # includes the forward recompute
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(flops_all / dt / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "whole workload (B=8 H=16 N=4096 d=128), float64 numpy, fwd+bwd",
+        "seconds": round(dt, 2),
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * spattn.h -- C ABI of the band-partitioned (SPAttention) attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method ("Making Every Head Count: Sparse Attention Without the
+ * Speed-Performance Trade-off", abstract and Figure 1 caption): Balanced
+ * Distance Partitioning cuts the causal distance spectrum d = i - j in
+ * [0, N-1] into H contiguous, non-overlapping bands of width floor(N/H) or
+ * ceil(N/H), head 0 nearest; head h runs ordinary softmax attention over only
+ * the keys whose distance lies in its band.  The per-head rule is the
+ * masked-set sparse-attention formula ("Story of Attention -- Part 4: Sparse
+ * Attention, Then and Now", section 1): the attention formula is unchanged,
+ * only the key set the softmax runs over is restricted.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every function returns an int status (enum spattn_status); nothing throws
+ *   across this boundary.
+ * - Tensors are caller-owned DEVICE pointers to contiguous row-major
+ *   [B, H, N, d] arrays (batch, head, position, feature).  LSE and the
+ *   backward D vector are [B, H, N] float32.  Band arrays are HOST pointers.
+ * - dtype codes: SPATTN_F32 = 0 (float32 everywhere), SPATTN_BF16 = 1
+ *   (bfloat16 storage, float32 accumulation).  Head size d must be 64 or 128.
+ * - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *   are asynchronous: the status covers argument checks and the launch only;
+ *   faults during execution surface at the caller's next synchronisation.
+ * - The library allocates no device memory.  It keeps no mutable global
+ *   state, so calls on different streams may run concurrently.
+ * - Score scale: scale <= 0 selects 1/sqrt(d).
+ * - A query row whose key set is empty gets output 0 and LSE = -inf; it and
+ *   any key no query reaches get zero gradients.
+ */
+#ifndef SPATTN_H
+#define SPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum spattn_status {
+  SPATTN_OK = 0,
+  SPATTN_E_ARG = 1,          /* null pointer, size out of range, bad band */
+  SPATTN_E_UNSUPPORTED = 2,  /* head size / dtype combination not built */
+  SPATTN_E_HIP = 3,          /* the HIP runtime refused the launch */
+  SPATTN_E_WORKSPACE = 4     /* backward workspace too small */
+};
+
+enum spattn_dtype { SPATTN_F32 = 0, SPATTN_BF16 = 1 };
+
+/* Largest head count a call accepts (band bounds travel in the kernel
+ * argument block). */
+#define SPATTN_MAX_HEADS 256
+
+/*
+ * Band table of Balanced Distance Partitioning ("Making Every Head Count",
+ * Figure 1 caption).  Host only, no GPU needed.
+ *   N  sequence length (>= 1); H number of heads (1 .. SPATTN_MAX_HEADS).
+ *   lo, hi  caller-owned host arrays of H int32; on return head h covers the
+ *           distances lo[h] .. hi[h] inclusive.  Bands are contiguous from
+ *           distance 0, the first N mod H heads get width ceil(N/H), the rest
+ *           floor(N/H).  When H > N the heads beyond the first N get an empty
+ *           band, written as lo = N, hi = N - 1.
+ * Errors: SPATTN_E_ARG if N < 1, H < 1, H > SPATTN_MAX_HEADS or a pointer is
+ * NULL (outputs untouched).
+ */
+int spattn_band_table(int32_t N, int32_t H, int32_t* lo, int32_t* hi);
+
+/*
+ * Forward pass: for every (b, h, i), with S = { j : lo_h <= i - j <= hi_h,
+ * 0 <= j <= i },
+ *     o[b,h,i,:] = sum_{j in S} softmax_j(scale * q_i . k_j) v_j
+ *     lse[b,h,i] = ln sum_{j in S} exp(scale * q_i . k_j)
+ * (the masked-set formula of "Sparse Attention, Then and Now", section 1,
+ * over the band of "Making Every Head Count", Figure 1).
+ *   q, k, v  device, [B,H,N,d] of dtype, read only.
+ *   o        device, [B,H,N,d] of dtype, written (every row, empty rows = 0).
+ *   lse      device, [B,H,N] float32, written (-inf for empty rows).
+ *   band_lo, band_hi  host, H int32 each, or both NULL for the Balanced
+ *            Distance Partitioning table of (N, H).  Any bands with
+ *            0 <= lo <= hi + 1 and hi <= N - 1 are accepted (lo = hi + 1 is an
+ *            empty band), so one band [0, N-1] per head is dense causal
+ *            attention in the same kernels.
+ * Errors: SPATTN_E_ARG (null tensor, B/H/N < 1, H > SPATTN_MAX_HEADS, bad
+ * band), SPATTN_E_UNSUPPORTED (d not 64/128, unknown dtype), SPATTN_E_HIP.
+ */
+int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+               const int32_t* band_lo, const int32_t* band_hi, float scale,
+               void* stream);
+
+/*
+ * Bytes of device workspace spattn_bwd needs for these sizes: the float32 D
+ * vector [B,H,N] (D_i = dO_i . O_i) and, when grad_dtype is not float32, a
+ * float32 dQ accumulator [B,H,N,d].  Returns 0 for invalid sizes.
+ */
+size_t spattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d,
+                                  int32_t dtype, int32_t grad_dtype);
+
+/*
+ * Backward pass of spattn_fwd (the textbook derivative of the masked-set
+ * formula; no page gives one): with P the band-restricted softmax recomputed
+ * from the saved lse, D_i = dO_i . O_i and dS = P * (dO V^T - D),
+ *     dq = scale * dS K,   dk = scale * dS^T Q,   dv = P^T dO.
+ *   q, k, v, o, dout  device [B,H,N,d] of dtype, read only (o and lse from
+ *            spattn_fwd with the same bands).
+ *   lse      device [B,H,N] float32.
+ *   dq, dk, dv  device [B,H,N,d], written completely; element type float32
+ *            if grad_dtype == SPATTN_F32, else dtype.
+ *   grad_dtype  SPATTN_F32 or the input dtype.
+ *   workspace   device, >= spattn_bwd_workspace_bytes(...) bytes, 256-byte
+ *            aligned, caller-owned, contents need not be initialised.
+ * dq is accumulated with float32 atomics across key tiles, so its rounding
+ * order (not its value beyond rounding) may differ between runs.
+ * Errors: as spattn_fwd, plus SPATTN_E_WORKSPACE if workspace is NULL or too
+ * small.
+ */
+int spattn_bwd(const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+               int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi,
+               float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Tile sizes the forward kernel schedules with for (d, dtype): BQ query rows
+ * per workgroup and BK key rows per LDS stage.  Host only.
+ * Errors: SPATTN_E_ARG for NULL outputs, SPATTN_E_UNSUPPORTED otherwise.
+ */
+int spattn_kernel_tiles(int32_t d, int32_t dtype, int32_t* BQ, int32_t* BK);
+
+/*
+ * Test export of the band-tile schedule: runs, on the device, the same
+ * scheduling code the forward kernel uses, for one band [lo, hi] of a
+ * length-N sequence, and writes the query-major tile list in CSR form:
+ *   row_ptr  device int32 [ceil(N/BQ) + 1]
+ *   tiles    device int32 [cap]   key-tile indices u, ascending per query tile
+ *   kind     device uint8 [cap]   0 = FULL (every pair in band), 1 = PARTIAL
+ *   n_out    device int32 [1]     total number of listed tiles
+ * BQ = BK = 0 selects the forward kernel's own sizes for (d = 128, bf16).
+ * If the list is longer than cap, n_out still holds the full count and only
+ * the first cap entries are written.  A query tile t meets key tile u iff
+ * some pair (i, j) in them has j <= i < N and lo <= i - j <= hi.
+ * Errors: SPATTN_E_ARG (null pointers, N < 1, BQ or BK < 0, band outside
+ * [0, N-1]), SPATTN_E_HIP.
+ */
+int spattn_tile_list(int32_t N, int32_t lo, int32_t hi, int32_t BQ, int32_t BK,
+                     int32_t* row_ptr, int32_t* tiles, uint8_t* kind, int32_t cap,
+                     int32_t* n_out, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* spattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPATTN_H */

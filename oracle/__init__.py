@@ -41,12 +41,13 @@ from .attention import (
     band_attention_fwd,
     band_attention_bwd,
     band_attention_fwd_rows,
+    band_attention_bwd_rows,
 )
 from .tiles import query_tile_list, key_tile_list
 
 __all__ = [
     "band_table", "band_pairs", "band_table_sliding_window", "band_table_gapped_half",
     "masked_attention_literal", "masked_attention_dense", "masked_attention_dense_bwd",
-    "band_mask", "band_attention_fwd", "band_attention_bwd", "band_attention_fwd_rows",
+    "band_mask", "band_attention_fwd", "band_attention_bwd", "band_attention_fwd_rows", "band_attention_bwd_rows",
     "query_tile_list", "key_tile_list",
 ]

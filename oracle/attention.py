@@ -242,3 +242,53 @@ def band_attention_bwd(q, k, v, dout, lo, hi, scale=None):
                 dq[b, h, i0:i1] = sc * (ds @ kb)
                 dk[b, h, j0:j1 + 1] += sc * (ds.T @ qb)
     return dq, dk, dv, out, lse
+
+
+def band_attention_bwd_rows(q, k, v, dout, lo, hi, b, h, q_rows, k_rows, scale=None):
+    """Gradients for selected rows of one (b, h), each from the definition.
+
+    dq[r] = scale * sum_j dS_ij k_j for query row i = q_rows[r];
+    dk[r] = scale * sum_i dS_ij q_i and dv[r] = sum_i P_ij dO_i for key row
+    j = k_rows[r], summing over the queries i whose band reaches j.  Every
+    query row involved gets its own forward (O_i, LSE_i) and D_i = dO_i . O_i.
+    Returns (dq [len(q_rows), d], dk [len(k_rows), d], dv [len(k_rows), dv]).
+    """
+    d = q.shape[3]
+    N = q.shape[2]
+    sc = _default_scale(d, scale)
+    l, u = int(lo[h]), int(hi[h])
+    f64 = lambda x: np.asarray(x, dtype=np.float64)
+
+    def row_terms(i):
+        """(keys j0..j1, P_i over them, dS_i over them) or None if empty."""
+        j0, j1 = _key_range(i, i + 1, l, u)
+        if u < l or j1 < j0:
+            return None
+        qi = f64(q[b, h, i])
+        kb, vb = f64(k[b, h, j0:j1 + 1]), f64(v[b, h, j0:j1 + 1])
+        s = (kb @ qi) * sc
+        m = s.max()
+        e = np.exp(s - m)
+        p = e / e.sum()
+        o_i = p @ vb
+        do_i = f64(dout[b, h, i])
+        dcoef = float(do_i @ o_i)
+        ds = p * (vb @ do_i - dcoef)
+        return j0, j1, p, ds
+
+    dq = np.zeros((len(q_rows), d))
+    for r, i in enumerate(q_rows):
+        t = row_terms(i)
+        if t is not None:
+            j0, j1, _, ds = t
+            dq[r] = sc * (ds @ f64(k[b, h, j0:j1 + 1]))
+    dk = np.zeros((len(k_rows), d))
+    dv = np.zeros((len(k_rows), v.shape[3]))
+    for r, j in enumerate(k_rows):
+        if u < l or j + l > N - 1:
+            continue
+        for i in range(j + l, min(N - 1, j + u) + 1):
+            j0, j1, p, ds = row_terms(i)
+            dk[r] += sc * ds[j - j0] * f64(q[b, h, i])
+            dv[r] += p[j - j0] * f64(dout[b, h, i])
+    return dq, dk, dv

@@ -1,0 +1,70 @@
+"""ctypes binding of libspattn.so (the C ABI declared in include/spattn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  Loading fails loudly if the library has not been built.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspattn.so")
+
+OK, E_ARG, E_UNSUPPORTED, E_HIP, E_WORKSPACE = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+MAX_HEADS = 256
+
+EXPORTS = (
+    "spattn_band_table", "spattn_fwd", "spattn_bwd_workspace_bytes", "spattn_bwd",
+    "spattn_kernel_tiles", "spattn_tile_list", "spattn_status_string",
+)
+
+_lib = None
+
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class SpattnError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def load():
+    """Load (once) and return the library handle."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m structured_sparse_attention_spattn_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.spattn_band_table.argtypes = [_i32, _i32, _pi32, _pi32]
+    lib.spattn_band_table.restype = ctypes.c_int
+    lib.spattn_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32,
+                               ctypes.c_float, _p]
+    lib.spattn_fwd.restype = ctypes.c_int
+    lib.spattn_bwd_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+    lib.spattn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.spattn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _pi32, _pi32, ctypes.c_float, _p, ctypes.c_size_t, _p]
+    lib.spattn_bwd.restype = ctypes.c_int
+    lib.spattn_kernel_tiles.argtypes = [_i32, _i32, _pi32, _pi32]
+    lib.spattn_kernel_tiles.restype = ctypes.c_int
+    lib.spattn_tile_list.argtypes = [_i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p]
+    lib.spattn_tile_list.restype = ctypes.c_int
+    lib.spattn_status_string.argtypes = [ctypes.c_int]
+    lib.spattn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().spattn_status_string(int(status)).decode()
+
+
+def check(status, what):
+    if status != OK:
+        raise SpattnError(status, what)

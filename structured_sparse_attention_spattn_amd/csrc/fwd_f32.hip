@@ -1,0 +1,235 @@
+// Band-partitioned attention forward in float32 throughout, gfx950 fp32 MFMA
+// (v_mfma_f32_32x32x2_f32: full float32 products, no reduced-precision
+// inputs).  Same computation as the bfloat16 kernel: the masked-set softmax of
+// "Sparse Attention, Then and Now" section 1 over each head's distance band
+// ("Making Every Head Count", Figure 1 caption).
+//
+// One workgroup = (b, h, 128 query rows), 4 waves of 32 rows; key tiles of
+// 32 rows staged in LDS (double buffered), visited only inside the band
+// strip.  S^T = K Q^T and O^T += V^T P^T as in the bfloat16 kernel; with a
+// k-depth of 2 per product the operands are single floats, so V is read
+// row-major from LDS without a transpose.
+#include "common.h"
+
+namespace spattn {
+namespace {
+
+constexpr int kBQ = 128;
+constexpr int kBK = 32;
+constexpr int kThreads = 256;
+
+struct FwdF32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  int B, H, N;
+  int n_qt;
+  float scale_log2;
+  Bands bands;
+};
+
+template <int D>
+struct F32Smem {
+  static constexpr int kKRow = D + 2;  // odd-pair stride: 64 distinct banks per K read
+  static constexpr int kVRow = D + 8;  // rows 4 apart land 32 banks apart
+  static constexpr int kKStage = kBK * kKRow;
+  static constexpr int kStage = kKStage + kBK * kVRow;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
+  using SM = F32Smem<D>;
+  constexpr int kDT = D / 32;
+  constexpr int kKK = D / 2;
+  constexpr int kLoads = kBK * D / 4 / kThreads;  // float4 loads per thread per tensor
+  __shared__ float smem[2 * SM::kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+
+  const int total = p.B * p.H * p.n_qt;
+  const int item = xcd_remap(blockIdx.x, total);
+  const int t = item % p.n_qt;
+  const int bh = item / p.n_qt;
+  const int h = bh % p.H;
+  const int N = p.N;
+  const int lo = p.bands.lo[h];
+  const int hi = p.bands.hi[h];
+  const size_t base = (size_t)bh * N * D;
+  const float* __restrict__ qb = p.q + base;
+  const float* __restrict__ kb = p.k + base;
+  const float* __restrict__ vb = p.v + base;
+  float* __restrict__ ob = p.o + base;
+  float* __restrict__ lb = p.lse + (size_t)bh * N;
+  const float ninf = -__builtin_inff();
+
+  const int i_tile0 = t * kBQ;
+  const int i_tile1 = min(N - 1, i_tile0 + kBQ - 1);
+  const KeySpan span = band_key_span(i_tile0, i_tile1, lo, hi);
+  if (span.last < span.first) {
+    for (int c = tid; c < kBQ * (D / 4); c += kThreads) {
+      const int r = c / (D / 4), cc = c % (D / 4);
+      if (i_tile0 + r < N) *(f32x4*)(ob + (size_t)(i_tile0 + r) * D + cc * 4) = f32x4{0, 0, 0, 0};
+    }
+    for (int r = tid; r < kBQ; r += kThreads)
+      if (i_tile0 + r < N) lb[i_tile0 + r] = ninf;
+    return;
+  }
+  const int u_begin = span.first / kBK;
+  const int u_end = span.last / kBK + 1;
+
+  const int iw0 = i_tile0 + 32 * wave;
+  const int iw1 = min(N - 1, iw0 + 31);
+  const bool wave_live = iw0 <= N - 1;
+  const int iq = iw0 + c32;
+
+  float qreg[kKK];
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) qreg[kk] = iq < N ? qb[(size_t)iq * D + 2 * kk + g] : 0.f;
+
+  f32x4 kreg[kLoads], vreg[kLoads];
+  auto load_tile = [&](int u) {
+    const int j0 = u * kBK;
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 4), col = c % (D / 4);
+      const int j = j0 + row;
+      kreg[r] = j < N ? *(const f32x4*)(kb + (size_t)j * D + col * 4) : f32x4{0, 0, 0, 0};
+      vreg[r] = j < N ? *(const f32x4*)(vb + (size_t)j * D + col * 4) : f32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int s) {
+    float* ks = smem + s * SM::kStage;
+    float* vs = ks + SM::kKStage;
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 4), col = c % (D / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ks[row * SM::kKRow + col * 4 + e] = kreg[r][e];
+        vs[row * SM::kVRow + col * 4 + e] = vreg[r][e];
+      }
+    }
+  };
+
+  f32x16 acc[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  float m_run = ninf, l_run = 0.f;
+  const float sl2 = p.scale_log2;
+
+  load_tile(u_begin);
+  store_tile(0);
+  __syncthreads();
+
+  for (int u = u_begin; u < u_end; ++u) {
+    const int s = (u - u_begin) & 1;
+    const bool has_next = u + 1 < u_end;
+    if (has_next) load_tile(u + 1);
+    const float* ks = smem + s * SM::kStage;
+    const float* vs = ks + SM::kKStage;
+    const int jb = u * kBK;
+    const bool act = wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi);
+    if (act) {
+      f32x16 sacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) sacc = mfma32_f32(ks[c32 * SM::kKRow + 2 * kk + g], qreg[kk], sacc);
+      float x[16];
+      const bool full = tile_full(iw0, iw1, jb, jb + 31, lo, hi);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = jb + 8 * (i >> 2) + 4 * g + (i & 3);
+        const int dist = iq - j;
+        x[i] = (full || (dist >= lo && dist <= hi)) ? sacc[i] * sl2 : ninf;
+      }
+      float mx = ninf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == ninf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = fast_exp2(x[i] - m_use);
+        psum += x[i];
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = 8 * (i >> 2) + 4 * g + (i & 3);
+          acc[dt] = mfma32_f32(vs[j * SM::kVRow + 32 * dt + c32], x[i], acc[dt]);
+        }
+      }
+    }
+    if (has_next) store_tile(s ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (iq < N) {
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 w;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w[c] = acc[dt][4 * a + c] * inv;
+        *(f32x4*)(ob + (size_t)iq * D + 32 * dt + 8 * a + 4 * g) = w;
+      }
+    if (g == 0) lb[iq] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : ninf;
+  }
+}
+
+}  // namespace
+
+int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, const Bands& bands, float scale, hipStream_t stream) {
+  FwdF32Args a;
+  a.q = (const float*)q;
+  a.k = (const float*)k;
+  a.v = (const float*)v;
+  a.o = (float*)o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.n_qt = (N + kBQ - 1) / kBQ;
+  a.scale_log2 = scale * kLog2e;
+  a.bands = bands;
+  const long long total = (long long)B * H * a.n_qt;
+  if (total > 0x7fffffffLL) return SPATTN_E_ARG;
+  dim3 grid((unsigned)total), block(kThreads);
+  if (d == 128)
+    hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, block, 0, stream, a);
+  else if (d == 64)
+    hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block, 0, stream, a);
+  else
+    return SPATTN_E_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
+}
+
+void fwd_f32_tiles(int* BQ, int* BK) {
+  *BQ = kBQ;
+  *BK = kBK;
+}
+
+}  // namespace spattn

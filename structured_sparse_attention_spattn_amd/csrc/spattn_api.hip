@@ -1,0 +1,195 @@
+// C ABI of the band-partitioned attention library (declared in spattn.h):
+// argument checks, the Balanced Distance Partitioning band table, kernel
+// dispatch, and the tile-list export that runs the forward kernel's own
+// scheduling code on the device.
+#include <math.h>
+
+#include "common.h"
+
+namespace spattn {
+int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                    const Bands& bands, float scale, hipStream_t stream);
+int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   const Bands& bands, float scale, hipStream_t stream);
+void fwd_bf16_tiles(int* BQ, int* BK);
+void fwd_f32_tiles(int* BQ, int* BK);
+size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype);
+int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, int B, int H, int N, int d, int dtype, int grad_dtype,
+               const Bands& bands, float scale, void* workspace, hipStream_t stream);
+
+namespace {
+
+// Balanced Distance Partitioning ("Making Every Head Count", Figure 1
+// caption): contiguous bands from distance 0, widths floor(N/H) or ceil(N/H),
+// the wider ones first; heads past the first N get the empty band (N, N-1).
+void bdp_table(int N, int H, int32_t* lo, int32_t* hi) {
+  const int base = N / H, extra = N % H;
+  int start = 0;
+  for (int h = 0; h < H; ++h) {
+    const int w = base + (h < extra ? 1 : 0);
+    lo[h] = start;
+    hi[h] = start + w - 1;
+    start += w;
+  }
+}
+
+int make_bands(int N, int H, const int32_t* blo, const int32_t* bhi, Bands* out) {
+  if ((blo == nullptr) != (bhi == nullptr)) return SPATTN_E_ARG;
+  if (blo == nullptr) {
+    bdp_table(N, H, out->lo, out->hi);
+    return SPATTN_OK;
+  }
+  for (int h = 0; h < H; ++h) {
+    const int l = blo[h], u = bhi[h];
+    if (l < 0 || u > N - 1 || l > u + 1) return SPATTN_E_ARG;
+    out->lo[h] = l;
+    out->hi[h] = u;
+  }
+  return SPATTN_OK;
+}
+
+int check_sizes(int B, int H, int N, int d, int dtype) {
+  if (B < 1 || H < 1 || N < 1 || H > SPATTN_MAX_HEADS) return SPATTN_E_ARG;
+  if (dtype != SPATTN_F32 && dtype != SPATTN_BF16) return SPATTN_E_UNSUPPORTED;
+  if (d != 64 && d != 128) return SPATTN_E_UNSUPPORTED;
+  if ((long long)B * H * N * d > (1LL << 40)) return SPATTN_E_ARG;
+  return SPATTN_OK;
+}
+
+float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
+
+// Query-major tile list of one band, computed with the forward kernel's
+// scheduler (band_key_span + tile_full) by a single workgroup.
+__global__ __launch_bounds__(256) void tile_list_kernel(int N, int lo, int hi, int BQ, int BK, int32_t* row_ptr,
+                                                         int32_t* tiles, uint8_t* kind, int cap, int32_t* n_out) {
+  const int n_qt = (N + BQ - 1) / BQ;
+  for (int t = threadIdx.x; t < n_qt; t += blockDim.x) {
+    const int i_min = t * BQ, i_max = min(N - 1, i_min + BQ - 1);
+    const KeySpan s = band_key_span(i_min, i_max, lo, hi);
+    row_ptr[t + 1] = s.last < s.first ? 0 : s.last / BK - s.first / BK + 1;
+  }
+  __syncthreads();
+  __threadfence_block();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    row_ptr[0] = 0;
+    for (int t = 0; t < n_qt; ++t) {
+      run += row_ptr[t + 1];
+      row_ptr[t + 1] = run;
+    }
+    *n_out = run;
+  }
+  __syncthreads();
+  __threadfence_block();
+  for (int t = threadIdx.x; t < n_qt; t += blockDim.x) {
+    const int i_min = t * BQ, i_max = min(N - 1, i_min + BQ - 1);
+    const KeySpan s = band_key_span(i_min, i_max, lo, hi);
+    if (s.last < s.first) continue;
+    int pos = row_ptr[t];
+    for (int u = s.first / BK; u <= s.last / BK; ++u, ++pos) {
+      if (pos >= cap) break;
+      const int j0 = u * BK, j1 = min(N - 1, j0 + BK - 1);
+      tiles[pos] = u;
+      kind[pos] = tile_full(i_min, i_max, j0, j1, lo, hi) ? 0 : 1;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace spattn
+
+using namespace spattn;
+
+extern "C" {
+
+int spattn_band_table(int32_t N, int32_t H, int32_t* lo, int32_t* hi) {
+  if (N < 1 || H < 1 || H > SPATTN_MAX_HEADS || lo == nullptr || hi == nullptr) return SPATTN_E_ARG;
+  bdp_table(N, H, lo, hi);
+  return SPATTN_OK;
+}
+
+int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H, int32_t N,
+               int32_t d, int32_t dtype, const int32_t* band_lo, const int32_t* band_hi, float scale, void* stream) {
+  int st = check_sizes(B, H, N, d, dtype);
+  if (st != SPATTN_OK) return st;
+  if (!q || !k || !v || !o || !lse) return SPATTN_E_ARG;
+  Bands bands;
+  st = make_bands(N, H, band_lo, band_hi, &bands);
+  if (st != SPATTN_OK) return st;
+  const float sc = resolve_scale(scale, d);
+  if (dtype == SPATTN_BF16) return launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, bands, sc, (hipStream_t)stream);
+  return launch_fwd_f32(q, k, v, o, lse, B, H, N, d, bands, sc, (hipStream_t)stream);
+}
+
+size_t spattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype, int32_t grad_dtype) {
+  if (check_sizes(B, H, N, d, dtype) != SPATTN_OK) return 0;
+  if (grad_dtype != SPATTN_F32 && grad_dtype != dtype) return 0;
+  return bwd_workspace_bytes(B, H, N, d, dtype, grad_dtype);
+}
+
+int spattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+               int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi, float scale, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  int st = check_sizes(B, H, N, d, dtype);
+  if (st != SPATTN_OK) return st;
+  if (grad_dtype != SPATTN_F32 && grad_dtype != dtype) return SPATTN_E_UNSUPPORTED;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPATTN_E_ARG;
+  Bands bands;
+  st = make_bands(N, H, band_lo, band_hi, &bands);
+  if (st != SPATTN_OK) return st;
+  const size_t need = bwd_workspace_bytes(B, H, N, d, dtype, grad_dtype);
+  if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return SPATTN_E_WORKSPACE;
+  return launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, grad_dtype, bands, resolve_scale(scale, d),
+                    workspace, (hipStream_t)stream);
+}
+
+int spattn_kernel_tiles(int32_t d, int32_t dtype, int32_t* BQ, int32_t* BK) {
+  if (!BQ || !BK) return SPATTN_E_ARG;
+  if (d != 64 && d != 128) return SPATTN_E_UNSUPPORTED;
+  int bq, bk;
+  if (dtype == SPATTN_BF16)
+    fwd_bf16_tiles(&bq, &bk);
+  else if (dtype == SPATTN_F32)
+    fwd_f32_tiles(&bq, &bk);
+  else
+    return SPATTN_E_UNSUPPORTED;
+  *BQ = bq;
+  *BK = bk;
+  return SPATTN_OK;
+}
+
+int spattn_tile_list(int32_t N, int32_t lo, int32_t hi, int32_t BQ, int32_t BK, int32_t* row_ptr, int32_t* tiles,
+                     uint8_t* kind, int32_t cap, int32_t* n_out, void* stream) {
+  if (N < 1 || BQ < 0 || BK < 0 || cap < 0 || !row_ptr || !n_out || (cap > 0 && (!tiles || !kind)))
+    return SPATTN_E_ARG;
+  if (lo < 0 || hi > N - 1 || lo > hi + 1) return SPATTN_E_ARG;
+  if (BQ == 0 || BK == 0) {
+    if (BQ != BK) return SPATTN_E_ARG;
+    fwd_bf16_tiles(&BQ, &BK);
+  }
+  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, N, lo, hi, BQ, BK, row_ptr,
+                     tiles, kind, cap, n_out);
+  return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
+}
+
+const char* spattn_status_string(int status) {
+  switch (status) {
+    case SPATTN_OK:
+      return "ok";
+    case SPATTN_E_ARG:
+      return "invalid argument";
+    case SPATTN_E_UNSUPPORTED:
+      return "unsupported head size or dtype";
+    case SPATTN_E_HIP:
+      return "HIP launch error";
+    case SPATTN_E_WORKSPACE:
+      return "workspace missing or too small";
+    default:
+      return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""Torch-facing wrappers of the C ABI (include/spattn.h).
+
+torch provides device memory and the current stream; the computation runs
+entirely in libspattn.so.  Tensors are contiguous [B, H, N, d] on the GPU.
+"""
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bands_arg(bands, H):
+    if bands is None:
+        return None, None, None
+    lo = np.ascontiguousarray(np.asarray(bands[0], dtype=np.int32))
+    hi = np.ascontiguousarray(np.asarray(bands[1], dtype=np.int32))
+    if lo.shape != (H,) or hi.shape != (H,):
+        raise ValueError(f"band arrays must have shape ({H},)")
+    p_lo = lo.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    p_hi = hi.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    return p_lo, p_hi, (lo, hi)  # keep the arrays alive for the call
+
+
+def _check_qkv(*ts):
+    t0 = ts[0]
+    if t0.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    if t0.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t0.dtype}")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t.shape != t0.shape or t.dtype != t0.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v (and o, dout) must be contiguous with equal shape and dtype")
+
+
+def band_table(N, H):
+    """Balanced Distance Partitioning table from the library: (lo, hi) int32."""
+    lo = np.zeros(max(H, 0), dtype=np.int32)
+    hi = np.zeros(max(H, 0), dtype=np.int32)
+    st = _lib.load().spattn_band_table(
+        N, H, lo.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), hi.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    _lib.check(st, "spattn_band_table")
+    return lo, hi
+
+
+def dense_bands(N, H):
+    """Every head sees the whole causal range [0, N-1] (dense causal MHA)."""
+    return np.zeros(H, dtype=np.int32), np.full(H, N - 1, dtype=np.int32)
+
+
+def fwd(q, k, v, bands=None, scale=None, out=None, lse=None):
+    """Band attention forward.  Returns (o, lse); lse is float32 [B, H, N]."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_qkv(q, out)
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    p_lo, p_hi, _keep = _bands_arg(bands, H)
+    st = _lib.load().spattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, _DT[q.dtype],
+                                p_lo, p_hi, float(scale or 0.0), _stream_handle(q.device))
+    _lib.check(st, "spattn_fwd")
+    return out, lse
+
+
+def bwd_workspace_bytes(B, H, N, d, dtype, grad_dtype):
+    return int(_lib.load().spattn_bwd_workspace_bytes(B, H, N, d, _DT[dtype], _DT[grad_dtype]))
+
+
+def bwd(q, k, v, o, lse, dout, bands=None, scale=None, grad_dtype=None, workspace=None, out=None):
+    """Band attention backward.  Returns (dq, dk, dv) of ``grad_dtype``
+    (default: the input dtype); ``out`` may supply preallocated (dq, dk, dv)."""
+    _check_qkv(q, k, v, o, dout)
+    B, H, N, d = q.shape
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
+    need = bwd_workspace_bytes(B, H, N, d, q.dtype, grad_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = tuple(torch.empty(q.shape, dtype=grad_dtype, device=q.device) for _ in range(3))
+    dq, dk, dv = out
+    for t in out:
+        if t.shape != q.shape or t.dtype != grad_dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("gradient buffers must be contiguous GPU tensors of q's shape and grad_dtype")
+    p_lo, p_hi, _keep = _bands_arg(bands, H)
+    st = _lib.load().spattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                _ptr(dv), B, H, N, d, _DT[q.dtype], _DT[grad_dtype], p_lo, p_hi,
+                                float(scale or 0.0), _ptr(workspace), workspace.numel(),
+                                _stream_handle(q.device))
+    _lib.check(st, "spattn_bwd")
+    return dq, dk, dv
+
+
+def kernel_tiles(d, dtype):
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    st = _lib.load().spattn_kernel_tiles(d, _DT[dtype], ctypes.byref(bq), ctypes.byref(bk))
+    _lib.check(st, "spattn_kernel_tiles")
+    return bq.value, bk.value
+
+
+def tile_list(N, lo, hi, BQ=0, BK=0, device="cuda"):
+    """Device-computed query-major tile list (CSR) of one band.
+    Returns numpy (row_ptr, tiles, kind)."""
+    if BQ == 0 and BK == 0:
+        BQ, BK = kernel_tiles(128, torch.bfloat16)
+    n_qt = (N + BQ - 1) // BQ
+    cap = n_qt * ((N + BK - 1) // BK)
+    row_ptr = torch.zeros(n_qt + 1, dtype=torch.int32, device=device)
+    tiles = torch.zeros(max(cap, 1), dtype=torch.int32, device=device)
+    kind = torch.zeros(max(cap, 1), dtype=torch.uint8, device=device)
+    n_out = torch.zeros(1, dtype=torch.int32, device=device)
+    st = _lib.load().spattn_tile_list(N, lo, hi, BQ, BK, _ptr(row_ptr), _ptr(tiles), _ptr(kind), cap, _ptr(n_out),
+                                      _stream_handle(row_ptr.device))
+    _lib.check(st, "spattn_tile_list")
+    torch.cuda.current_stream(row_ptr.device).synchronize()
+    n = int(n_out.item())
+    return row_ptr.cpu().numpy(), tiles[:n].cpu().numpy(), kind[:n].cpu().numpy()

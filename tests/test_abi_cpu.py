@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/spattn.h declares, computes the band table bit-exactly
+like the oracle, and rejects bad arguments with the documented status codes
+before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from structured_sparse_attention_spattn_amd import _lib, ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "spattn.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(spattn_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (spattn_\w+)", out))
+    assert set(_declared_functions()) <= exported
+
+
+@pytest.mark.parametrize("N", range(1, 65))
+def test_band_table_bit_exact_vs_oracle(N):
+    for H in range(1, 17):
+        lo, hi = ops.band_table(N, H)
+        olo, ohi = oracle.band_table(N, H)
+        assert np.array_equal(lo, olo) and np.array_equal(hi, ohi)
+
+
+@pytest.mark.parametrize("N,H", [(1024, 8), (4096, 16), (8192, 32), (10000, 12), (3, 256), (100000, 7)])
+def test_band_table_workload_sizes(N, H):
+    lo, hi = ops.band_table(N, H)
+    olo, ohi = oracle.band_table(N, H)
+    assert np.array_equal(lo, olo) and np.array_equal(hi, ohi)
+
+
+def test_band_table_rejects_bad_args():
+    lib = _lib.load()
+    buf = (ctypes.c_int32 * 4)()
+    assert lib.spattn_band_table(0, 4, buf, buf) == _lib.E_ARG
+    assert lib.spattn_band_table(4, 0, buf, buf) == _lib.E_ARG
+    assert lib.spattn_band_table(4, 257, buf, buf) == _lib.E_ARG
+    assert lib.spattn_band_table(4, 2, None, buf) == _lib.E_ARG
+
+
+def _fwd(lib, ptr=1, B=1, H=2, N=8, d=64, dtype=_lib.BF16, lo=None, hi=None):
+    p = ctypes.c_void_p(ptr)
+    return lib.spattn_fwd(p, p, p, p, p, B, H, N, d, dtype, lo, hi, 0.0, None)
+
+
+def test_fwd_validation_before_launch():
+    lib = _lib.load()
+    assert _fwd(lib, B=0) == _lib.E_ARG
+    assert _fwd(lib, H=0) == _lib.E_ARG
+    assert _fwd(lib, N=0) == _lib.E_ARG
+    assert _fwd(lib, H=300) == _lib.E_ARG
+    assert _fwd(lib, d=96) == _lib.E_UNSUPPORTED
+    assert _fwd(lib, dtype=7) == _lib.E_UNSUPPORTED
+    assert _fwd(lib, ptr=0) == _lib.E_ARG
+    I2 = ctypes.c_int32 * 2
+    assert _fwd(lib, lo=I2(0, 5), hi=I2(4, 8)) == _lib.E_ARG       # hi > N - 1
+    assert _fwd(lib, lo=I2(0, -1), hi=I2(4, 3)) == _lib.E_ARG      # lo < 0
+    assert _fwd(lib, lo=I2(0, 6), hi=I2(4, 4)) == _lib.E_ARG       # lo > hi + 1
+    assert _fwd(lib, lo=I2(0, 5), hi=None) == _lib.E_ARG           # only one array
+
+
+def test_bwd_validation_and_workspace():
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+    need = lib.spattn_bwd_workspace_bytes(2, 3, 100, 128, _lib.BF16, _lib.BF16)
+    rows = 2 * 3 * 100
+    assert need == (rows * 4 + 255) // 256 * 256 + (rows * 128 * 4 + 255) // 256 * 256
+    assert lib.spattn_bwd_workspace_bytes(2, 3, 100, 128, _lib.BF16, _lib.F32) == (rows * 4 + 255) // 256 * 256
+    assert lib.spattn_bwd_workspace_bytes(0, 3, 100, 128, _lib.BF16, _lib.BF16) == 0
+    assert lib.spattn_bwd_workspace_bytes(1, 3, 100, 96, _lib.BF16, _lib.BF16) == 0
+
+    def bwd(ws, ws_bytes, grad=_lib.BF16, d=128):
+        return lib.spattn_bwd(p, p, p, p, p, p, p, p, p, 2, 3, 100, d, _lib.BF16, grad, None, None, 0.0,
+                              ctypes.c_void_p(ws), ws_bytes, None)
+    assert bwd(0, need) == _lib.E_WORKSPACE
+    assert bwd(256, need - 1) == _lib.E_WORKSPACE
+    assert bwd(256 + 8, need) == _lib.E_WORKSPACE  # misaligned
+    assert bwd(256, need, grad=5) == _lib.E_UNSUPPORTED
+    assert bwd(256, need, d=32) == _lib.E_UNSUPPORTED
+
+
+def test_kernel_tiles_and_status_strings():
+    lib = _lib.load()
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.spattn_kernel_tiles(128, _lib.BF16, ctypes.byref(bq), ctypes.byref(bk)) == _lib.OK
+    assert bq.value > 0 and bk.value > 0 and bq.value % 32 == 0 and bk.value % 32 == 0
+    assert lib.spattn_kernel_tiles(96, _lib.BF16, ctypes.byref(bq), ctypes.byref(bk)) == _lib.E_UNSUPPORTED
+    for s in range(5):
+        assert _lib.status_string(s)
+    assert _lib.status_string(99) == "unknown status"
+
+
+def test_tile_list_validation():
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+    assert lib.spattn_tile_list(0, 0, 0, 64, 64, p, p, p, 4, p, None) == _lib.E_ARG
+    assert lib.spattn_tile_list(10, 0, 10, 64, 64, p, p, p, 4, p, None) == _lib.E_ARG
+    assert lib.spattn_tile_list(10, 0, 5, 0, 64, p, p, p, 4, p, None) == _lib.E_ARG
+    assert lib.spattn_tile_list(10, 0, 5, 64, 64, None, p, p, 4, p, None) == _lib.E_ARG

@@ -1,0 +1,295 @@
+"""GPU parity: the HIP library, called through its C ABI, against the float64
+oracle on the same seeded inputs.
+
+Bars (stated per test): band tables and tile lists bit-exact; float32
+outputs within 1e-4 max-abs; bfloat16 outputs and gradients within 2e-2
+max-abs and 1e-2 relative L2; the positions of LSE = -inf identical.
+Small shapes are compared element by element; the full workload sizes are
+compared on sampled rows the oracle computes one by one, plus properties that
+hold at any size (empty-row positions, a closed form, gradient sums).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from structured_sparse_attention_spattn_amd import ops
+from structured_sparse_attention_spattn_amd.inputs import as_f64, make_inputs
+from structured_sparse_attention_spattn_amd.workloads import WORKLOADS, seed_for
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+BF16_REL = 1e-2
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _to_dev(inp):
+    return {k: v.to(DEV) for k, v in inp.items()}
+
+
+def _rel_l2(got, ref):
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(got - ref) / den if den > 0 else np.linalg.norm(got)
+
+
+def _check(got, ref, dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    if dtype == "f32":
+        assert err <= F32_TOL, f"{what}: max-abs {err:.3e} > {F32_TOL}"
+    else:
+        rel = _rel_l2(got, ref)
+        assert err <= BF16_TOL and rel <= BF16_REL, f"{what}: max-abs {err:.3e}, rel-L2 {rel:.3e}"
+    return err
+
+
+def _check_lse(got, ref, dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    gi, ri = np.isneginf(got), np.isneginf(ref)
+    assert np.array_equal(gi, ri), f"{what}: -inf positions differ ({int((gi != ri).sum())} rows)"
+    fin = ~ri
+    if fin.any():
+        err = float(np.max(np.abs(got[fin] - ref[fin])))
+        tol = F32_TOL if dtype == "f32" else BF16_TOL
+        assert err <= tol, f"{what}: LSE max-abs {err:.3e}"
+
+
+def _bands(kind, N, H):
+    if kind == "bdp":
+        return None, oracle.band_table(N, H)
+    if kind == "dense":
+        lo, hi = np.zeros(H, np.int32), np.full(H, N - 1, np.int32)
+    elif kind == "window":
+        lo, hi = oracle.band_table_sliding_window(N, H, max(1, N // H))
+    elif kind == "gapped":
+        lo, hi = oracle.band_table_gapped_half(N, H)
+    elif kind == "odd":  # arbitrary, partly overlapping bands incl. an empty one
+        rng = np.random.default_rng(N * 31 + H)
+        lo = rng.integers(0, N, H).astype(np.int32)
+        hi = np.minimum(N - 1, lo + rng.integers(0, max(1, N // 2), H)).astype(np.int32)
+        lo[0], hi[0] = min(N, 3), min(N, 3) - 1
+    else:
+        raise ValueError(kind)
+    return (lo, hi), (lo, hi)
+
+
+def _run_fwd(inp, bands):
+    d = _to_dev(inp)
+    o, lse = ops.fwd(d["q"], d["k"], d["v"], bands=bands)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ------------------------------------------------------------------ tile lists
+
+
+def test_tile_lists_bit_exact():
+    bq, bk = ops.kernel_tiles(128, torch.bfloat16)
+    cases = []
+    for idx, w in WORKLOADS.items():
+        lo, hi = oracle.band_table(w["N"], w["H"])
+        for h in range(w["H"]):
+            cases.append((w["N"], int(lo[h]), int(hi[h]), bq, bk))
+    for N in (1, 5, 64, 129, 300):
+        for (lo_, hi_) in [(0, N - 1), (0, 0), (N - 1, N - 1), (N // 3, N // 2), (N, N - 1)]:
+            for BQ, BK in [(1, 1), (3, 5), (16, 64), (64, 64), (128, 64)]:
+                cases.append((N, lo_, hi_, BQ, BK))
+    _say(f"tile lists: {len(cases)} cases")
+    for N, lo_, hi_, BQ, BK in cases:
+        rp, tl, kd = ops.tile_list(N, lo_, hi_, BQ, BK)
+        orp, otl, okd = oracle.query_tile_list(N, lo_, hi_, BQ, BK)
+        assert np.array_equal(rp, orp), (N, lo_, hi_, BQ, BK)
+        assert np.array_equal(tl, otl), (N, lo_, hi_, BQ, BK)
+        assert np.array_equal(kd, okd), (N, lo_, hi_, BQ, BK)
+
+
+# ------------------------------------------------------------------ forward, small
+
+
+FWD_SMALL = [
+    # (B, H, N, d, dtype, bands, seed, q_scale)
+    (1, 8, 1024, 64, "f32", "bdp", 1001, 1.0),     # the N = 1024, H = 8 workload, whole
+    (2, 3, 333, 128, "f32", "bdp", 11, 1.0),
+    (1, 5, 3, 64, "f32", "bdp", 12, 1.0),          # H > N: empty heads
+    (2, 4, 190, 64, "f32", "dense", 13, 1.0),
+    (2, 5, 300, 64, "bf16", "bdp", 21, 1.0),
+    (1, 12, 1000, 128, "bf16", "bdp", 22, 1.0),
+    (2, 3, 257, 128, "bf16", "bdp", 23, 1.0),
+    (1, 1, 1, 128, "bf16", "bdp", 24, 1.0),        # N = 1
+    (1, 7, 5, 64, "bf16", "bdp", 25, 1.0),         # H > N
+    (1, 4, 700, 128, "bf16", "dense", 26, 1.0),
+    (1, 8, 1024, 64, "bf16", "window", 27, 1.0),
+    (1, 8, 1024, 128, "bf16", "gapped", 28, 1.0),
+    (2, 6, 451, 64, "bf16", "odd", 29, 1.0),
+    (1, 6, 640, 128, "bf16", "bdp", 30, 8.0),      # large scores: online-softmax rescaling
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,bk,seed,qs", FWD_SMALL)
+def test_fwd_small_vs_oracle(B, H, N, d, dtype, bk, seed, qs):
+    _say(f"fwd small B={B} H={H} N={N} d={d} {dtype} {bk} seed={seed}")
+    inp = make_inputs(B, H, N, d, dtype=dtype, seed=seed)
+    if qs != 1.0:
+        inp["q"] = (inp["q"].float() * qs).to(inp["q"].dtype)
+    band_arg, (lo, hi) = _bands(bk, N, H)
+    o, lse = _run_fwd(inp, band_arg)
+    ro, rl = oracle.band_attention_fwd(as_f64(inp["q"]), as_f64(inp["k"]), as_f64(inp["v"]), lo, hi)
+    _check(o.float().cpu().numpy(), ro, dtype, "O")
+    _check_lse(lse.cpu().numpy(), rl, dtype, "LSE")
+
+
+# ------------------------------------------------------------------ forward, full workloads
+
+
+def _sample_rows(N, lo, hi, rng, bq=128):
+    rows = {0, N - 1, lo, lo - 1, lo + 1, min(N - 1, hi), min(N - 1, hi + 1), bq - 1, bq, N // 2}
+    rows |= set(rng.integers(0, N, 4).tolist())
+    return sorted(r for r in rows if 0 <= r < N)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_fwd_full_workload_sampled(idx):
+    w = WORKLOADS[idx]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    _say(f"fwd full workload {w['name']}")
+    inp = make_inputs(B, H, N, d, dtype=w["dtype"], seed=seed_for(idx), scale=w["scale"])
+    o, lse = _run_fwd(inp, None)
+    lo, hi = oracle.band_table(N, H)
+    lse_h = lse.cpu().numpy()
+    # empty rows are exactly the rows before each band's start
+    empty = np.arange(N)[None, None, :] < lo[None, :, None]
+    assert np.array_equal(np.isneginf(lse_h), np.broadcast_to(empty, lse_h.shape))
+    o_h = o.float().cpu().numpy()
+    assert np.all(o_h[np.broadcast_to(empty, lse_h.shape)] == 0)
+    q64, k64, v64 = (inp[n].float().numpy() for n in ("q", "k", "v"))
+    rng = np.random.default_rng(idx)
+    bq, _ = ops.kernel_tiles(d, torch.bfloat16 if w["dtype"] == "bf16" else torch.float32)
+    for b in sorted({0, B - 1}):
+        for h in range(H):
+            rows = _sample_rows(N, int(lo[h]), int(hi[h]), rng, bq)
+            ro, rl = oracle.band_attention_fwd_rows(q64, k64, v64, lo, hi, b, h, rows)
+            _check(o_h[b, h, rows], ro, w["dtype"], f"O b={b} h={h}")
+            _check_lse(lse_h[b, h, rows], rl, w["dtype"], f"LSE b={b} h={h}")
+
+
+@pytest.mark.parametrize("idx", [2, 4])
+def test_fwd_full_closed_form_zero_queries(idx):
+    """Q = 0 at full size: O_i is the mean of v_j over the band window and
+    LSE_i = ln |S_i| -- checked on every row via prefix sums."""
+    w = WORKLOADS[idx]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    _say(f"fwd closed form Q=0 {w['name']}")
+    inp = make_inputs(B, H, N, d, dtype=w["dtype"], seed=seed_for(idx) + 100)
+    inp["q"] = torch.zeros_like(inp["q"])
+    o, lse = _run_fwd(inp, None)
+    lo, hi = oracle.band_table(N, H)
+    o_h = o.float().cpu().numpy()
+    lse_h = lse.cpu().numpy().astype(np.float64)
+    v = inp["v"].double().numpy()
+    i = np.arange(N)
+    for h in range(H):
+        jf = np.maximum(0, i - int(hi[h]))
+        jl = i - int(lo[h])
+        live = jl >= jf
+        cnt = np.where(live, jl - jf + 1, 1)
+        pre = np.concatenate([np.zeros((B, 1, d)), np.cumsum(v[:, h], axis=1)], axis=1)
+        mean = (pre[:, np.where(live, jl + 1, 0)] - pre[:, np.where(live, jf, 0)]) / cnt[None, :, None]
+        mean[:, ~live] = 0.0
+        _check(o_h[:, h], mean, w["dtype"], f"O (Q=0) h={h}")
+        ref_l = np.where(live, np.log(cnt), -np.inf)
+        _check_lse(lse_h[:, h], np.broadcast_to(ref_l, (B, N)), w["dtype"], f"LSE (Q=0) h={h}")
+
+
+def test_fwd_dense_mode_matches_sdpa_at_shape():
+    """Dense-causal mode (every band [0, N-1]) against torch's float64 causal
+    SDPA on the CPU for two heads of the N = 4096, d = 128 shape."""
+    B, H, N, d = 1, 2, 4096, 128
+    inp = make_inputs(B, H, N, d, dtype="bf16", seed=77, scale=1 / math.sqrt(2))
+    o, lse = _run_fwd(inp, ops.dense_bands(N, H))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        inp["q"].double(), inp["k"].double(), inp["v"].double(), is_causal=True).numpy()
+    _check(o.float().cpu().numpy(), ref, "bf16", "dense O")
+
+
+# ------------------------------------------------------------------ backward
+
+
+BWD_SMALL = [
+    # (B, H, N, d, dtype, grad_dtype, bands, seed)
+    (2, 3, 300, 64, "bf16", "f32", "bdp", 41),
+    (1, 4, 515, 128, "bf16", "f32", "bdp", 42),
+    (1, 4, 515, 128, "bf16", "bf16", "bdp", 43),
+    (1, 9, 7, 64, "bf16", "f32", "bdp", 44),       # H > N
+    (1, 3, 260, 128, "bf16", "f32", "dense", 45),
+    (2, 6, 451, 64, "bf16", "bf16", "odd", 46),
+    (1, 3, 200, 64, "f32", "f32", "bdp", 47),
+    (1, 2, 130, 128, "f32", "f32", "dense", 48),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,gdt,bk,seed", BWD_SMALL)
+def test_bwd_small_vs_oracle(B, H, N, d, dtype, gdt, bk, seed):
+    _say(f"bwd small B={B} H={H} N={N} d={d} {dtype}->{gdt} {bk} seed={seed}")
+    inp = make_inputs(B, H, N, d, dtype=dtype, seed=seed, with_dout=True)
+    band_arg, (lo, hi) = _bands(bk, N, H)
+    dv_ = _to_dev(inp)
+    o, lse = ops.fwd(dv_["q"], dv_["k"], dv_["v"], bands=band_arg)
+    gt = torch.float32 if gdt == "f32" else dv_["q"].dtype
+    dq, dk, dv = ops.bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dv_["dout"], bands=band_arg, grad_dtype=gt)
+    torch.cuda.synchronize()
+    rq, rk, rv, _, _ = oracle.band_attention_bwd(*(as_f64(inp[n]) for n in ("q", "k", "v", "dout")), lo, hi)
+    tol_kind = "f32" if dtype == "f32" else "bf16"
+    _check(dq.float().cpu().numpy(), rq, tol_kind, "dQ")
+    _check(dk.float().cpu().numpy(), rk, tol_kind, "dK")
+    _check(dv.float().cpu().numpy(), rv, tol_kind, "dV")
+
+
+def test_bwd_full_workload_sampled_and_invariants():
+    w = WORKLOADS[5]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    _say(f"bwd full workload {w['name']}")
+    inp = make_inputs(B, H, N, d, dtype="bf16", seed=seed_for(5), with_dout=True)
+    dv_ = _to_dev(inp)
+    o, lse = ops.fwd(dv_["q"], dv_["k"], dv_["v"])
+    dq, dk, dv = ops.bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dv_["dout"], grad_dtype=torch.float32)
+    dq16, dk16, dv16 = ops.bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dv_["dout"])
+    torch.cuda.synchronize()
+    lo, hi = oracle.band_table(N, H)
+    dq_h, dk_h, dv_h = (x.cpu().numpy().astype(np.float64) for x in (dq, dk, dv))
+    dq16_h, dk16_h, dv16_h = (x.float().cpu().numpy().astype(np.float64) for x in (dq16, dk16, dv16))
+    do = inp["dout"].double().numpy()
+    empty_rows = np.arange(N)[None, :] < lo[:, None]           # [H, N]
+    never_keys = np.arange(N)[None, :] > (N - 1 - lo)[:, None]  # keys no query of the head reaches
+    for h in range(H):
+        assert np.all(dq_h[:, h][:, empty_rows[h]] == 0)
+        assert np.all(dk_h[:, h][:, never_keys[h]] == 0) and np.all(dv_h[:, h][:, never_keys[h]] == 0)
+        # sum_j dK_j = 0 and sum_j dV_j = sum of dO over non-empty rows
+        sk = dk_h[:, h].sum(axis=1)
+        assert np.max(np.abs(sk)) <= 2e-2 * max(1.0, np.max(np.abs(dk_h[:, h])) * math.sqrt(N)), h
+        sv = dv_h[:, h].sum(axis=1)
+        ref_sv = do[:, h][:, ~empty_rows[h]].sum(axis=1)
+        assert np.max(np.abs(sv - ref_sv)) <= 2e-2 * max(1.0, np.max(np.abs(ref_sv))), h
+    rng = np.random.default_rng(5)
+    q64, k64, v64, d64 = (inp[n].float().numpy() for n in ("q", "k", "v", "dout"))
+    for b in (0, B - 1):
+        for h in (0, 1, H // 2, H - 1):
+            rows = _sample_rows(N, int(lo[h]), int(hi[h]), rng)[:8]
+            krows = sorted({0, 127, 128, N - 1 - int(lo[h]), max(0, N - 2 - int(lo[h])), int(rng.integers(0, N))})
+            rq, rk, rv = oracle.band_attention_bwd_rows(q64, k64, v64, d64, lo, hi, b, h, rows, krows)
+            for got, ref, nm in ((dq_h[b, h, rows], rq, "dQ"), (dk_h[b, h, krows], rk, "dK"),
+                                 (dv_h[b, h, krows], rv, "dV"), (dq16_h[b, h, rows], rq, "dQ bf16"),
+                                 (dk16_h[b, h, krows], rk, "dK bf16"), (dv16_h[b, h, krows], rv, "dV bf16")):
+                err = np.max(np.abs(got - ref))
+                assert err <= BF16_TOL, f"{nm} b={b} h={h}: max-abs {err:.3e}"

@@ -237,3 +237,17 @@ def test_bwd_dense_form_and_invariants(N, H, monkeypatch):
         assert np.all(dq[0, h][~nonempty] == 0)
         never = np.arange(N) > N - 1 - int(lo[h])
         assert np.all(dk[0, h][never] == 0) and np.all(dv[0, h][never] == 0)
+
+
+def test_bwd_rows_api_matches_full(monkeypatch):
+    monkeypatch.setattr(oatt, "QUERY_BLOCK", 8)
+    N, H, d = 41, 3, 5
+    lo, hi = oracle.band_table(N, H)
+    q, k, v, do = (_rand((1, H, N, d), s) for s in (60, 61, 62, 63))
+    dq, dk, dv, _, _ = oracle.band_attention_bwd(q, k, v, do, lo, hi)
+    rows = [0, 3, 13, 14, 27, 40]
+    for h in range(H):
+        rq, rk, rv = oracle.band_attention_bwd_rows(q, k, v, do, lo, hi, 0, h, rows, rows)
+        assert np.max(np.abs(rq - dq[0, h, rows])) <= 1e-12
+        assert np.max(np.abs(rk - dk[0, h, rows])) <= 1e-12
+        assert np.max(np.abs(rv - dv[0, h, rows])) <= 1e-12
