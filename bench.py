@@ -44,6 +44,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal comparison")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the band kernels shard over "
@@ -53,6 +55,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 2, "copy_calibration_bytes_written":
+                          dst.numel() * 2}), flush=True)
+        return
 
     from structured_sparse_attention_spattn_amd import ops
     from structured_sparse_attention_spattn_amd.inputs import make_inputs

@@ -93,8 +93,8 @@ int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace spattn_bwd needs for these sizes: the float32 D
- * vector [B,H,N] (D_i = dO_i . O_i) and, when grad_dtype is not float32, a
- * float32 dQ accumulator [B,H,N,d].  Returns 0 for invalid sizes.
+ * vector [B,H,N] (D_i = dO_i . O_i), rounded up to 256 bytes.  Returns 0 for
+ * invalid sizes.
  */
 size_t spattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d,
                                   int32_t dtype, int32_t grad_dtype);
@@ -112,8 +112,8 @@ size_t spattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d,
  *   grad_dtype  SPATTN_F32 or the input dtype.
  *   workspace   device, >= spattn_bwd_workspace_bytes(...) bytes, 256-byte
  *            aligned, caller-owned, contents need not be initialised.
- * dq is accumulated with float32 atomics across key tiles, so its rounding
- * order (not its value beyond rounding) may differ between runs.
+ * The result is deterministic: dq is produced by a query-major pass and dk,
+ * dv by a key-major pass, with no atomics.
  * Errors: as spattn_fwd, plus SPATTN_E_WORKSPACE if workspace is NULL or too
  * small.
  */

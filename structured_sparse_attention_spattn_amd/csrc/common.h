@@ -61,6 +61,63 @@ __device__ __forceinline__ int perm_reg_row(int i, int g) {
   return ((i >> 3) << 4) + (g << 3) + (i & 7);
 }
 
+// ------------------------------------------------------------- LDS tiles
+// Row stride (bf16 elements) of a row-major [rows][D] tile in LDS.  The
+// padding makes three access patterns bank-conflict free on the 64 x 4-byte
+// LDS banks: 16-byte row reads under perm_row, 16-byte chunk stores, and the
+// transposing 8-byte reads of kmajor_operand.
+template <int D>
+struct TileRow {
+  static constexpr int kStride = D == 128 ? D + 24 : D + 8;
+};
+
+// ds_read_b64_tr_b16: within every group of 16 lanes, source lane j names 4
+// consecutive bf16 M[j][0..3]; destination lane l receives
+// {M[l/4][l%4], M[l/4+4][l%4], M[l/4+8][l%4], M[l/4+12][l%4]}.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// 32x32x16 operand whose k index runs down the rows of a row-major LDS tile:
+// lane l (group g = l/32) receives rows kbase + 8g .. kbase + 8g + 7 of column
+// n0 + (l % 32), i.e. the k-slots 8g .. 8g+7 of MFMA row/column l % 32.
+__device__ __forceinline__ bf16x8 kmajor_operand(const bf16* tile, int stride, int kbase, int n0, int lane) {
+  const int grp = lane >> 4, j = lane & 15, g = lane >> 5;
+  const bf16* src = tile + (kbase + 8 * g + (j >> 2)) * stride + n0 + 16 * (grp & 1) + 4 * (j & 3);
+  const bf16x4 a = lds_read_tr4(src);
+  const bf16x4 b = lds_read_tr4(src + 4 * stride);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Global -> register -> LDS copy of ROWS rows of a [N][D] bf16 tensor, rows
+// past N read as zero.  16-byte chunks, chunk index fastest across threads
+// (coalesced global reads, conflict-free LDS stores).
+template <int ROWS, int D, int THREADS>
+struct TileCopy {
+  static constexpr int kCpr = D / 8;  // chunks per row
+  static constexpr int kPer = ROWS * kCpr / THREADS;
+  static_assert(kPer * THREADS == ROWS * kCpr, "tile must split evenly over the threads");
+  u32x4 r[kPer];
+  __device__ __forceinline__ void load(const bf16* __restrict__ src, int row0, int N, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + THREADS * i;
+      const int row = row0 + c / kCpr;
+      r[i] = row < N ? *(const u32x4*)(src + (size_t)row * D + (c % kCpr) * 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(bf16* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + THREADS * i;
+      *(u32x4*)(dst + (c / kCpr) * TileRow<D>::kStride + (c % kCpr) * 8) = r[i];
+    }
+  }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -8,18 +8,21 @@
 //
 // Work decomposition
 //   one workgroup = (batch b, head h, query tile of BQ = 128 rows), 4 waves,
-//   each wave owns 32 query rows.  The workgroup visits only key tiles
-//   (BK = 64 rows) that intersect the diagonal strip [i - hi_h, i - lo_h] of
-//   its rows; inside a tile each wave skips the 32-key halves that miss its
-//   own 32-row strip and masks element-wise only where a half is PARTIAL.
-//   Workgroups are remapped so consecutive query tiles of one (b, h) run on
-//   the same XCD and share the K/V strip through that XCD's L2.
+//   each wave owns 32 query rows; two workgroups share a CU.  The workgroup
+//   visits only the key tiles (BK = 64 rows) that intersect the diagonal strip
+//   [i - hi_h, i - lo_h] of its rows; inside a tile each wave skips the 32-key
+//   halves that miss its own 32-row strip, and masks element-wise only where
+//   a half is PARTIAL (a wave-uniform branch).  Workgroups are remapped so
+//   consecutive query tiles of one (b, h) run on the same XCD and share the
+//   K/V strip through that XCD's L2.
 // Products (transposed so no register shuffles are needed between them)
 //   S^T (keys x queries) = K Q^T    A = K rows from LDS, B = Q in registers
-//   O^T (d x queries)   += V^T P^T  A = V^T from LDS (stored transposed),
+//   O^T (d x queries)   += V^T P^T  A = V^T read from the row-major V tile
+//                                    with the LDS transpose read,
 //                                    B = P^T straight from the S^T registers
 //   Each lane then owns one query column: the row maximum needs one
 //   cross-lane exchange (lanes l and l+32), the row sum none until the end.
+//   The score scale is folded into the exponent (one FMA per score).
 #include "common.h"
 
 namespace spattn {
@@ -28,7 +31,6 @@ namespace {
 constexpr int kBQ = 128;
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
-constexpr int kPad = 8;  // bf16 elements of row padding in LDS (16 bytes)
 
 struct FwdArgs {
   const bf16* q;
@@ -43,24 +45,12 @@ struct FwdArgs {
 };
 
 template <int D>
-struct FwdSmem {
-  static constexpr int kRow = D + kPad;     // K tile row stride (elements)
-  static constexpr int kVRow = kBK + kPad;  // V^T row stride (elements)
-  static constexpr int kKStage = kBK * kRow;
-  static constexpr int kVStage = D * kVRow;
-  static constexpr int kStage = kKStage + kVStage;
-  static constexpr int kBytes = 2 * kStage * 2;
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p) {
-  using SM = FwdSmem<D>;
-  constexpr int kKChunks = D / 32;          // 16-byte K chunks per thread per tile
-  constexpr int kVKeys = D / 32;            // keys per thread in the V transpose
-  constexpr int kVGroups = kBK / kVKeys;    // key groups across the workgroup
-  constexpr int kDT = D / 32;               // 32-row output blocks of O^T
-  constexpr int kKK = D / 16;               // k-steps of the score product
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * SM::kStage];
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
+  constexpr int kS = TileRow<D>::kStride;
+  constexpr int kTile = kBK * kS;  // one K or V tile, bf16 elements
+  constexpr int kDT = D / 32;      // 32-row output blocks of O^T
+  constexpr int kKK = D / 16;      // k-steps of the score product
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -82,26 +72,25 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p) {
   const bf16* __restrict__ vb = p.v + base;
   bf16* __restrict__ ob = p.o + base;
   float* __restrict__ lb = p.lse + (size_t)bh * N;
+  const float ninf = -__builtin_inff();
 
   const int i_tile0 = t * kBQ;
   const int i_tile1 = min(N - 1, i_tile0 + kBQ - 1);
   const KeySpan span = band_key_span(i_tile0, i_tile1, lo, hi);
   if (span.last < span.first) {
     // No row of this tile has a key: output 0, LSE -inf.
-    constexpr int kChunksPerRow = D / 8;
-    for (int c = tid; c < kBQ * kChunksPerRow; c += kThreads) {
-      const int r = c / kChunksPerRow, cc = c % kChunksPerRow;
-      const int i = i_tile0 + r;
-      if (i < N) *(u32x4*)(ob + (size_t)i * D + cc * 8) = u32x4{0, 0, 0, 0};
+    constexpr int kCpr = D / 8;
+    for (int c = tid; c < kBQ * kCpr; c += kThreads) {
+      const int i = i_tile0 + c / kCpr;
+      if (i < N) *(u32x4*)(ob + (size_t)i * D + (c % kCpr) * 8) = u32x4{0, 0, 0, 0};
     }
     for (int r = tid; r < kBQ; r += kThreads)
-      if (i_tile0 + r < N) lb[i_tile0 + r] = -__builtin_inff();
+      if (i_tile0 + r < N) lb[i_tile0 + r] = ninf;
     return;
   }
   const int u_begin = span.first / kBK;
   const int u_end = span.last / kBK + 1;
 
-  // Wave rows and their key strip.
   const int iw0 = i_tile0 + 32 * wave;
   const int iw1 = min(N - 1, iw0 + 31);
   const bool wave_live = iw0 <= N - 1;
@@ -110,81 +99,34 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p) {
   // Q^T operand: lane holds Q[iq][16kk + 8g .. +7].
   bf16x8 qreg[kKK];
 #pragma unroll
-  for (int kk = 0; kk < kKK; ++kk) {
-    if (iq < N)
-      qreg[kk] = *(const bf16x8*)(qb + (size_t)iq * D + 16 * kk + 8 * g);
-    else
-      qreg[kk] = bf16x8{};
-  }
+  for (int kk = 0; kk < kKK; ++kk)
+    qreg[kk] = iq < N ? *(const bf16x8*)(qb + (size_t)iq * D + 16 * kk + 8 * g) : bf16x8{};
 
-  // ---- global -> register staging of one K/V tile
-  u32x4 kreg[kKChunks];
-  u32x4 vreg[kVKeys];
-  const int vkg = tid % kVGroups;  // key group of this thread in the V transpose
-  const int vdc = tid / kVGroups;  // 8-wide feature chunk
-  auto load_tile = [&](int u) {
-    const int j0 = u * kBK;
-#pragma unroll
-    for (int r = 0; r < kKChunks; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / (D / 8), col = c % (D / 8);
-      const int j = j0 + row;
-      kreg[r] = j < N ? *(const u32x4*)(kb + (size_t)j * D + col * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int r = 0; r < kVKeys; ++r) {
-      const int j = j0 + kVKeys * vkg + r;
-      vreg[r] = j < N ? *(const u32x4*)(vb + (size_t)j * D + vdc * 8) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int s) {
-    bf16* ks = smem + s * SM::kStage;
-    bf16* vs = ks + SM::kKStage;
-#pragma unroll
-    for (int r = 0; r < kKChunks; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *(u32x4*)(ks + row * SM::kRow + col * 8) = kreg[r];
-    }
-    // V^T: feature row vdc*8 + e, keys kVKeys*vkg .. +kVKeys-1
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const int sh = (e & 1) * 16;
-      uint32_t h0 = (vreg[0][w] >> sh) & 0xffffu;
-      uint32_t h1 = (vreg[1][w] >> sh) & 0xffffu;
-      bf16* dst = vs + (vdc * 8 + e) * SM::kVRow + kVKeys * vkg;
-      if constexpr (kVKeys == 4) {
-        uint32_t h2 = (vreg[2][w] >> sh) & 0xffffu;
-        uint32_t h3 = (vreg[3][w] >> sh) & 0xffffu;
-        *(u32x2*)dst = u32x2{h0 | (h1 << 16), h2 | (h3 << 16)};
-      } else {
-        *(uint32_t*)dst = h0 | (h1 << 16);
-      }
-    }
-  };
-
+  TileCopy<kBK, D, kThreads> kcp, vcp;
   f32x16 acc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  float m_run = ninf;  // running row maximum of the raw (unscaled) scores
+  float l_run = 0.f;   // this lane's share of the row sum
   const float sl2 = p.scale_log2;
-  const float ninf = -__builtin_inff();
 
-  load_tile(u_begin);
-  store_tile(0);
+  kcp.load(kb, u_begin * kBK, N, tid);
+  vcp.load(vb, u_begin * kBK, N, tid);
+  kcp.store(smem, tid);
+  vcp.store(smem + kTile, tid);
   __syncthreads();
 
   for (int u = u_begin; u < u_end; ++u) {
     const int s = (u - u_begin) & 1;
     const bool has_next = u + 1 < u_end;
-    if (has_next) load_tile(u + 1);
-
-    const bf16* ks = smem + s * SM::kStage;
-    const bf16* vs = ks + SM::kKStage;
+    if (has_next) {
+      kcp.load(kb, (u + 1) * kBK, N, tid);
+      vcp.load(vb, (u + 1) * kBK, N, tid);
+    }
+    const bf16* ks = smem + s * 2 * kTile;
+    const bf16* vs = ks + kTile;
 
     float x[2][16];
     bool act[2];
@@ -196,21 +138,17 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p) {
         f32x16 sacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-        const bf16* krow = ks + (32 * m + perm_row(c32)) * SM::kRow + 8 * g;
+        const bf16* krow = ks + (32 * m + perm_row(c32)) * kS + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) {
-          const bf16x8 a = *(const bf16x8*)(krow + 16 * kk);
-          sacc = mfma32(a, qreg[kk], sacc);
-        }
-        const bool full = tile_full(iw0, iw1, jb, jb + 31, lo, hi);
-        if (full) {
+        for (int kk = 0; kk < kKK; ++kk) sacc = mfma32(*(const bf16x8*)(krow + 16 * kk), qreg[kk], sacc);
+        if (tile_full(iw0, iw1, jb, jb + 31, lo, hi)) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) x[m][i] = sacc[i] * sl2;
+          for (int i = 0; i < 16; ++i) x[m][i] = sacc[i];
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int dist = iq - (jb + perm_reg_row(i, g));
-            x[m][i] = (dist >= lo && dist <= hi) ? sacc[i] * sl2 : ninf;
+            x[m][i] = (dist >= lo && dist <= hi) ? sacc[i] : ninf;
           }
         }
       } else {
@@ -228,14 +166,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p) {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
       const float m_use = m_new == ninf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+      const float alpha = fast_exp2((m_run - m_use) * sl2);
+      const float nms = -m_use * sl2;
       m_run = m_new;
       float psum = 0.f;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          x[m][i] = fast_exp2(x[m][i] - m_use);
+          x[m][i] = fast_exp2(__builtin_fmaf(x[m][i], sl2, nms));
           psum += x[m][i];
         }
       l_run = l_run * alpha + psum;
@@ -251,20 +190,21 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p) {
         const bf16x8 pb1 = pack8(&x[m][8]);
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          const bf16* vrow = vs + (32 * dt + c32) * SM::kVRow + 32 * m + 8 * g;
-          const bf16x8 a0 = *(const bf16x8*)(vrow);
-          const bf16x8 a1 = *(const bf16x8*)(vrow + 16);
-          acc[dt] = mfma32(a0, pb0, acc[dt]);
-          acc[dt] = mfma32(a1, pb1, acc[dt]);
+          acc[dt] = mfma32(kmajor_operand(vs, kS, 32 * m, 32 * dt, lane), pb0, acc[dt]);
+          acc[dt] = mfma32(kmajor_operand(vs, kS, 32 * m + 16, 32 * dt, lane), pb1, acc[dt]);
         }
       }
     }
 
-    if (has_next) store_tile(s ^ 1);
+    if (has_next) {
+      bf16* nxt = smem + (s ^ 1) * 2 * kTile;
+      kcp.store(nxt, tid);
+      vcp.store(nxt + kTile, tid);
+    }
     __syncthreads();
   }
 
-  // ---- epilogue: O = acc / l, LSE = ln(sum exp)
+  // ---- epilogue: O = acc / l, LSE = scale * m + ln(sum)
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (iq < N) {
@@ -277,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p) {
         for (int c = 0; c < 4; ++c) w[c] = (bf16)(acc[dt][4 * a + c] * inv);
         *(bf16x4*)(ob + (size_t)iq * D + 32 * dt + 8 * a + 4 * g) = w;
       }
-    if (g == 0) lb[iq] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : ninf;
+    if (g == 0) lb[iq] = l_tot > 0.f ? (m_run * sl2 + fast_log2(l_tot)) * kLn2 : ninf;
   }
 }
 
