@@ -2,7 +2,8 @@
 
 One step = the whole hot path over one batch: spattn_fwd (band table, band
 tile schedule, scores, masks, online softmax, P V, epilogue) followed by
-spattn_bwd (D = rowsum(dO * O), band-tiled dK / dV / dQ, dQ finalize), on
+spattn_bwd's two stages (D = rowsum(dO * O) and band-tiled dQ; then band-tiled
+dK / dV), on
 B = 8, H = 16, N = 4096, d = 128, bfloat16 inputs resident in HBM.
 
 Prints ONE JSON line.  ``value`` is in-band TFLOP/s of fwd+bwd (14 d FLOP per
@@ -84,46 +85,57 @@ def main():
         ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads)
 
     def timed(bands, steps, warmup):
+        """Wall time of `steps` full steps, plus per-kernel HIP-event averages
+        (every event is recorded on the stream the kernels are launched on)."""
         for _ in range(warmup):
             step(bands)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for e0, e1, e2 in ev:
+        for e0, e1, e2, e3 in ev:
             e0.record()
             ops.fwd(q, k, v, bands=bands, out=o, lse=lse)
             e1.record()
-            ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads)
+            ops.bwd_dq(q, k, v, o, lse, do, ws, bands=bands, out=grads[0])
             e2.record()
+            ops.bwd_dkdv(q, k, v, lse, do, ws, bands=bands, out=grads[1:])
+            e3.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
-        bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
-        return wall, float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
+        per = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
+               for i, name in enumerate(("fwd", "bwd_dq", "bwd_dkdv"))}
+        return wall, per
 
-    wall, fwd_ms, bwd_ms = timed(None, args.steps, args.warmup)
+    wall, per = timed(None, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
+    fwd_ms, bwd_ms = per["fwd"], per["bwd_dq"] + per["bwd_dkdv"]
     pairs = pairs_total(lo, hi)
     fl_fwd = 4 * D * pairs
     fl_all = 14 * D * pairs
     value = fl_all / (ms_per_step * 1e-3) / 1e12
 
-    # forward kernel: one launch per spattn_fwd call.  Algorithmic bytes:
-    # read Q, K, V, write O (bf16) and LSE (fp32).
-    fwd_bytes = 4 * B * H * N * D * 2 + B * H * N * 4
-    fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    # Algorithmic HBM bytes per launch of each kernel (T = one [B,H,N,d] bf16
+    # tensor, R = one [B,H,N] fp32 row vector):
+    #   fwd      read Q, K, V; write O, LSE                  4T + R
+    #   bwd_dq   read Q, K, V, O, dO, LSE; write dQ, D        6T + 2R
+    #   bwd_dkdv read Q, K, V, dO, LSE, D; write dK, dV       6T + 2R
+    T = B * H * N * D * 2
+    R = B * H * N * 4
+    alg_bytes = {"fwd": 4 * T + R, "bwd_dq": 6 * T + 2 * R, "bwd_dkdv": 6 * T + 2 * R}
+    kern_names = {"fwd": "fwd_bf16_kernel<128>", "bwd_dq": "bwd_dq_kernel<128>", "bwd_dkdv": "bwd_dkdv_kernel<128>"}
+    dom = max(per, key=per.get)
+    gbs = alg_bytes[dom] / (per[dom] * 1e-3) / 1e9
     roofline = {
-        "kernel": "fwd_bf16_kernel<128>",
+        "kernel": kern_names[dom],
         "bound": "hbm",
-        "achieved": round(fwd_gbs, 1),
+        "achieved": round(gbs, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
-        "frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
         "traffic": None,
-        "avg_launch_ms": round(fwd_ms, 4),
-        "algorithmic_bytes_per_launch": fwd_bytes,
+        "avg_launch_ms": round(per[dom], 4),
+        "algorithmic_bytes_per_launch": alg_bytes[dom],
     }
 
     out = {
@@ -144,8 +156,9 @@ def main():
         "pct_bf16_mfma_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "inband_pairs": pairs,
         "pairs_per_s": round(pairs / (ms_per_step * 1e-3), 1),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
+        "kernel_ms": {kname: round(t, 4) for kname, t in per.items()},
+        "kernel_hbm_frac": {kname: round(alg_bytes[kname] / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                            for kname, t in per.items()},
         "fwd_tflops": round(fl_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_tflops": round(10 * D * pairs / (bwd_ms * 1e-3) / 1e12, 2),
         "roofline": roofline,
@@ -153,8 +166,9 @@ def main():
 
     if not args.no_dense:
         dlo, dhi = ops.dense_bands(N, H)
-        dwall, dfwd, dbwd = timed((dlo, dhi), max(2, args.steps // 5), 1)
+        dwall, dper = timed((dlo, dhi), max(2, args.steps // 5), 1)
         dms = dwall * 1e3 / max(2, args.steps // 5)
+        dfwd, dbwd = dper["fwd"], dper["bwd_dq"] + dper["bwd_dkdv"]
         out["dense_causal"] = {
             "ms_per_step": round(dms, 4), "fwd_ms": round(dfwd, 4), "bwd_ms": round(dbwd, 4),
             "speedup_fwdbwd": round(dms / ms_per_step, 3), "speedup_fwd": round(dfwd / fwd_ms, 3),

@@ -124,6 +124,27 @@ int spattn_bwd(const void* q, const void* k, const void* v, const void* o,
                float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two stages spattn_bwd runs, exported for callers that schedule them
+ * separately (and for per-kernel timing).  Same arguments and checks as
+ * spattn_bwd; together they compute exactly what spattn_bwd computes.
+ *   spattn_bwd_dq    writes D_i = dO_i . O_i into the workspace and dq.
+ *   spattn_bwd_dkdv  reads D from the workspace and writes dk, dv; it must run
+ *                    after spattn_bwd_dq with the same workspace, bands and
+ *                    inputs, on the same stream (or after a synchronisation).
+ */
+int spattn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, void* dq,
+                  int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+                  int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi,
+                  float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+int spattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                    const void* dout, void* dk, void* dv,
+                    int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+                    int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi,
+                    float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Tile sizes the forward kernel schedules with for (d, dtype): BQ query rows
  * per workgroup and BK key rows per LDS stage.  Host only.
  * Errors: SPATTN_E_ARG for NULL outputs, SPATTN_E_UNSUPPORTED otherwise.

@@ -7,4 +7,5 @@ Every Head Count: Sparse Attention Without the Speed-Performance Trade-off",
 abstract and Figure 1 caption).  The computation lives in the HIP library
 libspattn.so (C ABI in include/spattn.h); ``ops`` wraps it for torch tensors.
 """
-from .ops import band_table, dense_bands, fwd, bwd, bwd_workspace_bytes, kernel_tiles, tile_list  # noqa: F401
+from .ops import (band_table, dense_bands, fwd, bwd, bwd_dq, bwd_dkdv, bwd_workspace_bytes, kernel_tiles,  # noqa: F401
+                  tile_list)

@@ -161,30 +161,15 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype
   return (rows * sizeof(float) + 255) / 256 * 256;  // the D vector
 }
 
-int launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                    void* dq, void* dk, void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands,
-                    float scale, float* dvec, hipStream_t stream);
+int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                       void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, float scale,
+                       float* dvec, hipStream_t stream);
+int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
+                         void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, float scale,
+                         float* dvec, hipStream_t stream);
 
-int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-               void* dq, void* dk, void* dv, int B, int H, int N, int d, int dtype, int grad_dtype,
-               const Bands& bands, float scale, void* workspace, hipStream_t stream) {
-  const long long rows = (long long)B * H * N;
-  float* dvec = (float*)workspace;
-  if (dtype == SPATTN_BF16)
-    return launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, grad_dtype == SPATTN_F32, bands, scale,
-                           dvec, stream);
-
-  {
-    const long long threads = rows * (d / 8);
-    dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
-    if (d == 128)
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, block, 0, stream, (const float*)o, (const float*)dout,
-                         dvec, rows);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, block, 0, stream, (const float*)o, (const float*)dout,
-                         dvec, rows);
-    if (hipGetLastError() != hipSuccess) return SPATTN_E_HIP;
-  }
+static BwdF32Args f32_args(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
+                           void* dk, void* dv, int B, int H, int N, const Bands& bands, float scale, float* dvec) {
   BwdF32Args a;
   a.q = (const float*)q;
   a.k = (const float*)k;
@@ -200,14 +185,53 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* o, const
   a.N = N;
   a.scale = scale;
   a.bands = bands;
-  dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);
-  if (d == 128) {
-    hipLaunchKernelGGL(bwd_f32_dq_kernel<128>, grid, block, 0, stream, a);
-    hipLaunchKernelGGL(bwd_f32_dkdv_kernel<128>, grid, block, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(bwd_f32_dq_kernel<64>, grid, block, 0, stream, a);
-    hipLaunchKernelGGL(bwd_f32_dkdv_kernel<64>, grid, block, 0, stream, a);
+  return a;
+}
+
+// Stage 1: D_i = dO_i . O_i into the workspace, and dQ.
+int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands, float scale,
+                  void* workspace, hipStream_t stream) {
+  float* dvec = (float*)workspace;
+  if (dtype == SPATTN_BF16)
+    return launch_bwd_dq_bf16(q, k, v, o, lse, dout, dq, B, H, N, d, grad_dtype == SPATTN_F32, bands, scale, dvec,
+                              stream);
+  const long long rows = (long long)B * H * N;
+  {
+    const long long threads = rows * (d / 8);
+    dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
+    if (d == 128)
+      hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, block, 0, stream, (const float*)o, (const float*)dout,
+                         dvec, rows);
+    else
+      hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, block, 0, stream, (const float*)o, (const float*)dout,
+                         dvec, rows);
+    if (hipGetLastError() != hipSuccess) return SPATTN_E_HIP;
   }
+  BwdF32Args a = f32_args(q, k, v, lse, dout, dq, nullptr, nullptr, B, H, N, bands, scale, dvec);
+  dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_f32_dq_kernel<128>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_f32_dq_kernel<64>, grid, block, 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
+}
+
+// Stage 2: dK and dV, reading D from the workspace written by stage 1.
+int launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
+                    void* dv, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands, float scale,
+                    void* workspace, hipStream_t stream) {
+  float* dvec = (float*)workspace;
+  if (dtype == SPATTN_BF16)
+    return launch_bwd_dkdv_bf16(q, k, v, lse, dout, dk, dv, B, H, N, d, grad_dtype == SPATTN_F32, bands, scale, dvec,
+                                stream);
+  const long long rows = (long long)B * H * N;
+  BwdF32Args a = f32_args(q, k, v, lse, dout, nullptr, dk, dv, B, H, N, bands, scale, dvec);
+  dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_f32_dkdv_kernel<128>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_f32_dkdv_kernel<64>, grid, block, 0, stream, a);
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
 }
 

@@ -12,11 +12,12 @@
 //             kernel), then walks the 32-key tiles of its band strip:
 //             S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T (K^T is
 //             read from the row-major K tile with the LDS transpose read).
-//   bwd_dkdv  key-major, one workgroup per (b, h, 128 key rows), 4 waves of 32
-//             keys.  Walks the 32-row query blocks that reach its keys:
-//             S = Q K^T, dP = dO V^T, dS, dV += P^T dO, dK += dS^T Q, with dK
-//             and dV held in registers for the whole walk (dO and Q enter the
-//             last two products through the LDS transpose read).
+//   bwd_dkdv  key-major, one workgroup per (b, h, 128 key rows), 8 waves in
+//             4 pairs of 32 keys.  Walks the 32-row query blocks that reach its
+//             keys: S = Q K^T and dV += P^T dO in one wave of a pair, dP = dO V^T,
+//             dS and dK += dS^T Q in the other, dK / dV held in registers for
+//             the whole walk (dO and Q enter the last two products through the
+//             LDS transpose read).
 // Both recompute P from the saved LSE with the same band-tile enumeration as
 // the forward pass and mask element-wise only on tiles that are not FULL.
 #include "common.h"
@@ -58,20 +59,22 @@ __device__ __forceinline__ void store4(void* base, size_t idx, const float* x, b
 }
 
 // =====================================================================  dQ
-constexpr int kDqBQ = 128;  // query rows per workgroup
-constexpr int kDqBK = 32;   // key rows per stage
+constexpr int kDqBQ = 128;    // query rows per workgroup
+constexpr int kDqBK = 32;     // key rows per stage
+constexpr int kDqStages = 4;  // LDS ring depth: tiles u+1 .. u+3 load while u is used
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
-  constexpr int kS = TileRow<D>::kStride;
-  constexpr int kTile = kDqBK * kS;
+  constexpr int kTile = kDqBK * D;
   constexpr int kKK = D / 16;
   constexpr int kDT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];  // [stage][K, V]
+  using Tile = AsyncTile<kDqBK, D, kThreads / 64>;
+  constexpr int kL = 2 * Tile::kPer;  // loads per wave per stage
+  __shared__ __attribute__((aligned(16))) bf16 smem[kDqStages * 2 * kTile];  // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
@@ -117,6 +120,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const float scl = p.scale;
   // exponent offset: P = exp2(s * sl2 - lse2), lse2 = LSE * log2(e)
   const float nlse2 = row_ok ? -p.lse[(size_t)bh * N + iq] * kLog2e : 0.f;
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) {
+    settle(qreg[kk]);
+    settle(doreg[kk]);
+  }
+  settle(nlse2);
+  settle(dval);
 
   const int i_tile1 = min(N - 1, i_tile0 + kDqBQ - 1);
   const KeySpan span = band_key_span(i_tile0, i_tile1, lo, hi);
@@ -130,20 +140,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   if (span.last >= span.first) {
     const int u_begin = span.first / kDqBK;
     const int u_end = span.last / kDqBK + 1;
-    TileCopy<kDqBK, D, kThreads> kcp, vcp;
-    kcp.load(kb, u_begin * kDqBK, N, tid);
-    vcp.load(vb, u_begin * kDqBK, N, tid);
-    kcp.store(smem, tid);
-    vcp.store(smem + kTile, tid);
-    __syncthreads();
+    auto issue = [&](int u) {
+      bf16* st = smem + ((u - u_begin) % kDqStages) * 2 * kTile;
+      Tile::load(st, kb, u * kDqBK, N, wave, lane);
+      Tile::load(st + kTile, vb, u * kDqBK, N, wave, lane);
+    };
+#pragma unroll
+    for (int i = 0; i < kDqStages - 1; ++i)
+      if (u_begin + i < u_end) issue(u_begin + i);
     for (int u = u_begin; u < u_end; ++u) {
-      const int s = (u - u_begin) & 1;
-      const bool has_next = u + 1 < u_end;
-      if (has_next) {
-        kcp.load(kb, (u + 1) * kDqBK, N, tid);
-        vcp.load(vb, (u + 1) * kDqBK, N, tid);
-      }
-      const bf16* ks = smem + s * 2 * kTile;
+      const int ahead = u_end - 1 - u;  // tiles issued after u and possibly in flight
+      if (ahead >= 2)
+        wait_vmcnt<2 * kL>();
+      else if (ahead == 1)
+        wait_vmcnt<kL>();
+      else
+        wait_vmcnt<0>();
+      __syncthreads();  // tile u complete for everyone; tile u - 1 released
+      if (u + kDqStages - 1 < u_end) issue(u + kDqStages - 1);
+      const bf16* ks = smem + ((u - u_begin) % kDqStages) * 2 * kTile;
       const bf16* vs = ks + kTile;
       const int jb = u * kDqBK;
       if (wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi)) {
@@ -153,12 +168,31 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
           sacc[i] = 0.f;
           pacc[i] = 0.f;
         }
-        const bf16* krow = ks + perm_row(c32) * kS + 8 * g;
-        const bf16* vrow = vs + perm_row(c32) * kS + 8 * g;
+        const int prow = perm_row(c32);
+        // operands in two batches of 8 reads, each ahead of its 8 products
 #pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) {
-          sacc = mfma32(*(const bf16x8*)(krow + 16 * kk), qreg[kk], sacc);
-          pacc = mfma32(*(const bf16x8*)(vrow + 16 * kk), doreg[kk], pacc);
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 ka[kKK / 2], va[kKK / 2];
+#pragma unroll
+          for (int q = 0; q < kKK / 2; ++q) {
+            const int kk = half * (kKK / 2) + q;
+            ka[q] = row_chunk<D>(ks, prow, 16 * kk + 8 * g);
+            va[q] = row_chunk<D>(vs, prow, 16 * kk + 8 * g);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < kKK / 2; ++q) {
+            const int kk = half * (kKK / 2) + q;
+            sacc = mfma32(ka[q], qreg[kk], sacc);
+            pacc = mfma32(va[q], doreg[kk], pacc);
+          }
+        }
+        // K^T operands of dQ^T += K^T dS^T, in flight during the dS math
+        bf16x8 kt[2 * kDT];
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) {
+          kt[2 * dt] = kmajor_operand<D>(ks, 0, 32 * dt, lane);
+          kt[2 * dt + 1] = kmajor_operand<D>(ks, 16, 32 * dt, lane);
         }
         float ds[16];
         if (tile_full(iw0, iw1, jb, jb + 31, lo, hi)) {
@@ -175,18 +209,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
           }
         }
         const bf16x8 d0 = pack8(&ds[0]), d1 = pack8(&ds[8]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          acc[dt] = mfma32(kmajor_operand(ks, kS, 0, 32 * dt, lane), d0, acc[dt]);
-          acc[dt] = mfma32(kmajor_operand(ks, kS, 16, 32 * dt, lane), d1, acc[dt]);
+          acc[dt] = mfma32(kt[2 * dt], d0, acc[dt]);
+          acc[dt] = mfma32(kt[2 * dt + 1], d1, acc[dt]);
         }
       }
-      if (has_next) {
-        bf16* nxt = smem + (s ^ 1) * 2 * kTile;
-        kcp.store(nxt, tid);
-        vcp.store(nxt + kTile, tid);
-      }
-      __syncthreads();
     }
   }
 
@@ -203,22 +232,36 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
 }
 
 // =====================================================================  dK dV
-constexpr int kKvBK = 128;  // key rows per workgroup
-constexpr int kKvQB = 32;   // query rows per stage
+// Warp-specialised: 8 waves, 128 keys.  Wave w < 4 ("P wave") owns keys
+// 32w .. 32w+31 of the tile: S = Q K^T, P, and dV += P^T dO.  Wave w + 4
+// ("dS wave") owns the same keys: dP = dO V^T, then -- with P handed over
+// through LDS -- dS = P (dP - D) and dK += dS^T Q.  A P wave and its dS wave
+// share a SIMD, so one's MFMAs overlap the other's vector work, and each
+// wave keeps a single 32 x d accumulator.
+constexpr int kKvBK = 128;    // key rows per workgroup
+constexpr int kKvQB = 32;     // query rows per stage
+constexpr int kKvStages = 6;  // LDS ring depth: blocks tq+1 .. tq+5 load while tq is used
+constexpr int kKvThreads = 512;
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdArgs p) {
-  constexpr int kS = TileRow<D>::kStride;
-  constexpr int kTile = kKvQB * kS;
+__global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs p) {
+  constexpr int kWaves = kKvThreads / 64;
+  constexpr int kTile = kKvQB * D;
   constexpr int kKK = D / 16;
   constexpr int kDT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(16))) float lse_s[2][kKvQB];     // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float dd_s[2][kKvQB];
+  using Tile = AsyncTile<kKvQB, D, kWaves>;
+  constexpr int kL = 2 * Tile::kPer + 1;  // loads per wave per stage (Q, dO, LSE|D)
+  __shared__ __attribute__((aligned(16))) bf16 smem[kKvStages * 2 * kTile];  // [stage][Q, dO]
+  // [stage][wave][LSE of the 32 rows | D of the 32 rows]: every wave loads its own copy
+  __shared__ __attribute__((aligned(16))) float rowv[kKvStages][kWaves][2 * kKvQB];
+  // P handed from P wave w to dS wave w + 4: [w][lane][16 floats]
+  __shared__ __attribute__((aligned(16))) float pbuf[4][64][16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pwave = wave < 4;
+  const int kw = wave & 3;  // key group shared by the P / dS wave pair
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
@@ -238,134 +281,158 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   const int j0 = ut * kKvBK;
   const int j1 = min(N - 1, j0 + kKvBK - 1);
-  const int kw0 = j0 + 32 * wave;
+  const int kw0 = j0 + 32 * kw;
   const int kw1 = min(N - 1, kw0 + 31);
   const bool wave_live = kw0 <= N - 1;
   const bool wave_keys_full = kw0 + 31 <= N - 1;
   const int kj = kw0 + c32;
   const bool key_ok = kj < N;
 
-  f32x16 dvacc[kDT], dkacc[kDT];
+  f32x16 acc[kDT];  // dV (P waves) or dK (dS waves)
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dvacc[dt][i] = 0.f;
-      dkacc[dt][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
   const KeySpan qspan = band_query_span(j0, j1, lo, hi, N);
   if (qspan.last >= qspan.first) {
-    bf16x8 kop[kKK], vop[kKK];
+    // B operand of this wave's score product: K rows (P wave) or V rows (dS wave)
+    bf16x8 bop[kKK];
+    {
+      const bf16* src = pwave ? p.k : p.v;
 #pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) {
-      const size_t off = base + (size_t)kj * D + 16 * kk + 8 * g;
-      kop[kk] = key_ok ? *(const bf16x8*)(p.k + off) : bf16x8{};
-      vop[kk] = key_ok ? *(const bf16x8*)(p.v + off) : bf16x8{};
+      for (int kk = 0; kk < kKK; ++kk)
+        bop[kk] = key_ok ? *(const bf16x8*)(src + base + (size_t)kj * D + 16 * kk + 8 * g) : bf16x8{};
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) settle(bop[kk]);
     }
-    TileCopy<kKvQB, D, kThreads> qcp, dcp;
-    float lse_n = 0.f, dd_n = 0.f;
-    auto load_blk = [&](int tq) {
-      qcp.load(qb, tq * kKvQB, N, tid);
-      dcp.load(dob, tq * kKvQB, N, tid);
-      if (tid < kKvQB) {
-        const int i = tq * kKvQB + tid;
-        lse_n = i < N ? lseb[i] * kLog2e : 0.f;
-        dd_n = i < N ? ddb[i] : 0.f;
-      }
-    };
-    auto store_blk = [&](int s) {
-      bf16* st = smem + s * 2 * kTile;
-      qcp.store(st, tid);
-      dcp.store(st + kTile, tid);
-      if (tid < kKvQB) {
-        lse_s[s][tid] = lse_n;
-        dd_s[s][tid] = dd_n;
-      }
-    };
-
     const float sl2 = p.scale_log2;
     const float scl = p.scale;
     const int tq_begin = qspan.first / kKvQB;
     const int tq_end = qspan.last / kKvQB + 1;
-    load_blk(tq_begin);
-    store_blk(0);
-    __syncthreads();
+    auto issue = [&](int tq) {
+      const int st = (tq - tq_begin) % kKvStages;
+      bf16* t = smem + st * 2 * kTile;
+      Tile::load(t, qb, tq * kKvQB, N, wave, lane);
+      Tile::load(t + kTile, dob, tq * kKvQB, N, wave, lane);
+      const int i = min(tq * kKvQB + (lane & 31), N - 1);
+      const float* src = lane < 32 ? lseb + i : ddb + i;
+      lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr(&rowv[st][wave][0])), src);
+    };
+#pragma unroll
+    for (int i = 0; i < kKvStages - 1; ++i)
+      if (tq_begin + i < tq_end) issue(tq_begin + i);
     for (int tq = tq_begin; tq < tq_end; ++tq) {
-      const int s = (tq - tq_begin) & 1;
-      const bool has_next = tq + 1 < tq_end;
-      if (has_next) load_blk(tq + 1);
+      const int ahead = tq_end - 1 - tq;
+      if (ahead >= 4)
+        wait_vmcnt<4 * kL>();
+      else if (ahead == 3)
+        wait_vmcnt<3 * kL>();
+      else if (ahead == 2)
+        wait_vmcnt<2 * kL>();
+      else if (ahead == 1)
+        wait_vmcnt<kL>();
+      else
+        wait_vmcnt<0>();
+      __syncthreads();  // block tq complete for everyone; block tq - 1 released
+      if (tq + kKvStages - 1 < tq_end) issue(tq + kKvStages - 1);
+      const int s = (tq - tq_begin) % kKvStages;
       const bf16* qs = smem + s * 2 * kTile;
       const bf16* dos = qs + kTile;
+      const float* rv = &rowv[s][wave][0];
       const int i0 = tq * kKvQB;
       const int i1 = min(N - 1, i0 + kKvQB - 1);
-      // P and dS of this wave's 32 keys x 32 rows; zero when the rows miss the
-      // wave's band strip.  The dV / dK products below run unconditionally so
-      // their accumulators stay in place across iterations.
-      bf16x8 pp0{}, pp1{}, sp0{}, sp1{};
-      if (wave_live && tile_meets(i0, i1, kw0, kw1, lo, hi)) {
-        // LSE and D of the rows this lane holds: 16 * (r / 8) + 8 g + (r % 8)
-        const f32x4 l0 = *(const f32x4*)&lse_s[s][8 * g], l1 = *(const f32x4*)&lse_s[s][8 * g + 4];
-        const f32x4 l2 = *(const f32x4*)&lse_s[s][16 + 8 * g], l3 = *(const f32x4*)&lse_s[s][20 + 8 * g];
-        const f32x4 e0 = *(const f32x4*)&dd_s[s][8 * g], e1 = *(const f32x4*)&dd_s[s][8 * g + 4];
-        const f32x4 e2 = *(const f32x4*)&dd_s[s][16 + 8 * g], e3 = *(const f32x4*)&dd_s[s][20 + 8 * g];
-        const float lrow[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
-                                l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
-        const float drow_[16] = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3],
-                                 e2[0], e2[1], e2[2], e2[3], e3[0], e3[1], e3[2], e3[3]};
-        const bf16* qrow = qs + perm_row(c32) * kS + 8 * g;
-        const bf16* drow = dos + perm_row(c32) * kS + 8 * g;
-        const bool full = wave_keys_full && i0 + kKvQB - 1 <= N - 1 && tile_full(i0, i1, kw0, kw1, lo, hi);
-        float pv[16], ds[16];
-        {
-          f32x16 sacc;
+      const bool act = wave_live && tile_meets(i0, i1, kw0, kw1, lo, hi);
+      const bool full = wave_keys_full && i0 + kKvQB - 1 <= N - 1 && tile_full(i0, i1, kw0, kw1, lo, hi);
+      const int prow = perm_row(c32);
+      // per-lane row values of the 16 rows this lane holds: 16 (r / 8) + 8 g + (r % 8)
+      auto rows16 = [&](const float* v, float* out) {
+        const f32x4 a = *(const f32x4*)&v[8 * g], b = *(const f32x4*)&v[8 * g + 4];
+        const f32x4 c = *(const f32x4*)&v[16 + 8 * g], d = *(const f32x4*)&v[20 + 8 * g];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+        for (int e = 0; e < 4; ++e) {
+          out[e] = a[e];
+          out[4 + e] = b[e];
+          out[8 + e] = c[e];
+          out[12 + e] = d[e];
+        }
+      };
+      // ---- phase 1: P waves S -> P (handed over); dS waves dP
+      bf16x8 op0{}, op1{};  // packed P (P waves) or dS (dS waves)
+      f32x16 sc_;
 #pragma unroll
-          for (int kk = 0; kk < kKK; ++kk) sacc = mfma32(*(const bf16x8*)(qrow + 16 * kk), kop[kk], sacc);
+      for (int i = 0; i < 16; ++i) sc_[i] = 0.f;
+      if (act) {
+        const bf16* at = pwave ? qs : dos;
+        bf16x8 aa[kKK];
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(at, prow, 16 * kk + 8 * g);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) sc_ = mfma32(aa[kk], bop[kk], sc_);
+        if (pwave) {
+          float nl[16], pv[16];
+          rows16(rv, nl);
           if (full) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sacc[i], sl2, -lrow[i]));
+            for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
           } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int r = perm_reg_row(i, g);
               const int dist = i0 + r - kj;
               const bool ok = key_ok && i0 + r < N && dist >= lo && dist <= hi;
-              const float pe = fast_exp2(__builtin_fmaf(sacc[i], sl2, -lrow[i]));
+              const float pe = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
               pv[i] = ok ? pe : 0.f;
             }
           }
+          f32x4* dst = (f32x4*)&pbuf[kw][lane][0];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e] = f32x4{pv[4 * e], pv[4 * e + 1], pv[4 * e + 2], pv[4 * e + 3]};
+          op0 = pack8(&pv[0]);
+          op1 = pack8(&pv[8]);
         }
-        {
-          f32x16 pacc;
+      }
+      __syncthreads();  // P of this block visible to the dS waves
+      // ---- phase 2: P waves dV += P^T dO; dS waves dS, dK += dS^T Q
+      if (act) {
+        const bf16* bt = pwave ? dos : qs;
+        bf16x8 bb[2 * kDT];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pacc[i] = 0.f;
-#pragma unroll
-          for (int kk = 0; kk < kKK; ++kk) pacc = mfma32(*(const bf16x8*)(drow + 16 * kk), vop[kk], pacc);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ds[i] = pv[i] * (pacc[i] - drow_[i]) * scl;
+        for (int dt = 0; dt < kDT; ++dt) {
+          bb[2 * dt] = kmajor_operand<D>(bt, 0, 32 * dt, lane);
+          bb[2 * dt + 1] = kmajor_operand<D>(bt, 16, 32 * dt, lane);
         }
-        pp0 = pack8(&pv[0]);
-        pp1 = pack8(&pv[8]);
-        sp0 = pack8(&ds[0]);
-        sp1 = pack8(&ds[8]);
-      }
+        if (!pwave) {
+          float dd[16], pv[16], ds[16];
+          rows16(rv + kKvQB, dd);
+          const f32x4* src = (const f32x4*)&pbuf[kw][lane][0];
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
-        dvacc[dt] = mfma32(pp0, kmajor_operand(dos, kS, 0, 32 * dt, lane), dvacc[dt]);
-        dvacc[dt] = mfma32(pp1, kmajor_operand(dos, kS, 16, 32 * dt, lane), dvacc[dt]);
-        dkacc[dt] = mfma32(sp0, kmajor_operand(qs, kS, 0, 32 * dt, lane), dkacc[dt]);
-        dkacc[dt] = mfma32(sp1, kmajor_operand(qs, kS, 16, 32 * dt, lane), dkacc[dt]);
+          for (int e = 0; e < 4; ++e) {
+            const f32x4 t = src[e];
+            pv[4 * e] = t[0];
+            pv[4 * e + 1] = t[1];
+            pv[4 * e + 2] = t[2];
+            pv[4 * e + 3] = t[3];
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ds[i] = pv[i] * (sc_[i] - dd[i]) * scl;
+          op0 = pack8(&ds[0]);
+          op1 = pack8(&ds[8]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op0, bb[2 * dt], acc[dt]);
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op1, bb[2 * dt + 1], acc[dt]);
       }
-      if (has_next) store_blk(s ^ 1);
-      __syncthreads();
     }
   }
 
-  // dK, dV rows of this wave: key kw0 + 8a + 4g + c, features 32dt + c32.
+  // dV (P waves) or dK (dS waves) rows: key kw0 + 8a + 4g + c, features 32dt + c32.
   if (wave_live) {
     const bool f32 = p.grad_f32 != 0;
+    void* dst = pwave ? p.dv : p.dk;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -373,13 +440,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int j = kw0 + 8 * (i >> 2) + 4 * g + (i & 3);
         if (j < N) {
           const size_t idx = base + (size_t)j * D + 32 * dt + c32;
-          if (f32) {
-            ((float*)p.dk)[idx] = dkacc[dt][i];
-            ((float*)p.dv)[idx] = dvacc[dt][i];
-          } else {
-            ((bf16*)p.dk)[idx] = (bf16)dkacc[dt][i];
-            ((bf16*)p.dv)[idx] = (bf16)dvacc[dt][i];
-          }
+          if (f32)
+            ((float*)dst)[idx] = acc[dt][i];
+          else
+            ((bf16*)dst)[idx] = (bf16)acc[dt][i];
         }
       }
   }
@@ -387,9 +451,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 }  // namespace
 
-int launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                    void* dq, void* dk, void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands,
-                    float scale, float* dvec, hipStream_t stream) {
+static BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, bool grad_f32,
+                         const Bands& bands, float scale, float* dvec) {
   BwdArgs a;
   a.q = (const bf16*)q;
   a.k = (const bf16*)k;
@@ -405,24 +469,38 @@ int launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
   a.B = B;
   a.H = H;
   a.N = N;
+  a.n_tiles = 0;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   a.bands = bands;
-  dim3 block(kThreads);
+  return a;
+}
+
+int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                       void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, float scale,
+                       float* dvec, hipStream_t stream) {
+  BwdArgs a = make_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, grad_f32, bands, scale, dvec);
   a.n_tiles = (N + kDqBQ - 1) / kDqBQ;
-  long long total = (long long)B * H * a.n_tiles;
+  const long long total = (long long)B * H * a.n_tiles;
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   if (d == 128)
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)total), block, 0, stream, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)total), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)total), block, 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return SPATTN_E_HIP;
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)total), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
+}
+
+int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
+                         void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, float scale,
+                         float* dvec, hipStream_t stream) {
+  BwdArgs a = make_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, grad_f32, bands, scale, dvec);
   a.n_tiles = (N + kKvBK - 1) / kKvBK;
-  total = (long long)B * H * a.n_tiles;
+  const long long total = (long long)B * H * a.n_tiles;
+  if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   if (d == 128)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)total), block, 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)total), dim3(kKvThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)total), block, 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)total), dim3(kKvThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
 }
 

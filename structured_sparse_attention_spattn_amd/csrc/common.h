@@ -62,14 +62,24 @@ __device__ __forceinline__ int perm_reg_row(int i, int g) {
 }
 
 // ------------------------------------------------------------- LDS tiles
-// Row stride (bf16 elements) of a row-major [rows][D] tile in LDS.  The
-// padding makes three access patterns bank-conflict free on the 64 x 4-byte
-// LDS banks: 16-byte row reads under perm_row, 16-byte chunk stores, and the
-// transposing 8-byte reads of kmajor_operand.
+// Row-major [rows][D] bf16 tiles in LDS are stored without padding; the 16-byte
+// chunks of row r are XOR-permuted by swz<D>(r).  The permutation makes four
+// access patterns free of bank conflicts on the 64 x 4-byte LDS banks: the
+// 16-byte row reads under perm_row, the transposing 8-byte reads of
+// kmajor_operand (the LDS serves 32 lanes of those per cycle), and the 1 KB
+// contiguous writes of the direct global -> LDS loads.
 template <int D>
-struct TileRow {
-  static constexpr int kStride = D == 128 ? D + 24 : D + 8;
-};
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128)
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  else
+    return ((r >> 2) & 3) ^ (((r >> 1) & 1) << 2);
+}
+// Element (row r, column col) of a swizzled tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
+}
 
 // ds_read_b64_tr_b16: within every group of 16 lanes, source lane j names 4
 // consecutive bf16 M[j][0..3]; destination lane l receives
@@ -81,42 +91,101 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// 32x32x16 operand whose k index runs down the rows of a row-major LDS tile:
-// lane l (group g = l/32) receives rows kbase + 8g .. kbase + 8g + 7 of column
+// 32x32x16 operand whose k index runs down the rows of a swizzled tile: lane l
+// (group g = l/32) receives rows kbase + 8g .. kbase + 8g + 7 of column
 // n0 + (l % 32), i.e. the k-slots 8g .. 8g+7 of MFMA row/column l % 32.
-__device__ __forceinline__ bf16x8 kmajor_operand(const bf16* tile, int stride, int kbase, int n0, int lane) {
+template <int D>
+__device__ __forceinline__ bf16x8 kmajor_operand(const bf16* tile, int kbase, int n0, int lane) {
   const int grp = lane >> 4, j = lane & 15, g = lane >> 5;
-  const bf16* src = tile + (kbase + 8 * g + (j >> 2)) * stride + n0 + 16 * (grp & 1) + 4 * (j & 3);
-  const bf16x4 a = lds_read_tr4(src);
-  const bf16x4 b = lds_read_tr4(src + 4 * stride);
+  const int r = kbase + 8 * g + (j >> 2);
+  const int col = n0 + 16 * (grp & 1) + 4 * (j & 3);
+  const bf16x4 a = lds_read_tr4(tile + tile_off<D>(r, col));
+  const bf16x4 b = lds_read_tr4(tile + tile_off<D>(r + 4, col));
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Global -> register -> LDS copy of ROWS rows of a [N][D] bf16 tensor, rows
-// past N read as zero.  16-byte chunks, chunk index fastest across threads
-// (coalesced global reads, conflict-free LDS stores).
-template <int ROWS, int D, int THREADS>
-struct TileCopy {
-  static constexpr int kCpr = D / 8;  // chunks per row
-  static constexpr int kPer = ROWS * kCpr / THREADS;
-  static_assert(kPer * THREADS == ROWS * kCpr, "tile must split evenly over the threads");
-  u32x4 r[kPer];
-  __device__ __forceinline__ void load(const bf16* __restrict__ src, int row0, int N, int tid) {
+// 16-byte row read (8 consecutive columns from col, col % 8 == 0).
+template <int D>
+__device__ __forceinline__ bf16x8 row_chunk(const bf16* tile, int r, int col) {
+  return *(const bf16x8*)(tile + tile_off<D>(r, col));
+}
+
+// One direct global -> LDS load (global_load_lds_dwordx4 / _dword): every lane
+// sends `bytes` bytes from its own global address to lds_base + bytes * lane.
+// Issued from inline assembly so that the compiler does not see an LDS write
+// in flight: it would otherwise drain every such load before each LDS read.
+// Completion is tracked by the vector-memory counter (wait_vmcnt) and is the
+// caller's responsibility.  M0 carries the LDS base and is restored.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gaddr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(gaddr)
+      : "memory");
+}
+__device__ __forceinline__ void lds_dma4(uint32_t lds_base, const void* gaddr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(gaddr)
+      : "memory");
+}
+// LDS byte address of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const char lchar;
+  return (uint32_t)(uintptr_t)(lchar*)p;
+}
+
+// Direct global -> LDS copy of ROWS rows of a [N][D] bf16 tensor into a
+// swizzled tile: every wave instruction moves 1 KB, lane l landing at byte
+// 16 l of it.  Rows past N are clamped to row N - 1 (callers mask them).
+// Every wave issues kPer loads; when the tile has fewer 1 KB pieces than there
+// are waves, the surplus waves repeat a piece (identical bytes to the same
+// place), which keeps the per-wave load count uniform.
+template <int ROWS, int D, int WAVES>
+struct AsyncTile {
+  static constexpr int kRpi = 512 / D;  // rows per 1 KB instruction
+  static constexpr int kPieces = ROWS / kRpi;
+  static constexpr int kPer = (kPieces + WAVES - 1) / WAVES;
+  static_assert(kPieces * kRpi == ROWS && (kPieces % WAVES == 0 || kPieces < WAVES), "uneven tile split");
+  __device__ __forceinline__ static void load(bf16* tile, const bf16* __restrict__ src, int row0, int N, int wave,
+                                              int lane) {
+    const int lr = lane / (D / 8), p = lane % (D / 8);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int c = tid + THREADS * i;
-      const int row = row0 + c / kCpr;
-      r[i] = row < N ? *(const u32x4*)(src + (size_t)row * D + (c % kCpr) * 8) : u32x4{0, 0, 0, 0};
-    }
-  }
-  __device__ __forceinline__ void store(bf16* dst, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + THREADS * i;
-      *(u32x4*)(dst + (c / kCpr) * TileRow<D>::kStride + (c % kCpr) * 8) = r[i];
+      const int rb = ((wave + WAVES * i) % kPieces) * kRpi;
+      const int r = rb + lr;
+      const int grow = min(row0 + r, N - 1);
+      const int c = p ^ swz<D>(r);
+      lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr(tile + rb * D)), src + (size_t)grow * D + c * 8);
     }
   }
 };
+
+// Make the compiler complete the load that produced x here (it inserts the
+// vector-memory wait before this empty statement), so no such wait is left
+// inside a loop that also has direct LDS loads in flight.
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" ::"v"(x));
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

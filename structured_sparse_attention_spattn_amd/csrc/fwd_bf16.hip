@@ -8,7 +8,9 @@
 //
 // Work decomposition
 //   one workgroup = (batch b, head h, query tile of BQ = 128 rows), 4 waves,
-//   each wave owns 32 query rows; two workgroups share a CU.  The workgroup
+//   each wave owns 32 query rows; two workgroups share a CU.  K and V tiles
+//   stream into a double-buffered LDS ring with direct global -> LDS loads
+//   (no register staging); tile u + 1 is in flight while tile u is used.  The workgroup
 //   visits only the key tiles (BK = 64 rows) that intersect the diagonal strip
 //   [i - hi_h, i - lo_h] of its rows; inside a tile each wave skips the 32-key
 //   halves that miss its own 32-row strip, and masks element-wise only where
@@ -46,15 +48,15 @@ struct FwdArgs {
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
-  constexpr int kS = TileRow<D>::kStride;
-  constexpr int kTile = kBK * kS;  // one K or V tile, bf16 elements
+  constexpr int kTile = kBK * D;  // one K or V tile, bf16 elements
+  using Tile = AsyncTile<kBK, D, kThreads / 64>;
   constexpr int kDT = D / 32;      // 32-row output blocks of O^T
   constexpr int kKK = D / 16;      // k-steps of the score product
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
@@ -101,8 +103,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
 #pragma unroll
   for (int kk = 0; kk < kKK; ++kk)
     qreg[kk] = iq < N ? *(const bf16x8*)(qb + (size_t)iq * D + 16 * kk + 8 * g) : bf16x8{};
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) settle(qreg[kk]);
 
-  TileCopy<kBK, D, kThreads> kcp, vcp;
   f32x16 acc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
@@ -112,22 +115,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   float l_run = 0.f;   // this lane's share of the row sum
   const float sl2 = p.scale_log2;
 
-  kcp.load(kb, u_begin * kBK, N, tid);
-  vcp.load(vb, u_begin * kBK, N, tid);
-  kcp.store(smem, tid);
-  vcp.store(smem + kTile, tid);
-  __syncthreads();
+  Tile::load(smem, kb, u_begin * kBK, N, wave, lane);
+  Tile::load(smem + kTile, vb, u_begin * kBK, N, wave, lane);
 
   for (int u = u_begin; u < u_end; ++u) {
     const int s = (u - u_begin) & 1;
-    const bool has_next = u + 1 < u_end;
-    if (has_next) {
-      kcp.load(kb, (u + 1) * kBK, N, tid);
-      vcp.load(vb, (u + 1) * kBK, N, tid);
+    wait_vmcnt<0>();  // this wave's part of tile u has landed
+    __syncthreads();  // ... everyone's, and everyone is done with tile u - 1
+    if (u + 1 < u_end) {
+      bf16* nxt = smem + (s ^ 1) * 2 * kTile;
+      Tile::load(nxt, kb, (u + 1) * kBK, N, wave, lane);
+      Tile::load(nxt + kTile, vb, (u + 1) * kBK, N, wave, lane);
     }
     const bf16* ks = smem + s * 2 * kTile;
     const bf16* vs = ks + kTile;
 
+    // Scores of both 32-key halves.  Operands are read in batches ahead of
+    // their products (sched_barrier keeps the compiler from interleaving each
+    // read with its MFMA, which would expose the LDS latency every time).
     float x[2][16];
     bool act[2];
 #pragma unroll
@@ -135,12 +140,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
       const int jb = u * kBK + 32 * m;
       act[m] = wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi);
       if (act[m]) {
+        const int krow = 32 * m + perm_row(c32);
+        bf16x8 ka[kKK];
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) ka[kk] = row_chunk<D>(ks, krow, 16 * kk + 8 * g);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 sacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-        const bf16* krow = ks + (32 * m + perm_row(c32)) * kS + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) sacc = mfma32(*(const bf16x8*)(krow + 16 * kk), qreg[kk], sacc);
+        for (int kk = 0; kk < kKK; ++kk) sacc = mfma32(ka[kk], qreg[kk], sacc);
         if (tile_full(iw0, iw1, jb, jb + 31, lo, hi)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) x[m][i] = sacc[i];
@@ -158,6 +167,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
     }
 
     if (act[0] || act[1]) {
+      // V^T operands of the first active half: in flight during the softmax.
+      const int m0 = act[0] ? 0 : 1;
+      bf16x8 va[2 * kDT];
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) {
+        va[2 * dt] = kmajor_operand<D>(vs, 32 * m0, 32 * dt, lane);
+        va[2 * dt + 1] = kmajor_operand<D>(vs, 32 * m0 + 16, 32 * dt, lane);
+      }
       float mx = ninf;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -183,25 +200,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
 
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (!act[m]) continue;
-        const bf16x8 pb0 = pack8(&x[m][0]);
-        const bf16x8 pb1 = pack8(&x[m][8]);
+      {
+        const bf16x8 pb0 = pack8(&x[m0][0]);
+        const bf16x8 pb1 = pack8(&x[m0][8]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          acc[dt] = mfma32(kmajor_operand(vs, kS, 32 * m, 32 * dt, lane), pb0, acc[dt]);
-          acc[dt] = mfma32(kmajor_operand(vs, kS, 32 * m + 16, 32 * dt, lane), pb1, acc[dt]);
+          acc[dt] = mfma32(va[2 * dt], pb0, acc[dt]);
+          acc[dt] = mfma32(va[2 * dt + 1], pb1, acc[dt]);
+        }
+      }
+      if (m0 == 0 && act[1]) {
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) {
+          va[2 * dt] = kmajor_operand<D>(vs, 32, 32 * dt, lane);
+          va[2 * dt + 1] = kmajor_operand<D>(vs, 48, 32 * dt, lane);
+        }
+        const bf16x8 pb0 = pack8(&x[1][0]);
+        const bf16x8 pb1 = pack8(&x[1][8]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) {
+          acc[dt] = mfma32(va[2 * dt], pb0, acc[dt]);
+          acc[dt] = mfma32(va[2 * dt + 1], pb1, acc[dt]);
         }
       }
     }
-
-    if (has_next) {
-      bf16* nxt = smem + (s ^ 1) * 2 * kTile;
-      kcp.store(nxt, tid);
-      vcp.store(nxt + kTile, tid);
-    }
-    __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, LSE = scale * m + ln(sum)

@@ -14,9 +14,12 @@ int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
 void fwd_bf16_tiles(int* BQ, int* BK);
 void fwd_f32_tiles(int* BQ, int* BK);
 size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype);
-int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-               void* dq, void* dk, void* dv, int B, int H, int N, int d, int dtype, int grad_dtype,
-               const Bands& bands, float scale, void* workspace, hipStream_t stream);
+int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands, float scale,
+                  void* workspace, hipStream_t stream);
+int launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
+                    void* dv, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands, float scale,
+                    void* workspace, hipStream_t stream);
 
 namespace {
 
@@ -128,22 +131,58 @@ size_t spattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, in
   return bwd_workspace_bytes(B, H, N, d, dtype, grad_dtype);
 }
 
-int spattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-               void* dq, void* dk, void* dv, int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
-               int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi, float scale, void* workspace,
-               size_t workspace_bytes, void* stream) {
+// Shared checks of the backward entry points.
+static int bwd_check(int B, int H, int N, int d, int dtype, int grad_dtype, const int32_t* band_lo,
+                     const int32_t* band_hi, void* workspace, size_t workspace_bytes, Bands* bands) {
   int st = check_sizes(B, H, N, d, dtype);
   if (st != SPATTN_OK) return st;
   if (grad_dtype != SPATTN_F32 && grad_dtype != dtype) return SPATTN_E_UNSUPPORTED;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPATTN_E_ARG;
-  Bands bands;
-  st = make_bands(N, H, band_lo, band_hi, &bands);
+  st = make_bands(N, H, band_lo, band_hi, bands);
   if (st != SPATTN_OK) return st;
   const size_t need = bwd_workspace_bytes(B, H, N, d, dtype, grad_dtype);
   if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
     return SPATTN_E_WORKSPACE;
-  return launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, grad_dtype, bands, resolve_scale(scale, d),
-                    workspace, (hipStream_t)stream);
+  return SPATTN_OK;
+}
+
+int spattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype, int32_t grad_dtype,
+                  const int32_t* band_lo, const int32_t* band_hi, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  Bands bands;
+  int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
+  if (st != SPATTN_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq) return SPATTN_E_ARG;
+  return launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, resolve_scale(scale, d),
+                       workspace, (hipStream_t)stream);
+}
+
+int spattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
+                    void* dv, int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype, int32_t grad_dtype,
+                    const int32_t* band_lo, const int32_t* band_hi, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  Bands bands;
+  int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
+  if (st != SPATTN_OK) return st;
+  if (!q || !k || !v || !lse || !dout || !dk || !dv) return SPATTN_E_ARG;
+  return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, resolve_scale(scale, d),
+                         workspace, (hipStream_t)stream);
+}
+
+int spattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+               int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi, float scale, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  Bands bands;
+  int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
+  if (st != SPATTN_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPATTN_E_ARG;
+  const float sc = resolve_scale(scale, d);
+  st = launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, sc, workspace,
+                     (hipStream_t)stream);
+  if (st != SPATTN_OK) return st;
+  return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, sc, workspace,
+                         (hipStream_t)stream);
 }
 
 int spattn_kernel_tiles(int32_t d, int32_t dtype, int32_t* BQ, int32_t* BK) {

@@ -83,21 +83,54 @@ def bwd_workspace_bytes(B, H, N, d, dtype, grad_dtype):
     return int(_lib.load().spattn_bwd_workspace_bytes(B, H, N, d, _DT[dtype], _DT[grad_dtype]))
 
 
-def bwd(q, k, v, o, lse, dout, bands=None, scale=None, grad_dtype=None, workspace=None, out=None):
-    """Band attention backward.  Returns (dq, dk, dv) of ``grad_dtype``
-    (default: the input dtype); ``out`` may supply preallocated (dq, dk, dv)."""
-    _check_qkv(q, k, v, o, dout)
+def _bwd_prep(q, k, v, o, lse, dout, grad_dtype, workspace, out, n_out):
+    if o is not None:
+        _check_qkv(q, k, v, o, dout)
+    else:
+        _check_qkv(q, k, v, dout)
     B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
     grad_dtype = q.dtype if grad_dtype is None else grad_dtype
     need = bwd_workspace_bytes(B, H, N, d, q.dtype, grad_dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if out is None:
-        out = tuple(torch.empty(q.shape, dtype=grad_dtype, device=q.device) for _ in range(3))
-    dq, dk, dv = out
+        out = tuple(torch.empty(q.shape, dtype=grad_dtype, device=q.device) for _ in range(n_out))
     for t in out:
         if t.shape != q.shape or t.dtype != grad_dtype or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("gradient buffers must be contiguous GPU tensors of q's shape and grad_dtype")
+    return B, H, N, d, grad_dtype, workspace, out
+
+
+def bwd_dq(q, k, v, o, lse, dout, workspace, bands=None, scale=None, grad_dtype=None, out=None):
+    """First backward stage: D into ``workspace`` and dq.  Returns dq."""
+    B, H, N, d, grad_dtype, workspace, out = _bwd_prep(q, k, v, o, lse, dout, grad_dtype, workspace,
+                                                       None if out is None else (out,), 1)
+    p_lo, p_hi, _keep = _bands_arg(bands, H)
+    st = _lib.load().spattn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(out[0]),
+                                   B, H, N, d, _DT[q.dtype], _DT[grad_dtype], p_lo, p_hi, float(scale or 0.0),
+                                   _ptr(workspace), workspace.numel(), _stream_handle(q.device))
+    _lib.check(st, "spattn_bwd_dq")
+    return out[0]
+
+
+def bwd_dkdv(q, k, v, lse, dout, workspace, bands=None, scale=None, grad_dtype=None, out=None):
+    """Second backward stage (after bwd_dq with the same workspace): dk, dv."""
+    B, H, N, d, grad_dtype, workspace, out = _bwd_prep(q, k, v, None, lse, dout, grad_dtype, workspace, out, 2)
+    p_lo, p_hi, _keep = _bands_arg(bands, H)
+    st = _lib.load().spattn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(out[0]), _ptr(out[1]),
+                                     B, H, N, d, _DT[q.dtype], _DT[grad_dtype], p_lo, p_hi, float(scale or 0.0),
+                                     _ptr(workspace), workspace.numel(), _stream_handle(q.device))
+    _lib.check(st, "spattn_bwd_dkdv")
+    return out
+
+
+def bwd(q, k, v, o, lse, dout, bands=None, scale=None, grad_dtype=None, workspace=None, out=None):
+    """Band attention backward.  Returns (dq, dk, dv) of ``grad_dtype``
+    (default: the input dtype); ``out`` may supply preallocated (dq, dk, dv)."""
+    B, H, N, d, grad_dtype, workspace, out = _bwd_prep(q, k, v, o, lse, dout, grad_dtype, workspace, out, 3)
+    dq, dk, dv = out
     p_lo, p_hi, _keep = _bands_arg(bands, H)
     st = _lib.load().spattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                 _ptr(dv), B, H, N, d, _DT[q.dtype], _DT[grad_dtype], p_lo, p_hi,

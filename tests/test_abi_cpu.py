@@ -119,3 +119,22 @@ def test_tile_list_validation():
     assert lib.spattn_tile_list(10, 0, 10, 64, 64, p, p, p, 4, p, None) == _lib.E_ARG
     assert lib.spattn_tile_list(10, 0, 5, 0, 64, p, p, p, 4, p, None) == _lib.E_ARG
     assert lib.spattn_tile_list(10, 0, 5, 64, 64, None, p, p, 4, p, None) == _lib.E_ARG
+
+
+def test_bwd_stage_validation():
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+    need = lib.spattn_bwd_workspace_bytes(2, 3, 100, 128, _lib.BF16, _lib.BF16)
+    ws = ctypes.c_void_p(256)
+    assert lib.spattn_bwd_dq(p, p, p, p, p, p, p, 2, 3, 100, 128, _lib.BF16, _lib.BF16, None, None, 0.0,
+                             ctypes.c_void_p(0), need, None) == _lib.E_WORKSPACE
+    assert lib.spattn_bwd_dq(p, p, p, None, p, p, p, 2, 3, 100, 128, _lib.BF16, _lib.BF16, None, None, 0.0,
+                             ws, need, None) == _lib.E_ARG
+    assert lib.spattn_bwd_dq(p, p, p, p, p, p, p, 2, 3, 100, 96, _lib.BF16, _lib.BF16, None, None, 0.0,
+                             ws, need, None) == _lib.E_UNSUPPORTED
+    assert lib.spattn_bwd_dkdv(p, p, p, p, p, p, p, 2, 3, 100, 128, _lib.BF16, _lib.BF16, None, None, 0.0,
+                               ws, need - 4, None) == _lib.E_WORKSPACE
+    assert lib.spattn_bwd_dkdv(p, p, p, p, p, None, p, 2, 3, 100, 128, _lib.BF16, _lib.BF16, None, None, 0.0,
+                               ws, need, None) == _lib.E_ARG
+    assert lib.spattn_bwd_dkdv(p, p, p, p, p, p, p, 0, 3, 100, 128, _lib.BF16, _lib.BF16, None, None, 0.0,
+                               ws, need, None) == _lib.E_ARG

@@ -293,3 +293,18 @@ def test_bwd_full_workload_sampled_and_invariants():
                                  (dk16_h[b, h, krows], rk, "dK bf16"), (dv16_h[b, h, krows], rv, "dV bf16")):
                 err = np.max(np.abs(got - ref))
                 assert err <= BF16_TOL, f"{nm} b={b} h={h}: max-abs {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype,gdt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
+def test_bwd_stages_equal_combined(dtype, gdt):
+    """spattn_bwd_dq then spattn_bwd_dkdv reproduce spattn_bwd bit for bit."""
+    B, H, N, d = 2, 5, 333, 128 if dtype == "bf16" else 64
+    inp = _to_dev(make_inputs(B, H, N, d, dtype=dtype, seed=91, with_dout=True))
+    o, lse = ops.fwd(inp["q"], inp["k"], inp["v"])
+    gt = torch.float32 if gdt == "f32" else inp["q"].dtype
+    dq, dk, dv = ops.bwd(inp["q"], inp["k"], inp["v"], o, lse, inp["dout"], grad_dtype=gt)
+    ws = torch.empty(ops.bwd_workspace_bytes(B, H, N, d, inp["q"].dtype, gt), dtype=torch.uint8, device=DEV)
+    dq2 = ops.bwd_dq(inp["q"], inp["k"], inp["v"], o, lse, inp["dout"], ws, grad_dtype=gt)
+    dk2, dv2 = ops.bwd_dkdv(inp["q"], inp["k"], inp["v"], lse, inp["dout"], ws, grad_dtype=gt)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
