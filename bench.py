@@ -28,6 +28,34 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 
 
+def kernel_source_hash():
+    """sha256 over every file of the HIP sources (name + bytes, sorted)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "structured_sparse_attention_spattn_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record (copy-calibrated), or None when the kernel sources have
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_B8_H16_N4096_d128.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["traffic_bytes"])
+
+
 def pairs_total(lo, hi):
     tot = 0
     for l, u in zip(lo, hi):
@@ -133,7 +161,7 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(gbs / HBM_PEAK_GBS, 4),
-        "traffic": None,
+        "traffic": measured_traffic(kern_names[dom]),
         "avg_launch_ms": round(per[dom], 4),
         "algorithmic_bytes_per_launch": alg_bytes[dom],
     }

@@ -12,8 +12,8 @@
 //             kernel), then walks the 32-key tiles of its band strip:
 //             S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T (K^T is
 //             read from the row-major K tile with the LDS transpose read).
-//   bwd_dkdv  key-major, one workgroup per (b, h, 128 key rows), 8 waves in
-//             4 pairs of 32 keys.  Walks the 32-row query blocks that reach its
+//   bwd_dkdv  key-major, one workgroup per (b, h, 64 key rows), 4 waves in
+//             2 pairs of 32 keys.  Walks the 32-row query blocks that reach its
 //             keys: S = Q K^T and dV += P^T dO in one wave of a pair, dP = dO V^T,
 //             dS and dK += dS^T Q in the other, dK / dV held in registers for
 //             the whole walk (dO and Q enter the last two products through the
@@ -162,30 +162,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
       const bf16* vs = ks + kTile;
       const int jb = u * kDqBK;
       if (wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi)) {
+        const int prow = perm_row(c32);
+        // S^T and dP^T as four independent MFMA chains (even / odd k-steps),
+        // operands read two k-steps at a time ahead of their products.
+        f32x16 s0, s1, p0, p1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s0[i] = 0.f;
+          s1[i] = 0.f;
+          p0[i] = 0.f;
+          p1[i] = 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < kKK; kk += 2) {
+          const bf16x8 ka0 = row_chunk<D>(ks, prow, 16 * kk + 8 * g);
+          const bf16x8 ka1 = row_chunk<D>(ks, prow, 16 * kk + 16 + 8 * g);
+          const bf16x8 va0 = row_chunk<D>(vs, prow, 16 * kk + 8 * g);
+          const bf16x8 va1 = row_chunk<D>(vs, prow, 16 * kk + 16 + 8 * g);
+          __builtin_amdgcn_sched_barrier(0);
+          s0 = mfma32(ka0, qreg[kk], s0);
+          p0 = mfma32(va0, doreg[kk], p0);
+          s1 = mfma32(ka1, qreg[kk + 1], s1);
+          p1 = mfma32(va1, doreg[kk + 1], p1);
+        }
         f32x16 sacc, pacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sacc[i] = 0.f;
-          pacc[i] = 0.f;
-        }
-        const int prow = perm_row(c32);
-        // operands in two batches of 8 reads, each ahead of its 8 products
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 ka[kKK / 2], va[kKK / 2];
-#pragma unroll
-          for (int q = 0; q < kKK / 2; ++q) {
-            const int kk = half * (kKK / 2) + q;
-            ka[q] = row_chunk<D>(ks, prow, 16 * kk + 8 * g);
-            va[q] = row_chunk<D>(vs, prow, 16 * kk + 8 * g);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int q = 0; q < kKK / 2; ++q) {
-            const int kk = half * (kKK / 2) + q;
-            sacc = mfma32(ka[q], qreg[kk], sacc);
-            pacc = mfma32(va[q], doreg[kk], pacc);
-          }
+          sacc[i] = s0[i] + s1[i];
+          pacc[i] = p0[i] + p1[i];
         }
         // K^T operands of dQ^T += K^T dS^T, in flight during the dS math
         bf16x8 kt[2 * kDT];
@@ -232,19 +236,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
 }
 
 // =====================================================================  dK dV
-// Warp-specialised: 8 waves, 128 keys.  Wave w < 4 ("P wave") owns keys
-// 32w .. 32w+31 of the tile: S = Q K^T, P, and dV += P^T dO.  Wave w + 4
-// ("dS wave") owns the same keys: dP = dO V^T, then -- with P handed over
-// through LDS -- dS = P (dP - D) and dK += dS^T Q.  A P wave and its dS wave
-// share a SIMD, so one's MFMAs overlap the other's vector work, and each
-// wave keeps a single 32 x d accumulator.
-constexpr int kKvBK = 128;    // key rows per workgroup
+// Warp-specialised: 4 waves, 64 keys, two workgroups per CU.  Wave w < 2
+// ("P wave") owns keys 32w .. 32w+31 of the tile: S = Q K^T, P, and
+// dV += P^T dO.  Wave w + 2 ("dS wave") owns the same keys: dP = dO V^T, then
+// -- with P handed over through LDS -- dS = P (dP - D) and dK += dS^T Q.  Each
+// wave keeps a single 32 x d accumulator; the two workgroups on a CU run
+// their barrier-separated phases independently, so one's LDS reads overlap
+// the other's matrix products.
+constexpr int kKvBK = 64;     // key rows per workgroup
 constexpr int kKvQB = 32;     // query rows per stage
-constexpr int kKvStages = 6;  // LDS ring depth: blocks tq+1 .. tq+5 load while tq is used
-constexpr int kKvThreads = 512;
+constexpr int kKvStages = 4;  // LDS ring depth: blocks tq+1 .. tq+3 load while tq is used
+constexpr int kKvThreads = 256;
+constexpr int kKvPairs = kKvThreads / 128;
 
 template <int D>
-__global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs p) {
+__global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   constexpr int kWaves = kKvThreads / 64;
   constexpr int kTile = kKvQB * D;
   constexpr int kKK = D / 16;
@@ -254,14 +260,14 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) bf16 smem[kKvStages * 2 * kTile];  // [stage][Q, dO]
   // [stage][wave][LSE of the 32 rows | D of the 32 rows]: every wave loads its own copy
   __shared__ __attribute__((aligned(16))) float rowv[kKvStages][kWaves][2 * kKvQB];
-  // P handed from P wave w to dS wave w + 4: [w][lane][16 floats]
-  __shared__ __attribute__((aligned(16))) float pbuf[4][64][16];
+  // P handed from P wave w to dS wave w + kKvPairs: [w][lane][16 floats]
+  __shared__ __attribute__((aligned(16))) float pbuf[kKvPairs][64][16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool pwave = wave < 4;
-  const int kw = wave & 3;  // key group shared by the P / dS wave pair
+  const bool pwave = wave < kKvPairs;
+  const int kw = wave % kKvPairs;  // key group shared by the P / dS wave pair
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
@@ -323,12 +329,9 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs p) {
     for (int i = 0; i < kKvStages - 1; ++i)
       if (tq_begin + i < tq_end) issue(tq_begin + i);
     for (int tq = tq_begin; tq < tq_end; ++tq) {
-      const int ahead = tq_end - 1 - tq;
-      if (ahead >= 4)
-        wait_vmcnt<4 * kL>();
-      else if (ahead == 3)
-        wait_vmcnt<3 * kL>();
-      else if (ahead == 2)
+      const int ahead = tq_end - 1 - tq;  // blocks issued after tq (at most kKvStages - 2 in flight)
+      static_assert(kKvStages == 4, "the wait ladder below assumes a 4-deep ring");
+      if (ahead >= 2)
         wait_vmcnt<2 * kL>();
       else if (ahead == 1)
         wait_vmcnt<kL>();
@@ -368,8 +371,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(at, prow, 16 * kk + 8 * g);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) sc_ = mfma32(aa[kk], bop[kk], sc_);
+        sc_ = mfma_ksum<kKK>(aa, bop);
         if (pwave) {
           float nl[16], pv[16];
           rows16(rv, nl);

@@ -187,6 +187,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Sum over kk of a[kk] x b[kk] (32x32 output, k = 16 per product) with the
+// products spread over up to four independent accumulators: a chain of
+// dependent MFMAs waits the full MFMA latency per step, four chains keep the
+// matrix pipe issuing back to back.
+template <int KK>
+__device__ __forceinline__ f32x16 mfma_ksum(const bf16x8* a, const bf16x8* b) {
+  constexpr int kCh = KK < 4 ? KK : 4;
+  f32x16 part[kCh];
+#pragma unroll
+  for (int c = 0; c < kCh; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[c][i] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) part[kk % kCh] = mfma32(a[kk], b[kk], part[kk % kCh]);
+#pragma unroll
+  for (int c = 1; c < kCh; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[0][i] += part[c][i];
+  return part[0];
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -145,11 +145,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) ka[kk] = row_chunk<D>(ks, krow, 16 * kk + 8 * g);
         __builtin_amdgcn_sched_barrier(0);
-        f32x16 sacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) sacc = mfma32(ka[kk], qreg[kk], sacc);
+        const f32x16 sacc = mfma_ksum<kKK>(ka, qreg);
         if (tile_full(iw0, iw1, jb, jb + 31, lo, hi)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) x[m][i] = sacc[i];
