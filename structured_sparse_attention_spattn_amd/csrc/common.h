@@ -41,6 +41,12 @@ struct Bands {
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// 16x16x32 bf16 -> f32.  Operand layout (lane l, group q = l / 16):
+//   A: row l % 16, k-slots 8q .. 8q+7;   B: column l % 16, k-slots 8q .. 8q+7
+//   C: column l % 16, register r holds row 4q + r.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 // 32x32x2 f32: A row l % 32, k-slot g; B column l % 32, k-slot g; C as above.
 __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -99,6 +105,19 @@ __device__ __forceinline__ bf16x8 kmajor_operand(const bf16* tile, int kbase, in
   const int grp = lane >> 4, j = lane & 15, g = lane >> 5;
   const int r = kbase + 8 * g + (j >> 2);
   const int col = n0 + 16 * (grp & 1) + 4 * (j & 3);
+  const bf16x4 a = lds_read_tr4(tile + tile_off<D>(r, col));
+  const bf16x4 b = lds_read_tr4(tile + tile_off<D>(r + 4, col));
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// 16x16x32 operand whose k index runs down the rows of a swizzled tile: lane
+// l (group q = l/16) receives rows kbase + 8q .. kbase + 8q + 7 of column
+// n0 + (l % 16), i.e. the k-slots 8q .. 8q+7 of MFMA row/column l % 16.
+template <int D>
+__device__ __forceinline__ bf16x8 kmajor16_operand(const bf16* tile, int kbase, int n0, int lane) {
+  const int q = lane >> 4, j = lane & 15;
+  const int r = kbase + 8 * q + (j >> 2);
+  const int col = n0 + 4 * (j & 3);
   const bf16x4 a = lds_read_tr4(tile + tile_off<D>(r, col));
   const bf16x4 b = lds_read_tr4(tile + tile_off<D>(r + 4, col));
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -191,9 +210,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // products spread over up to four independent accumulators: a chain of
 // dependent MFMAs waits the full MFMA latency per step, four chains keep the
 // matrix pipe issuing back to back.
-template <int KK>
+template <int KK, int CH = 4>
 __device__ __forceinline__ f32x16 mfma_ksum(const bf16x8* a, const bf16x8* b) {
-  constexpr int kCh = KK < 4 ? KK : 4;
+  constexpr int kCh = KK < CH ? KK : CH;
   f32x16 part[kCh];
 #pragma unroll
   for (int c = 0; c < kCh; ++c)
@@ -208,8 +227,63 @@ __device__ __forceinline__ f32x16 mfma_ksum(const bf16x8* a, const bf16x8* b) {
   return part[0];
 }
 
+// Scheduling pattern for the current region: NM times {one MFMA, up to NT
+// transcendental and up to NV other vector-ALU instructions}, so independent
+// VALU work issues while each MFMA runs instead of after the last one.
+template <int NM, int NT, int NV>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x400, NT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
+// Keep the computation of x inside the current region (an empty asm that
+// reads it; no instruction is emitted).
+template <typename T>
+__device__ __forceinline__ void keep_here(const T& x) {
+  asm volatile("" ::"v"(x));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Combine the values of lanes l and l ^ 32 (the two 16-row halves of one
+// 32x32 accumulator column) without going through LDS: v_permlane32_swap
+// exchanges lanes 32..63 of one register with lanes 0..31 of another, so on
+// two copies of x it leaves each lane holding its own value in one of them
+// and its partner's in the other.  Issued from inline assembly: the compiler's
+// intrinsic has been seen to substitute the first result for the second,
+// losing the partner's value.  The s_nop covers the wait states a permlane
+// swap needs after a VALU write of its operands.
+__device__ __forceinline__ void pair_exchange(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  pair_exchange(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  pair_exchange(x, a, b);
+  return a + b;
+}
+
+// Band mask of one 32x32 score accumulator under perm_row: register i of a
+// lane in group g holds key row kb + perm_reg_row(i, g) against query iq;
+// the pair is kept when lo <= iq - key <= hi.  base = iq - kb - 8 g - lo,
+// width = hi - lo; one unsigned compare per score.
+__device__ __forceinline__ void band_mask(float* x, int base, int width) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = ((i >> 3) << 4) + (i & 7);
+    x[i] = (uint32_t)(base - c) <= (uint32_t)width ? x[i] : -__builtin_inff();
+  }
+}
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   bf16x8 r;

@@ -25,6 +25,8 @@
 //   Each lane then owns one query column: the row maximum needs one
 //   cross-lane exchange (lanes l and l+32), the row sum none until the end.
 //   The score scale is folded into the exponent (one FMA per score).
+#include <type_traits>
+
 #include "common.h"
 
 namespace spattn {
@@ -45,6 +47,218 @@ struct FwdArgs {
   float scale_log2;
   Bands bands;
 };
+
+// Online-softmax state of one wave: O^T accumulator blocks, the reference
+// maximum of every query column (raw score units) and this lane's share of
+// the row sum, all relative to that reference.
+template <int D>
+struct OnlineState {
+  f32x16 acc[D / 32];
+  float m_ref;
+  float l_run;
+};
+
+// A new reference maximum is taken only when some row's maximum has grown by
+// more than 2^kRescaleLog2 over its reference (wave-uniform decision): until
+// then probabilities are exp2 of at most kRescaleLog2, and numerator and
+// denominator share the reference, so the result is the same softmax.  Most
+// tiles then skip the rescale of the O accumulator entirely.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Independent accumulator chains of the score product: one chain needs no
+// adds afterwards, and the interleaved softmax work covers its latency.
+#ifndef SPATTN_FWD_CHAINS
+#define SPATTN_FWD_CHAINS 1
+#endif
+constexpr int kChains = SPATTN_FWD_CHAINS;
+
+// Row maximum of one 32-key half, new reference, correction factor for the
+// state accumulated so far (1 when the reference is kept) and the exponent
+// offset -m_ref * scale_log2 of the probabilities.
+__device__ __forceinline__ void reference_update(const float* x, float& m_ref, float sl2, float& alpha, bool& moved,
+                                                 float& nms) {
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+  mx = pair_max(mx);
+  const float m_new = fmaxf(m_ref, mx);
+  moved = __ballot((m_new - m_ref) * sl2 > kRescaleLog2) != 0;  // -inf - -inf is NaN: false
+  const float m_next = moved ? m_new : m_ref;
+  alpha = m_next == m_ref ? 1.f : fast_exp2((m_ref - m_next) * sl2);
+  m_ref = m_next;
+  nms = -(m_ref == -__builtin_inff() ? 0.f : m_ref) * sl2;
+}
+
+// Probabilities of one half (in place), their sum, packed as the P^T operand.
+__device__ __forceinline__ float probs(float* x, float sl2, float nms, bf16x8& p0, bf16x8& p1) {
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[i] = fast_exp2(__builtin_fmaf(x[i], sl2, nms));
+    sum += x[i];
+  }
+  p0 = pack8(&x[0]);
+  p1 = pack8(&x[8]);
+  return sum;
+}
+
+template <int D>
+__device__ __forceinline__ void rescale(OnlineState<D>& st, float alpha) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.acc[dt][i] *= alpha;
+}
+
+// Per-lane byte offsets inside a swizzled K / V tile.  Row r and r + 32
+// (r + 16 for the transposing reads) share a swizzle, so one offset per
+// column block serves every 32-key half; the stage base is a compile-time
+// constant added on top.
+template <int D>
+struct LaneOffsets {
+  int k[D / 16];      // K row reads: row perm_row(l % 32), columns 16 kk + 8 g
+  int v[D / 32][2];   // V^T transposing reads: k rows 8 g + (l % 16) / 4 (+ 4)
+  __device__ __forceinline__ LaneOffsets(int lane) {
+    const int g = lane >> 5, grp = lane >> 4, j = lane & 15;
+    const int krow = perm_row(lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) k[kk] = 2 * tile_off<D>(krow, 16 * kk + 8 * g);
+    const int r = 8 * g + (j >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int col = 32 * dt + 16 * (grp & 1) + 4 * (j & 3);
+      v[dt][0] = 2 * tile_off<D>(r, col);
+      v[dt][1] = 2 * tile_off<D>(r + 4, col);
+    }
+  }
+  // Called at the top of every tile: makes the offsets opaque there, so the
+  // compiler folds each stage / half constant into the LDS instruction's
+  // immediate instead of keeping one hoisted register per combination.
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(k[kk]));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+v"(v[dt][0]), "+v"(v[dt][1]));
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void load_ka(bf16x8* ka, const bf16* ks, const LaneOffsets<D>& off, int row0) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    ka[kk] = *(const bf16x8*)((const char*)ks + off.k[kk] + row0 * D * 2);
+}
+// V^T operands of keys row0 .. row0 + 31: va[2 dt] covers k rows row0 .. +15,
+// va[2 dt + 1] rows row0 + 16 .. +31.
+template <int D>
+__device__ __forceinline__ void load_va(bf16x8* va, const bf16* vs, const LaneOffsets<D>& off, int row0) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const char* t = (const char*)vs + (row0 + 16 * h) * D * 2;
+      const bf16x4 a = lds_read_tr4((const bf16*)(t + off.v[dt][0]));
+      const bf16x4 b = lds_read_tr4((const bf16*)(t + off.v[dt][1]));
+      va[2 * dt + h] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+}
+template <int D>
+__device__ __forceinline__ void pv(OnlineState<D>& st, const bf16x8* va, bf16x8 p0, bf16x8 p1) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    st.acc[dt] = mfma32(va[2 * dt], p0, st.acc[dt]);
+    st.acc[dt] = mfma32(va[2 * dt + 1], p1, st.acc[dt]);
+  }
+}
+
+// Both 32-key halves of a tile meet the wave's rows.  Software-pipelined so
+// the exponentials of half 0 issue between the score MFMAs of half 1 and
+// those of half 1 between the PV MFMAs of half 0.  When `masked` (a
+// wave-uniform flag) the band mask is applied to both halves; the mask sits
+// between phases, so its branch does not split an interleaved phase.
+template <int D>
+__device__ __forceinline__ void tile_pair(OnlineState<D>& st, const bf16* ks, const bf16* vs,
+                                          const LaneOffsets<D>& off, const bf16x8* qreg, float sl2, bool masked,
+                                          int mbase, int width) {
+  constexpr int kKK = D / 16, kDT = D / 32;
+  // Phase boundaries are pinned (sched_barrier) so that operand reads of a
+  // later phase are not hoisted into an earlier one, where they would only
+  // lengthen register lifetimes.
+  bf16x8 ka[kKK];
+  load_ka<D>(ka, ks, off, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  const f32x16 s0 = mfma_ksum<kKK, kChains>(ka, qreg);
+  __builtin_amdgcn_sched_barrier(0);
+  load_ka<D>(ka, ks, off, 32);
+  float x0[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x0[i] = s0[i];
+  if (masked) band_mask(x0, mbase, width);
+  float alpha0, nms0;
+  bool moved0;
+  reference_update(x0, st.m_ref, sl2, alpha0, moved0, nms0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // scores of half 1 || probabilities of half 0
+  const f32x16 s1 = mfma_ksum<kKK, kChains>(ka, qreg);
+  bf16x8 pa0, pa1;
+  st.l_run = st.l_run * alpha0 + probs(x0, sl2, nms0, pa0, pa1);
+  keep_here(pa0);
+  keep_here(pa1);
+  interleave_mfma_valu<kKK, 16 / kKK, 48 / kKK>();
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 va[2 * kDT];
+  load_va<D>(va, vs, off, 0);  // in flight during the half-1 row maximum
+
+  float x1[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x1[i] = s1[i];
+  if (masked) band_mask(x1, mbase - 32, width);
+  float alpha1, nms1;
+  bool moved1;
+  reference_update(x1, st.m_ref, sl2, alpha1, moved1, nms1);
+  if (moved0) rescale<D>(st, alpha0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // PV of half 0 || probabilities of half 1
+  pv<D>(st, va, pa0, pa1);
+  bf16x8 pb0, pb1;
+  st.l_run = st.l_run * alpha1 + probs(x1, sl2, nms1, pb0, pb1);
+  keep_here(pb0);
+  keep_here(pb1);
+  interleave_mfma_valu<2 * kDT, 8 / kDT, 24 / kDT>();
+  __builtin_amdgcn_sched_barrier(0);
+  load_va<D>(va, vs, off, 32);
+  if (moved1) rescale<D>(st, alpha1);
+  __builtin_amdgcn_sched_barrier(0);
+  pv<D>(st, va, pb0, pb1);
+}
+
+// Only half m of the tile meets the wave's rows (always masked).
+template <int D>
+__device__ __forceinline__ void tile_half(OnlineState<D>& st, const bf16* ks, const bf16* vs,
+                                          const LaneOffsets<D>& off, const bf16x8* qreg, float sl2, int m, int mbase,
+                                          int width) {
+  constexpr int kKK = D / 16, kDT = D / 32;
+  bf16x8 ka[kKK];
+  load_ka<D>(ka, ks, off, 32 * m);
+  __builtin_amdgcn_sched_barrier(0);
+  const f32x16 s = mfma_ksum<kKK, kChains>(ka, qreg);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 va[2 * kDT];
+  load_va<D>(va, vs, off, 32 * m);
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = s[i];
+  band_mask(x, mbase - 32 * m, width);
+  float alpha, nms;
+  bool moved;
+  reference_update(x, st.m_ref, sl2, alpha, moved, nms);
+  bf16x8 p0, p1;
+  st.l_run = st.l_run * alpha + probs(x, sl2, nms, p0, p1);
+  if (moved) rescale<D>(st, alpha);
+  pv<D>(st, va, p0, p1);
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
@@ -105,127 +319,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
     qreg[kk] = iq < N ? *(const bf16x8*)(qb + (size_t)iq * D + 16 * kk + 8 * g) : bf16x8{};
 #pragma unroll
   for (int kk = 0; kk < kKK; ++kk) settle(qreg[kk]);
+  LaneOffsets<D> off(lane);
 
-  f32x16 acc[kDT];
+  OnlineState<D> st;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-  float m_run = ninf;  // running row maximum of the raw (unscaled) scores
-  float l_run = 0.f;   // this lane's share of the row sum
+    for (int i = 0; i < 16; ++i) st.acc[dt][i] = 0.f;
+  st.m_ref = ninf;
+  st.l_run = 0.f;
   const float sl2 = p.scale_log2;
+  const int width = hi - lo;
 
   Tile::load(smem, kb, u_begin * kBK, N, wave, lane);
   Tile::load(smem + kTile, vb, u_begin * kBK, N, wave, lane);
 
-  for (int u = u_begin; u < u_end; ++u) {
-    const int s = (u - u_begin) & 1;
+  // One tile from LDS stage S (a compile-time constant, so every LDS offset
+  // is an immediate).
+  auto step = [&](auto stage, int u) {
+    constexpr int S = decltype(stage)::value;
     wait_vmcnt<0>();  // this wave's part of tile u has landed
     __syncthreads();  // ... everyone's, and everyone is done with tile u - 1
     if (u + 1 < u_end) {
-      bf16* nxt = smem + (s ^ 1) * 2 * kTile;
+      bf16* nxt = smem + (S ^ 1) * 2 * kTile;
       Tile::load(nxt, kb, (u + 1) * kBK, N, wave, lane);
       Tile::load(nxt + kTile, vb, (u + 1) * kBK, N, wave, lane);
     }
-    const bf16* ks = smem + s * 2 * kTile;
+    const bf16* ks = smem + S * 2 * kTile;
     const bf16* vs = ks + kTile;
-
-    // Scores of both 32-key halves.  Operands are read in batches ahead of
-    // their products (sched_barrier keeps the compiler from interleaving each
-    // read with its MFMA, which would expose the LDS latency every time).
-    float x[2][16];
-    bool act[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int jb = u * kBK + 32 * m;
-      act[m] = wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi);
-      if (act[m]) {
-        const int krow = 32 * m + perm_row(c32);
-        bf16x8 ka[kKK];
-#pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) ka[kk] = row_chunk<D>(ks, krow, 16 * kk + 8 * g);
-        __builtin_amdgcn_sched_barrier(0);
-        const f32x16 sacc = mfma_ksum<kKK>(ka, qreg);
-        if (tile_full(iw0, iw1, jb, jb + 31, lo, hi)) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[m][i] = sacc[i];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int dist = iq - (jb + perm_reg_row(i, g));
-            x[m][i] = (dist >= lo && dist <= hi) ? sacc[i] : ninf;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[m][i] = ninf;
-      }
+    off.refresh();
+    const int jb = u * kBK;
+    const bool a0 = wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi);
+    const bool a1 = wave_live && tile_meets(iw0, iw1, jb + 32, jb + 63, lo, hi);
+    const int mbase = iq - jb - 8 * g - lo;
+    if (a0 && a1) {
+      tile_pair<D>(st, ks, vs, off, qreg, sl2, !tile_full(iw0, iw1, jb, jb + 63, lo, hi), mbase, width);
+    } else if (a0 || a1) {
+      tile_half<D>(st, ks, vs, off, qreg, sl2, a0 ? 0 : 1, mbase, width);
     }
-
-    if (act[0] || act[1]) {
-      // V^T operands of the first active half: in flight during the softmax.
-      const int m0 = act[0] ? 0 : 1;
-      bf16x8 va[2 * kDT];
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
-        va[2 * dt] = kmajor_operand<D>(vs, 32 * m0, 32 * dt, lane);
-        va[2 * dt + 1] = kmajor_operand<D>(vs, 32 * m0 + 16, 32 * dt, lane);
-      }
-      float mx = ninf;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[m][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == ninf ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * sl2);
-      const float nms = -m_use * sl2;
-      m_run = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          x[m][i] = fast_exp2(__builtin_fmaf(x[m][i], sl2, nms));
-          psum += x[m][i];
-        }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-
-      {
-        const bf16x8 pb0 = pack8(&x[m0][0]);
-        const bf16x8 pb1 = pack8(&x[m0][8]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          acc[dt] = mfma32(va[2 * dt], pb0, acc[dt]);
-          acc[dt] = mfma32(va[2 * dt + 1], pb1, acc[dt]);
-        }
-      }
-      if (m0 == 0 && act[1]) {
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          va[2 * dt] = kmajor_operand<D>(vs, 32, 32 * dt, lane);
-          va[2 * dt + 1] = kmajor_operand<D>(vs, 48, 32 * dt, lane);
-        }
-        const bf16x8 pb0 = pack8(&x[1][0]);
-        const bf16x8 pb1 = pack8(&x[1][8]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          acc[dt] = mfma32(va[2 * dt], pb0, acc[dt]);
-          acc[dt] = mfma32(va[2 * dt + 1], pb1, acc[dt]);
-        }
-      }
-    }
+  };
+  for (int u = u_begin; u < u_end; u += 2) {
+    step(std::integral_constant<int, 0>{}, u);
+    if (u + 1 < u_end) step(std::integral_constant<int, 1>{}, u + 1);
   }
 
   // ---- epilogue: O = acc / l, LSE = scale * m + ln(sum)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(st.l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (iq < N) {
 #pragma unroll
@@ -234,10 +373,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
       for (int a = 0; a < 4; ++a) {
         bf16x4 w;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) w[c] = (bf16)(acc[dt][4 * a + c] * inv);
+        for (int c = 0; c < 4; ++c) w[c] = (bf16)(st.acc[dt][4 * a + c] * inv);
         *(bf16x4*)(ob + (size_t)iq * D + 32 * dt + 8 * a + 4 * g) = w;
       }
-    if (g == 0) lb[iq] = l_tot > 0.f ? (m_run * sl2 + fast_log2(l_tot)) * kLn2 : ninf;
+    if (g == 0) lb[iq] = l_tot > 0.f ? (st.m_ref * sl2 + fast_log2(l_tot)) * kLn2 : ninf;
   }
 }
 
