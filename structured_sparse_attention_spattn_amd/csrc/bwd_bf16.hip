@@ -118,6 +118,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   if (row_ok && g == 0) p.dvec[(size_t)bh * N + iq] = dval;
   const float sl2 = p.scale_log2;
   const float scl = p.scale;
+  const float ndsc = -dval * scl;
   // exponent offset: P = exp2(s * sl2 - lse2), lse2 = LSE * log2(e)
   const float nlse2 = row_ok ? -p.lse[(size_t)bh * N + iq] * kLog2e : 0.f;
 #pragma unroll
@@ -163,15 +164,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
       const int jb = u * kDqBK;
       if (wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi)) {
         const int prow = perm_row(c32);
-        // S^T and dP^T as four independent MFMA chains (even / odd k-steps),
-        // operands read two k-steps at a time ahead of their products.
-        f32x16 s0, s1, p0, p1;
+        // S^T and dP^T as two single-accumulator MFMA chains issued
+        // alternately (a dependent chain costs nothing extra when another
+        // chain's products sit between its steps); operands are read two
+        // k-steps at a time ahead of their products.
+        f32x16 sacc, pacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          s0[i] = 0.f;
-          s1[i] = 0.f;
-          p0[i] = 0.f;
-          p1[i] = 0.f;
+          sacc[i] = 0.f;
+          pacc[i] = 0.f;
         }
 #pragma unroll
         for (int kk = 0; kk < kKK; kk += 2) {
@@ -180,16 +181,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
           const bf16x8 va0 = row_chunk<D>(vs, prow, 16 * kk + 8 * g);
           const bf16x8 va1 = row_chunk<D>(vs, prow, 16 * kk + 16 + 8 * g);
           __builtin_amdgcn_sched_barrier(0);
-          s0 = mfma32(ka0, qreg[kk], s0);
-          p0 = mfma32(va0, doreg[kk], p0);
-          s1 = mfma32(ka1, qreg[kk + 1], s1);
-          p1 = mfma32(va1, doreg[kk + 1], p1);
-        }
-        f32x16 sacc, pacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[i] = s0[i] + s1[i];
-          pacc[i] = p0[i] + p1[i];
+          sacc = mfma32(ka0, qreg[kk], sacc);
+          pacc = mfma32(va0, doreg[kk], pacc);
+          sacc = mfma32(ka1, qreg[kk + 1], sacc);
+          pacc = mfma32(va1, doreg[kk + 1], pacc);
         }
         // K^T operands of dQ^T += K^T dS^T, in flight during the dS math
         bf16x8 kt[2 * kDT];
@@ -198,18 +193,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
           kt[2 * dt] = kmajor_operand<D>(ks, 0, 32 * dt, lane);
           kt[2 * dt + 1] = kmajor_operand<D>(ks, 16, 32 * dt, lane);
         }
+        // dS = P (dP - D) scale, with (dP - D) scale as one FMA
         float ds[16];
         if (tile_full(iw0, iw1, jb, jb + 31, lo, hi)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            ds[i] = fast_exp2(__builtin_fmaf(sacc[i], sl2, nlse2)) * (pacc[i] - dval) * scl;
+            ds[i] = fast_exp2(__builtin_fmaf(sacc[i], sl2, nlse2)) * __builtin_fmaf(pacc[i], scl, ndsc);
         } else {
+          const int mb = iq - jb - 8 * g - lo;  // (iq - key - lo) + c for register i
+          const uint32_t width = (uint32_t)(hi - lo);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int dist = iq - (jb + perm_reg_row(i, g));
-            const bool ok = row_ok && dist >= lo && dist <= hi;
+            const int c = ((i >> 3) << 4) + (i & 7);  // perm_reg_row(i, 0)
             const float pe = fast_exp2(__builtin_fmaf(sacc[i], sl2, nlse2));
-            ds[i] = ok ? pe * (pacc[i] - dval) * scl : 0.f;
+            ds[i] = (uint32_t)(mb - c) <= width && row_ok ? pe * __builtin_fmaf(pacc[i], scl, ndsc) : 0.f;
           }
         }
         const bf16x8 d0 = pack8(&ds[0]), d1 = pack8(&ds[8]);
@@ -237,17 +234,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
 
 // =====================================================================  dK dV
 // Warp-specialised: 4 waves, 64 keys, two workgroups per CU.  Wave w < 2
-// ("P wave") owns keys 32w .. 32w+31 of the tile: S = Q K^T, P, and
-// dV += P^T dO.  Wave w + 2 ("dS wave") owns the same keys: dP = dO V^T, then
-// -- with P handed over through LDS -- dS = P (dP - D) and dK += dS^T Q.  Each
-// wave keeps a single 32 x d accumulator; the two workgroups on a CU run
-// their barrier-separated phases independently, so one's LDS reads overlap
-// the other's matrix products.
+// ("P wave") owns keys 32w .. 32w+31 of the tile: S = Q K^T, P -- handed to
+// its partner through LDS -- and dV += P^T dO.  Wave w + 2 ("dS wave") owns
+// the same keys: dP = dO V^T for the current query block and, one block
+// behind, dS = P (dP - D) and dK += dS^T Q with the P its partner handed over
+// in the previous iteration.  The lag leaves one barrier per block and no
+// wait of one role on the other inside it: P is double-buffered by block
+// parity, and the ring keeps the previous block's Q tile until the dS wave
+// is done with it (blocks tq - 1 .. tq + 2 occupy the four stages).  Each
+// wave keeps a single 32 x d accumulator.
 constexpr int kKvBK = 64;     // key rows per workgroup
 constexpr int kKvQB = 32;     // query rows per stage
-constexpr int kKvStages = 4;  // LDS ring depth: blocks tq+1 .. tq+3 load while tq is used
+constexpr int kKvStages = 4;  // LDS ring depth
+constexpr int kKvAhead = 2;   // blocks tq + 1 .. tq + kKvAhead in flight while tq is used
 constexpr int kKvThreads = 256;
 constexpr int kKvPairs = kKvThreads / 128;
+static_assert(kKvAhead + 2 <= kKvStages, "ring holds the lagging block, the current one and the prefetched ones");
+
+typedef _Float16 f16;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+// Eight values as float16 (round toward zero; P lies in [0, 1]).
+__device__ __forceinline__ f16x8 pack8_f16(const float* x) {
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const auto h2 = __builtin_amdgcn_cvt_pkrtz(x[j], x[j + 1]);
+    r[j] = h2[0];
+    r[j + 1] = h2[1];
+  }
+  return r;
+}
 
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
@@ -260,8 +277,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) bf16 smem[kKvStages * 2 * kTile];  // [stage][Q, dO]
   // [stage][wave][LSE of the 32 rows | D of the 32 rows]: every wave loads its own copy
   __shared__ __attribute__((aligned(16))) float rowv[kKvStages][kWaves][2 * kKvQB];
-  // P handed from P wave w to dS wave w + kKvPairs: [w][lane][16 floats]
-  __shared__ __attribute__((aligned(16))) float pbuf[kKvPairs][64][16];
+  // P from P wave w to dS wave w + kKvPairs: [block parity][w][lane][16 values]
+  __shared__ __attribute__((aligned(16))) f16 pbuf[2][kKvPairs][64][16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -326,108 +343,142 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr(&rowv[st][wave][0])), src);
     };
 #pragma unroll
-    for (int i = 0; i < kKvStages - 1; ++i)
+    for (int i = 0; i < kKvAhead; ++i)
       if (tq_begin + i < tq_end) issue(tq_begin + i);
-    for (int tq = tq_begin; tq < tq_end; ++tq) {
-      const int ahead = tq_end - 1 - tq;  // blocks issued after tq (at most kKvStages - 2 in flight)
-      static_assert(kKvStages == 4, "the wait ladder below assumes a 4-deep ring");
-      if (ahead >= 2)
-        wait_vmcnt<2 * kL>();
-      else if (ahead == 1)
+    const int prow = perm_row(c32);
+    // per-lane row values of the 16 rows this lane holds: 16 (r / 8) + 8 g + (r % 8)
+    auto rows16 = [&](const float* v, float* out) {
+      const f32x4 a = *(const f32x4*)&v[8 * g], b = *(const f32x4*)&v[8 * g + 4];
+      const f32x4 c = *(const f32x4*)&v[16 + 8 * g], d = *(const f32x4*)&v[20 + 8 * g];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        out[e] = a[e];
+        out[4 + e] = b[e];
+        out[8 + e] = c[e];
+        out[12 + e] = d[e];
+      }
+    };
+    // dS wave, block tq (one iteration late): dS = P (dP - D) scale and
+    // dK += dS^T Q.  P comes masked from the P wave (0 outside the band and
+    // on rows past N), so no mask is needed here.
+    auto ds_dk = [&](int tq, const f32x16& dpv) {
+      const int st = (tq - tq_begin) % kKvStages;
+      const bf16* qs = smem + st * 2 * kTile;
+      bf16x8 bb[2 * kDT];
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) {
+        bb[2 * dt] = kmajor_operand<D>(qs, 0, 32 * dt, lane);
+        bb[2 * dt + 1] = kmajor_operand<D>(qs, 16, 32 * dt, lane);
+      }
+      float dd[16], ds[16];
+      rows16(&rowv[st][wave][kKvQB], dd);
+      const f16x8* src = (const f16x8*)&pbuf[(tq - tq_begin) & 1][kw][lane][0];
+      const f16x8 pa = src[0], pb = src[1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ds[i] = (float)pa[i] * __builtin_fmaf(dpv[i], scl, -dd[i] * scl);
+        ds[8 + i] = (float)pb[i] * __builtin_fmaf(dpv[8 + i], scl, -dd[8 + i] * scl);
+      }
+      const bf16x8 op0 = pack8(&ds[0]), op1 = pack8(&ds[8]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op0, bb[2 * dt], acc[dt]);
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op1, bb[2 * dt + 1], acc[dt]);
+    };
+
+    // Top of every iteration, for both roles (same barrier sequence): wait for
+    // this wave's loads of block tq (those of tq + 1 may stay in flight), then
+    // the barrier -- block tq complete for everyone, iteration tq - 1 finished
+    // everywhere, so the stage of block tq - 2 is free and the P of block
+    // tq - 1 is visible -- then prefetch block tq + kKvAhead.
+    auto block_start = [&](int tq) {
+      if (tq + 1 < tq_end)
         wait_vmcnt<kL>();
       else
         wait_vmcnt<0>();
-      __syncthreads();  // block tq complete for everyone; block tq - 1 released
-      if (tq + kKvStages - 1 < tq_end) issue(tq + kKvStages - 1);
-      const int s = (tq - tq_begin) % kKvStages;
-      const bf16* qs = smem + s * 2 * kTile;
-      const bf16* dos = qs + kTile;
-      const float* rv = &rowv[s][wave][0];
+      __syncthreads();
+      if (tq + kKvAhead < tq_end) issue(tq + kKvAhead);
+    };
+    auto block_act = [&](int tq) {
       const int i0 = tq * kKvQB;
-      const int i1 = min(N - 1, i0 + kKvQB - 1);
-      const bool act = wave_live && tile_meets(i0, i1, kw0, kw1, lo, hi);
-      const bool full = wave_keys_full && i0 + kKvQB - 1 <= N - 1 && tile_full(i0, i1, kw0, kw1, lo, hi);
-      const int prow = perm_row(c32);
-      // per-lane row values of the 16 rows this lane holds: 16 (r / 8) + 8 g + (r % 8)
-      auto rows16 = [&](const float* v, float* out) {
-        const f32x4 a = *(const f32x4*)&v[8 * g], b = *(const f32x4*)&v[8 * g + 4];
-        const f32x4 c = *(const f32x4*)&v[16 + 8 * g], d = *(const f32x4*)&v[20 + 8 * g];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          out[e] = a[e];
-          out[4 + e] = b[e];
-          out[8 + e] = c[e];
-          out[12 + e] = d[e];
-        }
-      };
-      // ---- phase 1: P waves S -> P (handed over); dS waves dP
-      bf16x8 op0{}, op1{};  // packed P (P waves) or dS (dS waves)
-      f32x16 sc_;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc_[i] = 0.f;
-      if (act) {
-        const bf16* at = pwave ? qs : dos;
+      return wave_live && tile_meets(i0, min(N - 1, i0 + kKvQB - 1), kw0, kw1, lo, hi);
+    };
+
+    if (pwave) {
+      for (int tq = tq_begin; tq < tq_end; ++tq) {
+        block_start(tq);
+        if (!block_act(tq)) continue;
+        const int s = (tq - tq_begin) % kKvStages;
+        const bf16* qs = smem + s * 2 * kTile;
+        const bf16* dos = qs + kTile;
+        const int i0 = tq * kKvQB;
+        const int i1 = min(N - 1, i0 + kKvQB - 1);
+        const bool full = wave_keys_full && i0 + kKvQB - 1 <= N - 1 && tile_full(i0, i1, kw0, kw1, lo, hi);
         bf16x8 aa[kKK];
 #pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(at, prow, 16 * kk + 8 * g);
+        for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(qs, prow, 16 * kk + 8 * g);
         __builtin_amdgcn_sched_barrier(0);
-        sc_ = mfma_ksum<kKK>(aa, bop);
-        if (pwave) {
-          float nl[16], pv[16];
-          rows16(rv, nl);
-          if (full) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
-          } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = perm_reg_row(i, g);
-              const int dist = i0 + r - kj;
-              const bool ok = key_ok && i0 + r < N && dist >= lo && dist <= hi;
-              const float pe = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
-              pv[i] = ok ? pe : 0.f;
-            }
-          }
-          f32x4* dst = (f32x4*)&pbuf[kw][lane][0];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = f32x4{pv[4 * e], pv[4 * e + 1], pv[4 * e + 2], pv[4 * e + 3]};
-          op0 = pack8(&pv[0]);
-          op1 = pack8(&pv[8]);
-        }
-      }
-      __syncthreads();  // P of this block visible to the dS waves
-      // ---- phase 2: P waves dV += P^T dO; dS waves dS, dK += dS^T Q
-      if (act) {
-        const bf16* bt = pwave ? dos : qs;
+        const f32x16 sc_ = mfma_ksum<kKK, 1>(aa, bop);
+        __builtin_amdgcn_sched_barrier(0);
         bf16x8 bb[2 * kDT];
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          bb[2 * dt] = kmajor_operand<D>(bt, 0, 32 * dt, lane);
-          bb[2 * dt + 1] = kmajor_operand<D>(bt, 16, 32 * dt, lane);
+          bb[2 * dt] = kmajor_operand<D>(dos, 0, 32 * dt, lane);
+          bb[2 * dt + 1] = kmajor_operand<D>(dos, 16, 32 * dt, lane);
         }
-        if (!pwave) {
-          float dd[16], pv[16], ds[16];
-          rows16(rv + kKvQB, dd);
-          const f32x4* src = (const f32x4*)&pbuf[kw][lane][0];
+        float nl[16], pv[16];
+        rows16(&rowv[s][wave][0], nl);
+        if (full) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const f32x4 t = src[e];
-            pv[4 * e] = t[0];
-            pv[4 * e + 1] = t[1];
-            pv[4 * e + 2] = t[2];
-            pv[4 * e + 3] = t[3];
+          for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
+        } else {
+          const int mb = kj + lo - i0;  // query row r is in band iff 0 <= r - mb <= hi - lo
+          const uint32_t width = (uint32_t)(hi - lo);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = perm_reg_row(i, g);
+            const bool ok = key_ok && i0 + r < N && (uint32_t)(r - mb) <= width;
+            const float pe = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
+            pv[i] = ok ? pe : 0.f;
           }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ds[i] = pv[i] * (sc_[i] - dd[i]) * scl;
-          op0 = pack8(&ds[0]);
-          op1 = pack8(&ds[8]);
         }
+        f16x8* dst = (f16x8*)&pbuf[(tq - tq_begin) & 1][kw][lane][0];
+        dst[0] = pack8_f16(&pv[0]);
+        dst[1] = pack8_f16(&pv[8]);
+        const bf16x8 op0 = pack8(&pv[0]), op1 = pack8(&pv[8]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op0, bb[2 * dt], acc[dt]);
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op1, bb[2 * dt + 1], acc[dt]);
       }
+      __syncthreads();  // matches the dS waves' final barrier
+    } else {
+      f32x16 dp_prev;  // dP of the previous block
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp_prev[i] = 0.f;
+      bool act_prev = false;
+      for (int tq = tq_begin; tq < tq_end; ++tq) {
+        block_start(tq);
+        const bool act = block_act(tq);
+        f32x16 dp_cur;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp_cur[i] = 0.f;
+        if (act) {
+          const bf16* dos = smem + ((tq - tq_begin) % kKvStages) * 2 * kTile + kTile;
+          bf16x8 aa[kKK];
+#pragma unroll
+          for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(dos, prow, 16 * kk + 8 * g);
+          __builtin_amdgcn_sched_barrier(0);
+          dp_cur = mfma_ksum<kKK, 1>(aa, bop);
+        }
+        if (act_prev) ds_dk(tq - 1, dp_prev);
+        dp_prev = dp_cur;
+        act_prev = act;
+      }
+      __syncthreads();  // P of the last block visible
+      if (act_prev) ds_dk(tq_end - 1, dp_prev);
     }
   }
 
