@@ -46,18 +46,6 @@ struct BwdArgs {
   Bands bands;
 };
 
-// Store 4 consecutive float values as bf16 or f32.
-__device__ __forceinline__ void store4(void* base, size_t idx, const float* x, bool f32) {
-  if (f32) {
-    *(f32x4*)((float*)base + idx) = f32x4{x[0], x[1], x[2], x[3]};
-  } else {
-    bf16x4 w;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) w[c] = (bf16)x[c];
-    *(bf16x4*)((bf16*)base + idx) = w;
-  }
-}
-
 // =====================================================================  dQ
 constexpr int kDqBQ = 128;    // query rows per workgroup
 constexpr int kDqBK = 32;     // key rows per stage
@@ -97,6 +85,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const int iq = iw0 + c32;
   const bool row_ok = iq < N;
 
+  const int i_tile1 = min(N - 1, i_tile0 + kDqBQ - 1);
+  const KeySpan span = band_key_span(i_tile0, i_tile1, lo, hi);
+  const bool any_key = span.last >= span.first;
+  const int u_begin = any_key ? span.first / kDqBK : 0;
+  const int u_end = any_key ? span.last / kDqBK + 1 : 0;
+  auto issue = [&](int u) {
+    bf16* st = smem + ((u - u_begin) % kDqStages) * 2 * kTile;
+    Tile::load(st, kb, u * kDqBK, N, wave, lane);
+    Tile::load(st + kTile, vb, u * kDqBK, N, wave, lane);
+  };
+  // Ring prefill first: its round trip overlaps that of the row loads below
+  // (the wait for those covers both).
+#pragma unroll
+  for (int i = 0; i < kDqStages - 1; ++i)
+    if (u_begin + i < u_end) issue(u_begin + i);
+
   // Q and dO operands; D_i = dO_i . O_i from the same lanes.
   bf16x8 qreg[kKK], doreg[kKK];
   float dpart = 0.f;
@@ -129,26 +133,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   settle(nlse2);
   settle(dval);
 
-  const int i_tile1 = min(N - 1, i_tile0 + kDqBQ - 1);
-  const KeySpan span = band_key_span(i_tile0, i_tile1, lo, hi);
-
   f32x16 acc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  if (span.last >= span.first) {
-    const int u_begin = span.first / kDqBK;
-    const int u_end = span.last / kDqBK + 1;
-    auto issue = [&](int u) {
-      bf16* st = smem + ((u - u_begin) % kDqStages) * 2 * kTile;
-      Tile::load(st, kb, u * kDqBK, N, wave, lane);
-      Tile::load(st + kTile, vb, u * kDqBK, N, wave, lane);
-    };
-#pragma unroll
-    for (int i = 0; i < kDqStages - 1; ++i)
-      if (u_begin + i < u_end) issue(u_begin + i);
+  if (any_key) {
+    LaneOffsets<D> off(lane);
     for (int u = u_begin; u < u_end; ++u) {
       const int ahead = u_end - 1 - u;  // tiles issued after u and possibly in flight
       if (ahead >= 2)
@@ -161,52 +153,48 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
       if (u + kDqStages - 1 < u_end) issue(u + kDqStages - 1);
       const bf16* ks = smem + ((u - u_begin) % kDqStages) * 2 * kTile;
       const bf16* vs = ks + kTile;
+      off.refresh();
       const int jb = u * kDqBK;
       if (wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi)) {
-        const int prow = perm_row(c32);
-        // S^T and dP^T as two single-accumulator MFMA chains issued
-        // alternately (a dependent chain costs nothing extra when another
-        // chain's products sit between its steps); operands are read two
-        // k-steps at a time ahead of their products.
-        f32x16 sacc, pacc;
+        // S^T first, then dP^T with the exponentials of S^T issued between
+        // its products (one accumulator chain each; a dependent chain costs
+        // nothing extra when other work sits between its steps).
+        bf16x8 opa[kKK];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[i] = 0.f;
-          pacc[i] = 0.f;
-        }
+        for (int kk = 0; kk < kKK; ++kk) opa[kk] = *(const bf16x8*)((const char*)ks + off.k[kk]);
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x16 sacc = mfma_ksum<kKK, 1>(opa, qreg);
 #pragma unroll
-        for (int kk = 0; kk < kKK; kk += 2) {
-          const bf16x8 ka0 = row_chunk<D>(ks, prow, 16 * kk + 8 * g);
-          const bf16x8 ka1 = row_chunk<D>(ks, prow, 16 * kk + 16 + 8 * g);
-          const bf16x8 va0 = row_chunk<D>(vs, prow, 16 * kk + 8 * g);
-          const bf16x8 va1 = row_chunk<D>(vs, prow, 16 * kk + 16 + 8 * g);
+        for (int kk = 0; kk < kKK; ++kk) opa[kk] = *(const bf16x8*)((const char*)vs + off.k[kk]);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 pacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pacc[i] = 0.f;
+        float pe[16];
+        // fixed order: one dP^T product, then its share of the exponentials
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) {
+          pacc = mfma32(opa[kk], doreg[kk], pacc);
+#pragma unroll
+          for (int i = kk * 16 / kKK; i < (kk + 1) * 16 / kKK; ++i)
+            pe[i] = fast_exp2(__builtin_fmaf(sacc[i], sl2, nlse2));
           __builtin_amdgcn_sched_barrier(0);
-          sacc = mfma32(ka0, qreg[kk], sacc);
-          pacc = mfma32(va0, doreg[kk], pacc);
-          sacc = mfma32(ka1, qreg[kk + 1], sacc);
-          pacc = mfma32(va1, doreg[kk + 1], pacc);
         }
         // K^T operands of dQ^T += K^T dS^T, in flight during the dS math
         bf16x8 kt[2 * kDT];
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          kt[2 * dt] = kmajor_operand<D>(ks, 0, 32 * dt, lane);
-          kt[2 * dt + 1] = kmajor_operand<D>(ks, 16, 32 * dt, lane);
-        }
-        // dS = P (dP - D) scale, with (dP - D) scale as one FMA
+        load_va<D>(kt, ks, off, 0);
+        // dS = P (dP - D) scale, with (dP - D) scale as one FMA; on a partial
+        // tile the band is applied by selection (P may overflow out of band)
         float ds[16];
-        if (tile_full(iw0, iw1, jb, jb + 31, lo, hi)) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            ds[i] = fast_exp2(__builtin_fmaf(sacc[i], sl2, nlse2)) * __builtin_fmaf(pacc[i], scl, ndsc);
-        } else {
+        for (int i = 0; i < 16; ++i) ds[i] = pe[i] * __builtin_fmaf(pacc[i], scl, ndsc);
+        if (!tile_full(iw0, iw1, jb, jb + 31, lo, hi)) {
           const int mb = iq - jb - 8 * g - lo;  // (iq - key - lo) + c for register i
           const uint32_t width = (uint32_t)(hi - lo);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int c = ((i >> 3) << 4) + (i & 7);  // perm_reg_row(i, 0)
-            const float pe = fast_exp2(__builtin_fmaf(sacc[i], sl2, nlse2));
-            ds[i] = (uint32_t)(mb - c) <= width && row_ok ? pe * __builtin_fmaf(pacc[i], scl, ndsc) : 0.f;
+            ds[i] = (uint32_t)(mb - c) <= width && row_ok ? ds[i] : 0.f;
           }
         }
         const bf16x8 d0 = pack8(&ds[0]), d1 = pack8(&ds[8]);
@@ -220,15 +208,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
     }
   }
 
-  if (row_ok) {
-    const bool f32 = p.grad_f32 != 0;
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float x4[4] = {acc[dt][4 * a], acc[dt][4 * a + 1], acc[dt][4 * a + 2], acc[dt][4 * a + 3]};
-        store4(p.dq, base + (size_t)iq * D + 32 * dt + 8 * a + 4 * g, x4, f32);
-      }
+  __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
+  if (wave_live) {
+    float* stg = (float*)smem + wave * 32 * D;
+    stage_transposed<D>(stg, acc, 1.f, lane);
+    store_staged<D>(stg, p.dq, (size_t)bh * N + iw0, min(32, N - iw0), p.grad_f32 != 0, lane);
   }
 }
 
@@ -319,16 +303,6 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 
   const KeySpan qspan = band_query_span(j0, j1, lo, hi, N);
   if (qspan.last >= qspan.first) {
-    // B operand of this wave's score product: K rows (P wave) or V rows (dS wave)
-    bf16x8 bop[kKK];
-    {
-      const bf16* src = pwave ? p.k : p.v;
-#pragma unroll
-      for (int kk = 0; kk < kKK; ++kk)
-        bop[kk] = key_ok ? *(const bf16x8*)(src + base + (size_t)kj * D + 16 * kk + 8 * g) : bf16x8{};
-#pragma unroll
-      for (int kk = 0; kk < kKK; ++kk) settle(bop[kk]);
-    }
     const float sl2 = p.scale_log2;
     const float scl = p.scale;
     const int tq_begin = qspan.first / kKvQB;
@@ -342,9 +316,20 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       const float* src = lane < 32 ? lseb + i : ddb + i;
       lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr(&rowv[st][wave][0])), src);
     };
+    // Ring prefill first: its round trip overlaps that of the row loads below.
 #pragma unroll
     for (int i = 0; i < kKvAhead; ++i)
       if (tq_begin + i < tq_end) issue(tq_begin + i);
+    // B operand of this wave's score product: K rows (P wave) or V rows (dS wave)
+    bf16x8 bop[kKK];
+    {
+      const bf16* src = pwave ? p.k : p.v;
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk)
+        bop[kk] = key_ok ? *(const bf16x8*)(src + base + (size_t)kj * D + 16 * kk + 8 * g) : bf16x8{};
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) settle(bop[kk]);
+    }
     const int prow = perm_row(c32);
     // per-lane row values of the 16 rows this lane holds: 16 (r / 8) + 8 g + (r % 8)
     auto rows16 = [&](const float* v, float* out) {
@@ -406,54 +391,88 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
     };
 
     if (pwave) {
+      // dV += P^T dO runs one block late as well, so the exponentials of
+      // block tq issue between the dV products of block tq - 1 (whose dO tile
+      // the ring still holds for the dS wave's Q).
+      LaneOffsets<D> off(lane);
+      bf16x8 pp0{}, pp1{};  // packed P of the previous block
+      bool act_prev = false;
+      auto dv_operands = [&](int tq, bf16x8* bb) {
+        const bf16* dos = smem + ((tq - tq_begin) % kKvStages) * 2 * kTile + kTile;
+        load_va<D>(bb, dos, off, 0);
+      };
+      auto dv_update = [&](const bf16x8* bb, bf16x8 p0, bf16x8 p1) {
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(p0, bb[2 * dt], acc[dt]);
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(p1, bb[2 * dt + 1], acc[dt]);
+      };
       for (int tq = tq_begin; tq < tq_end; ++tq) {
         block_start(tq);
-        if (!block_act(tq)) continue;
-        const int s = (tq - tq_begin) % kKvStages;
-        const bf16* qs = smem + s * 2 * kTile;
-        const bf16* dos = qs + kTile;
-        const int i0 = tq * kKvQB;
-        const int i1 = min(N - 1, i0 + kKvQB - 1);
-        const bool full = wave_keys_full && i0 + kKvQB - 1 <= N - 1 && tile_full(i0, i1, kw0, kw1, lo, hi);
-        bf16x8 aa[kKK];
+        off.refresh();
+        const bool act = block_act(tq);
+        if (act) {
+          const int s = (tq - tq_begin) % kKvStages;
+          const bf16* qs = smem + s * 2 * kTile;
+          const int i0 = tq * kKvQB;
+          const int i1 = min(N - 1, i0 + kKvQB - 1);
+          bf16x8 aa[kKK];
+          load_ka<D>(aa, qs, off, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          const f32x16 sc_ = mfma_ksum<kKK, 1>(aa, bop);
+          __builtin_amdgcn_sched_barrier(0);
+          float nl[16], pv[16];
+          rows16(&rowv[s][wave][0], nl);
+          if (act_prev) {
+            bf16x8 bb[2 * kDT];
+            dv_operands(tq - 1, bb);
+            // fixed order: one dV product of block tq - 1, then its share of
+            // the exponentials of block tq
 #pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(qs, prow, 16 * kk + 8 * g);
-        __builtin_amdgcn_sched_barrier(0);
-        const f32x16 sc_ = mfma_ksum<kKK, 1>(aa, bop);
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 bb[2 * kDT];
+            for (int m = 0; m < 2 * kDT; ++m) {
+              const int dt = m % kDT;
+              acc[dt] = mfma32(m < kDT ? pp0 : pp1, bb[2 * dt + (m < kDT ? 0 : 1)], acc[dt]);
 #pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          bb[2 * dt] = kmajor_operand<D>(dos, 0, 32 * dt, lane);
-          bb[2 * dt + 1] = kmajor_operand<D>(dos, 16, 32 * dt, lane);
-        }
-        float nl[16], pv[16];
-        rows16(&rowv[s][wave][0], nl);
-        if (full) {
+              for (int i = m * 16 / (2 * kDT); i < (m + 1) * 16 / (2 * kDT); ++i)
+                pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
-        } else {
-          const int mb = kj + lo - i0;  // query row r is in band iff 0 <= r - mb <= hi - lo
-          const uint32_t width = (uint32_t)(hi - lo);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = perm_reg_row(i, g);
-            const bool ok = key_ok && i0 + r < N && (uint32_t)(r - mb) <= width;
-            const float pe = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
-            pv[i] = ok ? pe : 0.f;
+            for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
           }
+          const bool full = wave_keys_full && i0 + kKvQB - 1 <= N - 1 && tile_full(i0, i1, kw0, kw1, lo, hi);
+          if (!full) {
+            // band applied by selection (P may overflow out of band)
+            const int mb = kj + lo - i0;  // query row r is in band iff 0 <= r - mb <= hi - lo
+            const uint32_t width = (uint32_t)(hi - lo);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int r = perm_reg_row(i, g);
+              const bool ok = key_ok && i0 + r < N && (uint32_t)(r - mb) <= width;
+              pv[i] = ok ? pv[i] : 0.f;
+            }
+          }
+          f16x8* dst = (f16x8*)&pbuf[(tq - tq_begin) & 1][kw][lane][0];
+          dst[0] = pack8_f16(&pv[0]);
+          dst[1] = pack8_f16(&pv[8]);
+          pp0 = pack8(&pv[0]);
+          pp1 = pack8(&pv[8]);
+        } else if (act_prev) {
+          bf16x8 bb[2 * kDT];
+          dv_operands(tq - 1, bb);
+          __builtin_amdgcn_sched_barrier(0);
+          dv_update(bb, pp0, pp1);
         }
-        f16x8* dst = (f16x8*)&pbuf[(tq - tq_begin) & 1][kw][lane][0];
-        dst[0] = pack8_f16(&pv[0]);
-        dst[1] = pack8_f16(&pv[8]);
-        const bf16x8 op0 = pack8(&pv[0]), op1 = pack8(&pv[8]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op0, bb[2 * dt], acc[dt]);
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op1, bb[2 * dt + 1], acc[dt]);
+        act_prev = act;
       }
       __syncthreads();  // matches the dS waves' final barrier
+      if (act_prev) {
+        bf16x8 bb[2 * kDT];
+        dv_operands(tq_end - 1, bb);
+        __builtin_amdgcn_sched_barrier(0);
+        dv_update(bb, pp0, pp1);
+      }
     } else {
       f32x16 dp_prev;  // dP of the previous block
 #pragma unroll
@@ -482,23 +501,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
     }
   }
 
-  // dV (P waves) or dK (dS waves) rows: key kw0 + 8a + 4g + c, features 32dt + c32.
+  // dV (P waves) or dK (dS waves) rows kw0 .. kw0 + 31
+  __syncthreads();  // ring and P buffers no longer read: the ring becomes the output staging area
   if (wave_live) {
-    const bool f32 = p.grad_f32 != 0;
-    void* dst = pwave ? p.dv : p.dk;
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = kw0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (j < N) {
-          const size_t idx = base + (size_t)j * D + 32 * dt + c32;
-          if (f32)
-            ((float*)dst)[idx] = acc[dt][i];
-          else
-            ((bf16*)dst)[idx] = (bf16)acc[dt][i];
-        }
-      }
+    float* stg = (float*)smem + wave * 32 * D;
+    stage_direct<D>(stg, acc, lane);
+    store_staged<D>(stg, pwave ? p.dv : p.dk, (size_t)bh * N + kw0, min(32, N - kw0), p.grad_f32 != 0, lane);
   }
 }
 

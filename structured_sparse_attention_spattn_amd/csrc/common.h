@@ -123,6 +123,61 @@ __device__ __forceinline__ bf16x8 kmajor16_operand(const bf16* tile, int kbase, 
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Per-lane byte offsets inside a swizzled [rows][D] tile for the two operand
+// reads of the 32x32x16 products: 16-byte row reads under perm_row (the row
+// operand) and the transposing reads of kmajor_operand (the k-major operand).
+// Rows r and r + 32 (r + 16 for the transposing reads) share a swizzle, so
+// one offset per column block serves every 32-row half; tile and stage bases
+// are added on top.
+template <int D>
+struct LaneOffsets {
+  int k[D / 16];      // row reads: row perm_row(l % 32), columns 16 kk + 8 g
+  int v[D / 32][2];   // transposing reads: k rows 8 g + (l % 16) / 4 (+ 4), column block dt
+  __device__ __forceinline__ LaneOffsets(int lane) {
+    const int g = lane >> 5, grp = lane >> 4, j = lane & 15;
+    const int krow = perm_row(lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) k[kk] = 2 * tile_off<D>(krow, 16 * kk + 8 * g);
+    const int r = 8 * g + (j >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int col = 32 * dt + 16 * (grp & 1) + 4 * (j & 3);
+      v[dt][0] = 2 * tile_off<D>(r, col);
+      v[dt][1] = 2 * tile_off<D>(r + 4, col);
+    }
+  }
+  // Called at the top of every tile: makes the offsets opaque there, so the
+  // compiler folds each stage / half constant into the LDS instruction's
+  // immediate instead of keeping one hoisted register per combination.
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(k[kk]));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+v"(v[dt][0]), "+v"(v[dt][1]));
+  }
+};
+
+// Row operands (A of S^T = K Q^T): rows row0 + perm_row(l % 32), k-steps 0 .. D/16 - 1.
+template <int D>
+__device__ __forceinline__ void load_ka(bf16x8* ka, const bf16* ks, const LaneOffsets<D>& off, int row0) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    ka[kk] = *(const bf16x8*)((const char*)ks + off.k[kk] + row0 * D * 2);
+}
+// k-major operands over tile rows row0 .. row0 + 31 (k) for every 32-column
+// block dt: va[2 dt] covers k rows row0 .. +15, va[2 dt + 1] rows row0 + 16 .. +31.
+template <int D>
+__device__ __forceinline__ void load_va(bf16x8* va, const bf16* vs, const LaneOffsets<D>& off, int row0) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const char* t = (const char*)vs + (row0 + 16 * h) * D * 2;
+      const bf16x4 a = lds_read_tr4((const bf16*)(t + off.v[dt][0]));
+      const bf16x4 b = lds_read_tr4((const bf16*)(t + off.v[dt][1]));
+      va[2 * dt + h] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+}
 // 16-byte row read (8 consecutive columns from col, col % 8 == 0).
 template <int D>
 __device__ __forceinline__ bf16x8 row_chunk(const bf16* tile, int r, int col) {
@@ -290,6 +345,66 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) r[j] = (bf16)x[j];
   return r;
+}
+
+// -------------------------------------------------------------- epilogue
+// A wave's 32 x D float32 result tile is staged in LDS and written out as
+// whole rows: the MFMA accumulator layout would otherwise send 2- to 8-byte
+// pieces of 32 different rows per store instruction.  Staging layout: D floats
+// per row, the 16-byte chunks of row r XOR-permuted by r & 15, which keeps
+// the accumulator-layout writes and the row reads free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int stage_off(int r, int col) {
+  return r * D + (((col >> 2) ^ (r & 15)) << 2) + (col & 3);
+}
+// Accumulators of a transposed product X^T (column l % 32 = row of X,
+// register i of block dt = column 32 dt + 8 (i / 4) + 4 g + i % 4 of X),
+// times `mul`, into the staging tile.
+template <int D>
+__device__ __forceinline__ void stage_transposed(float* st, const f32x16* acc, float mul, int lane) {
+  const int g = lane >> 5, r = lane & 31;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      *(f32x4*)&st[stage_off<D>(r, 32 * dt + 8 * a + 4 * g)] =
+          f32x4{acc[dt][4 * a] * mul, acc[dt][4 * a + 1] * mul, acc[dt][4 * a + 2] * mul, acc[dt][4 * a + 3] * mul};
+}
+// Accumulators of X itself (column l % 32 = column 32 dt + l % 32 of X,
+// register i = row 8 (i / 4) + 4 g + i % 4) into the staging tile.
+template <int D>
+__device__ __forceinline__ void stage_direct(float* st, const f32x16* acc, int lane) {
+  const int g = lane >> 5, c = lane & 31;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[stage_off<D>(8 * (i >> 2) + 4 * g + (i & 3), 32 * dt + c)] = acc[dt][i];
+}
+// Rows 0 .. nrows - 1 of the staging tile to dst + row0 * D (row-major,
+// bfloat16 or float32): every lane moves 8 consecutive values of one row, so
+// one store instruction covers 512 / D whole rows.
+template <int D>
+__device__ __forceinline__ void store_staged(const float* st, void* dst, size_t row0, int nrows, bool f32, int lane) {
+  constexpr int kLpr = D / 8;      // lanes per row
+  constexpr int kRpp = 64 / kLpr;  // rows per pass
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging writes have landed
+#pragma unroll
+  for (int pass = 0; pass < 32 / kRpp; ++pass) {
+    const int r = pass * kRpp + lane / kLpr;
+    const int c = 8 * (lane % kLpr);
+    const f32x4 a = *(const f32x4*)&st[stage_off<D>(r, c)];
+    const f32x4 b = *(const f32x4*)&st[stage_off<D>(r, c + 4)];
+    if (r < nrows) {
+      const size_t idx = (row0 + r) * D + c;
+      if (f32) {
+        *(f32x4*)((float*)dst + idx) = a;
+        *(f32x4*)((float*)dst + idx + 4) = b;
+      } else {
+        *(bf16x8*)((bf16*)dst + idx) = bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                                             (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------ scheduler

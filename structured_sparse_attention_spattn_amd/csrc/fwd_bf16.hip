@@ -110,58 +110,6 @@ __device__ __forceinline__ void rescale(OnlineState<D>& st, float alpha) {
     for (int i = 0; i < 16; ++i) st.acc[dt][i] *= alpha;
 }
 
-// Per-lane byte offsets inside a swizzled K / V tile.  Row r and r + 32
-// (r + 16 for the transposing reads) share a swizzle, so one offset per
-// column block serves every 32-key half; the stage base is a compile-time
-// constant added on top.
-template <int D>
-struct LaneOffsets {
-  int k[D / 16];      // K row reads: row perm_row(l % 32), columns 16 kk + 8 g
-  int v[D / 32][2];   // V^T transposing reads: k rows 8 g + (l % 16) / 4 (+ 4)
-  __device__ __forceinline__ LaneOffsets(int lane) {
-    const int g = lane >> 5, grp = lane >> 4, j = lane & 15;
-    const int krow = perm_row(lane & 31);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) k[kk] = 2 * tile_off<D>(krow, 16 * kk + 8 * g);
-    const int r = 8 * g + (j >> 2);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int col = 32 * dt + 16 * (grp & 1) + 4 * (j & 3);
-      v[dt][0] = 2 * tile_off<D>(r, col);
-      v[dt][1] = 2 * tile_off<D>(r + 4, col);
-    }
-  }
-  // Called at the top of every tile: makes the offsets opaque there, so the
-  // compiler folds each stage / half constant into the LDS instruction's
-  // immediate instead of keeping one hoisted register per combination.
-  __device__ __forceinline__ void refresh() {
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(k[kk]));
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+v"(v[dt][0]), "+v"(v[dt][1]));
-  }
-};
-
-template <int D>
-__device__ __forceinline__ void load_ka(bf16x8* ka, const bf16* ks, const LaneOffsets<D>& off, int row0) {
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    ka[kk] = *(const bf16x8*)((const char*)ks + off.k[kk] + row0 * D * 2);
-}
-// V^T operands of keys row0 .. row0 + 31: va[2 dt] covers k rows row0 .. +15,
-// va[2 dt + 1] rows row0 + 16 .. +31.
-template <int D>
-__device__ __forceinline__ void load_va(bf16x8* va, const bf16* vs, const LaneOffsets<D>& off, int row0) {
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const char* t = (const char*)vs + (row0 + 16 * h) * D * 2;
-      const bf16x4 a = lds_read_tr4((const bf16*)(t + off.v[dt][0]));
-      const bf16x4 b = lds_read_tr4((const bf16*)(t + off.v[dt][1]));
-      va[2 * dt + h] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    }
-}
 template <int D>
 __device__ __forceinline__ void pv(OnlineState<D>& st, const bf16x8* va, bf16x8 p0, bf16x8 p1) {
 #pragma unroll
@@ -312,6 +260,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   const bool wave_live = iw0 <= N - 1;
   const int iq = iw0 + c32;
 
+  // First K / V tile before the Q loads: the two round trips overlap (the
+  // wait for Q covers both).
+  Tile::load(smem, kb, u_begin * kBK, N, wave, lane);
+  Tile::load(smem + kTile, vb, u_begin * kBK, N, wave, lane);
+
   // Q^T operand: lane holds Q[iq][16kk + 8g .. +7].
   bf16x8 qreg[kKK];
 #pragma unroll
@@ -330,9 +283,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   st.l_run = 0.f;
   const float sl2 = p.scale_log2;
   const int width = hi - lo;
-
-  Tile::load(smem, kb, u_begin * kBK, N, wave, lane);
-  Tile::load(smem + kTile, vb, u_begin * kBK, N, wave, lane);
 
   // One tile from LDS stage S (a compile-time constant, so every LDS offset
   // is an immediate).
@@ -366,17 +316,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   // ---- epilogue: O = acc / l, LSE = scale * m + ln(sum)
   const float l_tot = pair_sum(st.l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (iq < N) {
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        bf16x4 w;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) w[c] = (bf16)(st.acc[dt][4 * a + c] * inv);
-        *(bf16x4*)(ob + (size_t)iq * D + 32 * dt + 8 * a + 4 * g) = w;
-      }
-    if (g == 0) lb[iq] = l_tot > 0.f ? (st.m_ref * sl2 + fast_log2(l_tot)) * kLn2 : ninf;
+  if (iq < N && g == 0) lb[iq] = l_tot > 0.f ? (st.m_ref * sl2 + fast_log2(l_tot)) * kLn2 : ninf;
+  __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
+  if (wave_live) {
+    float* stg = (float*)smem + wave * 32 * D;
+    stage_transposed<D>(stg, st.acc, inv, lane);
+    store_staged<D>(stg, p.o, (size_t)bh * N + iw0, min(32, N - iw0), false, lane);
   }
 }
 
