@@ -12,6 +12,13 @@ i.e. ordinary attention whose softmax runs only over S_i.  SPAttention
 set S_i^h = { j : 0 <= j <= i, lo_h <= i - j <= hi_h }, one contiguous band of
 causal distances per head.
 
+Local sharing: the same page's Figure 2 caption describes its exclusive-band
+ablation as SPAttention with the local sharing removed, so the full method
+also lets every head see a shared local window.  Reading (width not given):
+head h's set becomes S_i^h united with { j : 0 <= i - j <= w - 1 } for a
+window width w >= 0 (w = 0 is the exclusive-band method above).  Every
+function below takes ``local_window`` = w, default 0.
+
 Readings (pages silent): an empty S_i gives output 0 and LSE = -inf;
 LSE_i = ln sum_{j in S_i} exp(scaled score); the backward pass is the
 textbook derivative of the formula (D_i = dO_i . O_i, dS = P * (dP - D)).
@@ -71,12 +78,22 @@ def masked_attention_literal(q, k, v, allowed, scale=None):
     return out, lse
 
 
-def band_mask(n_q, n_k, lo, hi):
-    """Boolean [n_q, n_k] mask of head (lo, hi): j <= i and lo <= i - j <= hi."""
+def _in_set(dist, lo, hi, local_window=0):
+    """Is causal distance `dist` in head (lo, hi)'s set: the band [lo, hi] or
+    the shared local window [0, local_window - 1]?"""
+    m = (dist >= max(lo, 0)) & (dist <= hi)
+    if local_window > 0:
+        m = m | ((dist >= 0) & (dist <= local_window - 1))
+    return m
+
+
+def band_mask(n_q, n_k, lo, hi, local_window=0):
+    """Boolean [n_q, n_k] mask of head (lo, hi): j <= i and lo <= i - j <= hi
+    (or 0 <= i - j < local_window)."""
     i = np.arange(n_q)[:, None]
     j = np.arange(n_k)[None, :]
     dist = i - j
-    return (j <= i) & (dist >= lo) & (dist <= hi)
+    return (j <= i) & _in_set(dist, lo, hi, local_window)
 
 
 def masked_attention_dense(q, k, v, mask, scale=None):
@@ -127,13 +144,40 @@ def _key_range(i0, i1, lo, hi):
     return max(0, i0 - hi), (i1 - 1) - lo
 
 
-def _block_forward(qb, kb, vb, i0, j0, lo, hi, sc):
-    """Forward on one query block against the gathered key rows."""
-    n_q, n_k = qb.shape[0], kb.shape[0]
+def _key_index(i0, i1, lo, hi, local_window=0):
+    """Sorted key rows a block of query rows [i0, i1) can reach: the band's
+    range, joined with [max(0, i0 - w + 1), i1 - 1] for a local window w."""
+    parts = []
+    if hi >= lo:
+        j0, j1 = _key_range(i0, i1, lo, hi)
+        if j1 >= j0:
+            parts.append(np.arange(j0, j1 + 1))
+    if local_window > 0:
+        parts.append(np.arange(max(0, i0 - local_window + 1), i1))
+    if not parts:
+        return np.zeros(0, dtype=np.int64)
+    return np.unique(np.concatenate(parts))
+
+
+def _query_index(j, lo, hi, N, local_window=0):
+    """Query rows i < N whose set contains key row j."""
+    parts = []
+    if hi >= lo and j + lo <= N - 1:
+        parts.append(np.arange(j + lo, min(N - 1, j + hi) + 1))
+    if local_window > 0:
+        parts.append(np.arange(j, min(N - 1, j + local_window - 1) + 1))
+    if not parts:
+        return np.zeros(0, dtype=np.int64)
+    return np.unique(np.concatenate(parts))
+
+
+def _block_forward(qb, kb, vb, i0, jidx, lo, hi, sc, local_window=0):
+    """Forward on one query block against the gathered key rows jidx."""
+    n_q = qb.shape[0]
     i = (i0 + np.arange(n_q))[:, None]
-    j = (j0 + np.arange(n_k))[None, :]
+    j = np.asarray(jidx)[None, :]
     dist = i - j
-    mask = (dist >= max(lo, 0)) & (dist <= hi)
+    mask = _in_set(dist, lo, hi, local_window)
     s = np.where(mask, (qb @ kb.T) * sc, -np.inf)
     nonempty = mask.any(axis=1)
     shift = np.where(nonempty, s.max(axis=1), 0.0)
@@ -146,12 +190,13 @@ def _block_forward(qb, kb, vb, i0, j0, lo, hi, sc):
     return out, lse, p
 
 
-def band_attention_fwd(q, k, v, lo, hi, scale=None, heads=None):
+def band_attention_fwd(q, k, v, lo, hi, scale=None, heads=None, local_window=0):
     """Band attention over [B, H, N, d] inputs.
 
     lo, hi: per-head inclusive distance bounds (length H).  Returns
     (out [B, H, N, dv] float64, lse [B, H, N] float64).  ``heads`` optionally
     restricts the work to a subset of head indices (others are left 0/-inf).
+    ``local_window`` adds the shared local window to every head's set.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -160,24 +205,25 @@ def band_attention_fwd(q, k, v, lo, hi, scale=None, heads=None):
     sc = _default_scale(d, scale)
     out = np.zeros(q.shape[:3] + (v.shape[3],))
     lse = np.full((B, H, N), -np.inf)
+    w = int(local_window)
     for b in range(B):
         for h in (range(H) if heads is None else heads):
             l, u = int(lo[h]), int(hi[h])
-            if u < l:
+            if u < l and w == 0:
                 continue
             for i0 in range(0, N, QUERY_BLOCK):
                 i1 = min(N, i0 + QUERY_BLOCK)
-                j0, j1 = _key_range(i0, i1, l, u)
-                if j1 < j0:
+                jidx = _key_index(i0, i1, l, u, w)
+                if jidx.size == 0:
                     continue
-                o_blk, l_blk, _ = _block_forward(q[b, h, i0:i1], k[b, h, j0:j1 + 1],
-                                                 v[b, h, j0:j1 + 1], i0, j0, l, u, sc)
+                o_blk, l_blk, _ = _block_forward(q[b, h, i0:i1], k[b, h, jidx], v[b, h, jidx], i0, jidx,
+                                                 l, u, sc, w)
                 out[b, h, i0:i1] = o_blk
                 lse[b, h, i0:i1] = l_blk
     return out, lse
 
 
-def band_attention_fwd_rows(q, k, v, lo, hi, b, h, rows, scale=None):
+def band_attention_fwd_rows(q, k, v, lo, hi, b, h, rows, scale=None, local_window=0):
     """Forward for selected query rows of one (b, h) only -- each row is
     computed on its own from the definition.  Returns (out [len(rows), dv],
     lse [len(rows)]).  Used to check sampled outputs at full sizes."""
@@ -187,19 +233,19 @@ def band_attention_fwd_rows(q, k, v, lo, hi, b, h, rows, scale=None):
     outs = np.zeros((len(rows), v.shape[3]))
     lses = np.full(len(rows), -np.inf)
     for r, i in enumerate(rows):
-        j0, j1 = _key_range(i, i + 1, l, u)
-        if u < l or j1 < j0:
+        jidx = _key_index(i, i + 1, l, u, int(local_window))
+        if jidx.size == 0:
             continue
         qb = np.asarray(q[b, h, i:i + 1], dtype=np.float64)
-        kb = np.asarray(k[b, h, j0:j1 + 1], dtype=np.float64)
-        vb = np.asarray(v[b, h, j0:j1 + 1], dtype=np.float64)
-        o_blk, l_blk, _ = _block_forward(qb, kb, vb, i, j0, l, u, sc)
+        kb = np.asarray(k[b, h, jidx], dtype=np.float64)
+        vb = np.asarray(v[b, h, jidx], dtype=np.float64)
+        o_blk, l_blk, _ = _block_forward(qb, kb, vb, i, jidx, l, u, sc, int(local_window))
         outs[r] = o_blk[0]
         lses[r] = l_blk[0]
     return outs, lses
 
 
-def band_attention_bwd(q, k, v, dout, lo, hi, scale=None):
+def band_attention_bwd(q, k, v, dout, lo, hi, scale=None, local_window=0):
     """Gradients of band attention over [B, H, N, d].
 
     Recomputes the forward in float64 per query block, then per block:
@@ -218,33 +264,34 @@ def band_attention_bwd(q, k, v, dout, lo, hi, scale=None):
     dv = np.zeros_like(v)
     out = np.zeros(q.shape[:3] + (v.shape[3],))
     lse = np.full((B, H, N), -np.inf)
+    w = int(local_window)
     for b in range(B):
         for h in range(H):
             l, u = int(lo[h]), int(hi[h])
-            if u < l:
+            if u < l and w == 0:
                 continue
             for i0 in range(0, N, QUERY_BLOCK):
                 i1 = min(N, i0 + QUERY_BLOCK)
-                j0, j1 = _key_range(i0, i1, l, u)
-                if j1 < j0:
+                jidx = _key_index(i0, i1, l, u, w)
+                if jidx.size == 0:
                     continue
                 qb = q[b, h, i0:i1]
-                kb = k[b, h, j0:j1 + 1]
-                vb = v[b, h, j0:j1 + 1]
+                kb = k[b, h, jidx]
+                vb = v[b, h, jidx]
                 dob = dout[b, h, i0:i1]
-                o_blk, l_blk, p = _block_forward(qb, kb, vb, i0, j0, l, u, sc)
+                o_blk, l_blk, p = _block_forward(qb, kb, vb, i0, jidx, l, u, sc, w)
                 out[b, h, i0:i1] = o_blk
                 lse[b, h, i0:i1] = l_blk
                 dcoef = (dob * o_blk).sum(axis=1)
-                dv[b, h, j0:j1 + 1] += p.T @ dob
+                dv[b, h, jidx] += p.T @ dob
                 dp = dob @ vb.T
                 ds = p * (dp - dcoef[:, None])
                 dq[b, h, i0:i1] = sc * (ds @ kb)
-                dk[b, h, j0:j1 + 1] += sc * (ds.T @ qb)
+                dk[b, h, jidx] += sc * (ds.T @ qb)
     return dq, dk, dv, out, lse
 
 
-def band_attention_bwd_rows(q, k, v, dout, lo, hi, b, h, q_rows, k_rows, scale=None):
+def band_attention_bwd_rows(q, k, v, dout, lo, hi, b, h, q_rows, k_rows, scale=None, local_window=0):
     """Gradients for selected rows of one (b, h), each from the definition.
 
     dq[r] = scale * sum_j dS_ij k_j for query row i = q_rows[r];
@@ -259,13 +306,15 @@ def band_attention_bwd_rows(q, k, v, dout, lo, hi, b, h, q_rows, k_rows, scale=N
     l, u = int(lo[h]), int(hi[h])
     f64 = lambda x: np.asarray(x, dtype=np.float64)
 
+    w = int(local_window)
+
     def row_terms(i):
-        """(keys j0..j1, P_i over them, dS_i over them) or None if empty."""
-        j0, j1 = _key_range(i, i + 1, l, u)
-        if u < l or j1 < j0:
+        """(key rows jidx, P_i over them, dS_i over them) or None if empty."""
+        jidx = _key_index(i, i + 1, l, u, w)
+        if jidx.size == 0:
             return None
         qi = f64(q[b, h, i])
-        kb, vb = f64(k[b, h, j0:j1 + 1]), f64(v[b, h, j0:j1 + 1])
+        kb, vb = f64(k[b, h, jidx]), f64(v[b, h, jidx])
         s = (kb @ qi) * sc
         m = s.max()
         e = np.exp(s - m)
@@ -274,21 +323,20 @@ def band_attention_bwd_rows(q, k, v, dout, lo, hi, b, h, q_rows, k_rows, scale=N
         do_i = f64(dout[b, h, i])
         dcoef = float(do_i @ o_i)
         ds = p * (vb @ do_i - dcoef)
-        return j0, j1, p, ds
+        return jidx, p, ds
 
     dq = np.zeros((len(q_rows), d))
     for r, i in enumerate(q_rows):
         t = row_terms(i)
         if t is not None:
-            j0, j1, _, ds = t
-            dq[r] = sc * (ds @ f64(k[b, h, j0:j1 + 1]))
+            jidx, _, ds = t
+            dq[r] = sc * (ds @ f64(k[b, h, jidx]))
     dk = np.zeros((len(k_rows), d))
     dv = np.zeros((len(k_rows), v.shape[3]))
     for r, j in enumerate(k_rows):
-        if u < l or j + l > N - 1:
-            continue
-        for i in range(j + l, min(N - 1, j + u) + 1):
-            j0, j1, p, ds = row_terms(i)
-            dk[r] += sc * ds[j - j0] * f64(q[b, h, i])
-            dv[r] += p[j - j0] * f64(dout[b, h, i])
+        for i in _query_index(j, l, u, N, w):
+            jidx, p, ds = row_terms(int(i))
+            pos = int(np.searchsorted(jidx, j))
+            dk[r] += sc * ds[pos] * f64(q[b, h, i])
+            dv[r] += p[pos] * f64(dout[b, h, i])
     return dq, dk, dv
