@@ -124,6 +124,28 @@ int spattn_bwd(const void* q, const void* k, const void* v, const void* o,
                float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Band attention with a shared local window ("Making Every Head Count",
+ * Figure 2 caption: its exclusive-band ablation is the method with the local
+ * sharing removed; the page gives no window width).  Head h attends
+ *     S = { j : 0 <= j <= i, lo_h <= i - j <= hi_h  or  i - j < local_window }
+ * i.e. its band joined with the distances [0, local_window - 1] that every
+ * head shares.  local_window = 0 is exactly spattn_fwd / spattn_bwd; widths
+ * above N act as N.  Arguments, outputs and errors as spattn_fwd and
+ * spattn_bwd, plus SPATTN_E_ARG for local_window < 0 and SPATTN_E_UNSUPPORTED
+ * for local_window > 0 with float32 inputs (bfloat16 only).
+ */
+int spattn_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+                     const int32_t* band_lo, const int32_t* band_hi,
+                     int32_t local_window, float scale, void* stream);
+int spattn_bwd_local(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+                     int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi,
+                     int32_t local_window, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * The two stages spattn_bwd runs, exported for callers that schedule them
  * separately (and for per-kernel timing).  Same arguments and checks as
  * spattn_bwd; together they compute exactly what spattn_bwd computes.

@@ -162,11 +162,11 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype
 }
 
 int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                       void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, float scale,
-                       float* dvec, hipStream_t stream);
+                       void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
+                       float scale, float* dvec, hipStream_t stream);
 int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
-                         void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, float scale,
-                         float* dvec, hipStream_t stream);
+                         void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
+                         float scale, float* dvec, hipStream_t stream);
 
 static BwdF32Args f32_args(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
                            void* dk, void* dv, int B, int H, int N, const Bands& bands, float scale, float* dvec) {
@@ -190,12 +190,13 @@ static BwdF32Args f32_args(const void* q, const void* k, const void* v, const fl
 
 // Stage 1: D_i = dO_i . O_i into the workspace, and dQ.
 int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                  void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands, float scale,
-                  void* workspace, hipStream_t stream) {
+                  void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
+                  int local_window, float scale, void* workspace, hipStream_t stream) {
   float* dvec = (float*)workspace;
   if (dtype == SPATTN_BF16)
-    return launch_bwd_dq_bf16(q, k, v, o, lse, dout, dq, B, H, N, d, grad_dtype == SPATTN_F32, bands, scale, dvec,
-                              stream);
+    return launch_bwd_dq_bf16(q, k, v, o, lse, dout, dq, B, H, N, d, grad_dtype == SPATTN_F32, bands, local_window,
+                              scale, dvec, stream);
+  if (local_window > 0) return SPATTN_E_UNSUPPORTED;
   const long long rows = (long long)B * H * N;
   {
     const long long threads = rows * (d / 8);
@@ -219,12 +220,13 @@ int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, co
 
 // Stage 2: dK and dV, reading D from the workspace written by stage 1.
 int launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
-                    void* dv, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands, float scale,
-                    void* workspace, hipStream_t stream) {
+                    void* dv, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
+                    int local_window, float scale, void* workspace, hipStream_t stream) {
   float* dvec = (float*)workspace;
   if (dtype == SPATTN_BF16)
-    return launch_bwd_dkdv_bf16(q, k, v, lse, dout, dk, dv, B, H, N, d, grad_dtype == SPATTN_F32, bands, scale, dvec,
-                                stream);
+    return launch_bwd_dkdv_bf16(q, k, v, lse, dout, dk, dv, B, H, N, d, grad_dtype == SPATTN_F32, bands,
+                                local_window, scale, dvec, stream);
+  if (local_window > 0) return SPATTN_E_UNSUPPORTED;
   const long long rows = (long long)B * H * N;
   BwdF32Args a = f32_args(q, k, v, lse, dout, nullptr, dk, dv, B, H, N, bands, scale, dvec);
   dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);

@@ -41,6 +41,7 @@ struct BwdArgs {
   int grad_f32;
   int B, H, N;
   int n_tiles;  // query tiles (bwd_dq) or key tiles (bwd_dkdv) per (b, h)
+  int local_window;  // shared local window width (0: exclusive bands)
   float scale;
   float scale_log2;
   Bands bands;
@@ -51,7 +52,7 @@ constexpr int kDqBQ = 128;    // query rows per workgroup
 constexpr int kDqBK = 32;     // key rows per stage
 constexpr int kDqStages = 4;  // LDS ring depth: tiles u+1 .. u+3 load while u is used
 
-template <int D>
+template <int D, bool TWO>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   constexpr int kTile = kDqBK * D;
   constexpr int kKK = D / 16;
@@ -72,8 +73,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const int bh = item / p.n_tiles;
   const int h = bh % p.H;
   const int N = p.N;
-  const int lo = p.bands.lo[h];
-  const int hi = p.bands.hi[h];
+  // the head's distance set: its band, joined with the local window if any
+  const DistSet dset = dist_set(p.bands.lo[h], p.bands.hi[h], TWO ? p.local_window : 0);
+  const int lo = dset.lo;
+  const int hi = dset.hi;
   const size_t base = (size_t)bh * N * D;
   const bf16* __restrict__ kb = p.k + base;
   const bf16* __restrict__ vb = p.v + base;
@@ -86,12 +89,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const bool row_ok = iq < N;
 
   const int i_tile1 = min(N - 1, i_tile0 + kDqBQ - 1);
-  const KeySpan span = band_key_span(i_tile0, i_tile1, lo, hi);
-  const bool any_key = span.last >= span.first;
-  const int u_begin = any_key ? span.first / kDqBK : 0;
-  const int u_end = any_key ? span.last / kDqBK + 1 : 0;
-  auto issue = [&](int u) {
-    bf16* st = smem + ((u - u_begin) % kDqStages) * 2 * kTile;
+  KeySpan span2{0, -1};
+  if constexpr (TWO)
+    if (has_second(dset)) span2 = band_key_span(i_tile0, i_tile1, dset.nlo, dset.nhi);
+  // key tiles to visit, in order; the ring holds visit v in stage v % kDqStages
+  const TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kDqBK);
+  const int n_visit = walk.n;
+  auto issue = [&](int v) {
+    bf16* st = smem + (v % kDqStages) * 2 * kTile;
+    const int u = walk.at(v);
     Tile::load(st, kb, u * kDqBK, N, wave, lane);
     Tile::load(st + kTile, vb, u * kDqBK, N, wave, lane);
   };
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   // (the wait for those covers both).
 #pragma unroll
   for (int i = 0; i < kDqStages - 1; ++i)
-    if (u_begin + i < u_end) issue(u_begin + i);
+    if (i < n_visit) issue(i);
 
   // Q and dO operands; D_i = dO_i . O_i from the same lanes.
   bf16x8 qreg[kKK], doreg[kKK];
@@ -139,23 +145,31 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  if (any_key) {
+  if (n_visit > 0) {
     LaneOffsets<D> off(lane);
-    for (int u = u_begin; u < u_end; ++u) {
-      const int ahead = u_end - 1 - u;  // tiles issued after u and possibly in flight
+    for (int v = 0; v < n_visit; ++v) {
+      const int ahead = n_visit - 1 - v;  // visits issued after v and possibly in flight
       if (ahead >= 2)
         wait_vmcnt<2 * kL>();
       else if (ahead == 1)
         wait_vmcnt<kL>();
       else
         wait_vmcnt<0>();
-      __syncthreads();  // tile u complete for everyone; tile u - 1 released
-      if (u + kDqStages - 1 < u_end) issue(u + kDqStages - 1);
-      const bf16* ks = smem + ((u - u_begin) % kDqStages) * 2 * kTile;
+      __syncthreads();  // tile of visit v complete for everyone; visit v - 1 released
+      if (v + kDqStages - 1 < n_visit) issue(v + kDqStages - 1);
+      const bf16* ks = smem + (v % kDqStages) * 2 * kTile;
       const bf16* vs = ks + kTile;
       off.refresh();
-      const int jb = u * kDqBK;
-      if (wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi)) {
+      const int jb = walk.at(v) * kDqBK;
+      bool meets, full;
+      if constexpr (TWO) {
+        meets = set_meets(iw0, iw1, jb, jb + 31, dset);
+        full = set_full(iw0, iw1, jb, jb + 31, dset);
+      } else {
+        meets = tile_meets(iw0, iw1, jb, jb + 31, lo, hi);
+        full = tile_full(iw0, iw1, jb, jb + 31, lo, hi);
+      }
+      if (wave_live && meets) {
         // S^T first, then dP^T with the exponentials of S^T issued between
         // its products (one accumulator chain each; a dependent chain costs
         // nothing extra when other work sits between its steps).
@@ -188,13 +202,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
         float ds[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) ds[i] = pe[i] * __builtin_fmaf(pacc[i], scl, ndsc);
-        if (!tile_full(iw0, iw1, jb, jb + 31, lo, hi)) {
+        if (!full) {
           const int mb = iq - jb - 8 * g - lo;  // (iq - key - lo) + c for register i
           const uint32_t width = (uint32_t)(hi - lo);
+          const int mb2 = iq - jb - 8 * g - dset.nlo;
+          const uint32_t width2 = (uint32_t)(dset.nhi - dset.nlo);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int c = ((i >> 3) << 4) + (i & 7);  // perm_reg_row(i, 0)
-            ds[i] = (uint32_t)(mb - c) <= width && row_ok ? ds[i] : 0.f;
+            bool in = (uint32_t)(mb - c) <= width;
+            if constexpr (TWO) in = in || (uint32_t)(mb2 - c) <= width2;
+            ds[i] = in && row_ok ? ds[i] : 0.f;
           }
         }
         const bf16x8 d0 = pack8(&ds[0]), d1 = pack8(&ds[8]);
@@ -250,7 +268,7 @@ __device__ __forceinline__ f16x8 pack8_f16(const float* x) {
   return r;
 }
 
-template <int D>
+template <int D, bool TWO>
 __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   constexpr int kWaves = kKvThreads / 64;
   constexpr int kTile = kKvQB * D;
@@ -278,8 +296,10 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   const int bh = item / p.n_tiles;
   const int h = bh % p.H;
   const int N = p.N;
-  const int lo = p.bands.lo[h];
-  const int hi = p.bands.hi[h];
+  // the head's distance set: its band, joined with the local window if any
+  const DistSet dset = dist_set(p.bands.lo[h], p.bands.hi[h], TWO ? p.local_window : 0);
+  const int lo = dset.lo;
+  const int hi = dset.hi;
   const size_t base = (size_t)bh * N * D;
   const bf16* __restrict__ qb = p.q + base;
   const bf16* __restrict__ dob = p.dout + base;
@@ -301,14 +321,18 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  const KeySpan qspan = band_query_span(j0, j1, lo, hi, N);
-  if (qspan.last >= qspan.first) {
+  KeySpan qspan2{0, -1};
+  if constexpr (TWO)
+    if (has_second(dset)) qspan2 = band_query_span(j0, j1, dset.nlo, dset.nhi, N);
+  // query blocks to visit, in order; visit v sits in ring stage v % kKvStages
+  const TileWalk walk = tile_walk(band_query_span(j0, j1, lo, hi, N), qspan2, kKvQB);
+  const int n_visit = walk.n;
+  if (n_visit > 0) {
     const float sl2 = p.scale_log2;
     const float scl = p.scale;
-    const int tq_begin = qspan.first / kKvQB;
-    const int tq_end = qspan.last / kKvQB + 1;
-    auto issue = [&](int tq) {
-      const int st = (tq - tq_begin) % kKvStages;
+    auto issue = [&](int v) {
+      const int st = v % kKvStages;
+      const int tq = walk.at(v);
       bf16* t = smem + st * 2 * kTile;
       Tile::load(t, qb, tq * kKvQB, N, wave, lane);
       Tile::load(t + kTile, dob, tq * kKvQB, N, wave, lane);
@@ -319,7 +343,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
     // Ring prefill first: its round trip overlaps that of the row loads below.
 #pragma unroll
     for (int i = 0; i < kKvAhead; ++i)
-      if (tq_begin + i < tq_end) issue(tq_begin + i);
+      if (i < n_visit) issue(i);
     // B operand of this wave's score product: K rows (P wave) or V rows (dS wave)
     bf16x8 bop[kKK];
     {
@@ -343,11 +367,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         out[12 + e] = d[e];
       }
     };
-    // dS wave, block tq (one iteration late): dS = P (dP - D) scale and
+    // dS wave, visit v (one iteration late): dS = P (dP - D) scale and
     // dK += dS^T Q.  P comes masked from the P wave (0 outside the band and
     // on rows past N), so no mask is needed here.
-    auto ds_dk = [&](int tq, const f32x16& dpv) {
-      const int st = (tq - tq_begin) % kKvStages;
+    auto ds_dk = [&](int v, const f32x16& dpv) {
+      const int st = v % kKvStages;
       const bf16* qs = smem + st * 2 * kTile;
       bf16x8 bb[2 * kDT];
 #pragma unroll
@@ -357,7 +381,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       }
       float dd[16], ds[16];
       rows16(&rowv[st][wave][kKvQB], dd);
-      const f16x8* src = (const f16x8*)&pbuf[(tq - tq_begin) & 1][kw][lane][0];
+      const f16x8* src = (const f16x8*)&pbuf[v & 1][kw][lane][0];
       const f16x8 pa = src[0], pb = src[1];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -373,21 +397,25 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
     };
 
     // Top of every iteration, for both roles (same barrier sequence): wait for
-    // this wave's loads of block tq (those of tq + 1 may stay in flight), then
-    // the barrier -- block tq complete for everyone, iteration tq - 1 finished
-    // everywhere, so the stage of block tq - 2 is free and the P of block
-    // tq - 1 is visible -- then prefetch block tq + kKvAhead.
-    auto block_start = [&](int tq) {
-      if (tq + 1 < tq_end)
+    // this wave's loads of visit v (those of v + 1 may stay in flight), then
+    // the barrier -- visit v complete for everyone, iteration v - 1 finished
+    // everywhere, so the stage of visit v - 2 is free and the P of visit
+    // v - 1 is visible -- then prefetch visit v + kKvAhead.
+    auto block_start = [&](int v) {
+      if (v + 1 < n_visit)
         wait_vmcnt<kL>();
       else
         wait_vmcnt<0>();
       __syncthreads();
-      if (tq + kKvAhead < tq_end) issue(tq + kKvAhead);
+      if (v + kKvAhead < n_visit) issue(v + kKvAhead);
     };
-    auto block_act = [&](int tq) {
-      const int i0 = tq * kKvQB;
-      return wave_live && tile_meets(i0, min(N - 1, i0 + kKvQB - 1), kw0, kw1, lo, hi);
+    auto block_act = [&](int v) {
+      const int i0 = walk.at(v) * kKvQB;
+      const int i1 = min(N - 1, i0 + kKvQB - 1);
+      if constexpr (TWO)
+        return wave_live && set_meets(i0, i1, kw0, kw1, dset);
+      else
+        return wave_live && tile_meets(i0, i1, kw0, kw1, lo, hi);
     };
 
     if (pwave) {
@@ -397,8 +425,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       LaneOffsets<D> off(lane);
       bf16x8 pp0{}, pp1{};  // packed P of the previous block
       bool act_prev = false;
-      auto dv_operands = [&](int tq, bf16x8* bb) {
-        const bf16* dos = smem + ((tq - tq_begin) % kKvStages) * 2 * kTile + kTile;
+      auto dv_operands = [&](int v, bf16x8* bb) {
+        const bf16* dos = smem + (v % kKvStages) * 2 * kTile + kTile;
         load_va<D>(bb, dos, off, 0);
       };
       auto dv_update = [&](const bf16x8* bb, bf16x8 p0, bf16x8 p1) {
@@ -407,14 +435,14 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(p1, bb[2 * dt + 1], acc[dt]);
       };
-      for (int tq = tq_begin; tq < tq_end; ++tq) {
-        block_start(tq);
+      for (int v = 0; v < n_visit; ++v) {
+        block_start(v);
         off.refresh();
-        const bool act = block_act(tq);
+        const bool act = block_act(v);
         if (act) {
-          const int s = (tq - tq_begin) % kKvStages;
+          const int s = v % kKvStages;
           const bf16* qs = smem + s * 2 * kTile;
-          const int i0 = tq * kKvQB;
+          const int i0 = walk.at(v) * kKvQB;
           const int i1 = min(N - 1, i0 + kKvQB - 1);
           bf16x8 aa[kKK];
           load_ka<D>(aa, qs, off, 0);
@@ -425,9 +453,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
           rows16(&rowv[s][wave][0], nl);
           if (act_prev) {
             bf16x8 bb[2 * kDT];
-            dv_operands(tq - 1, bb);
-            // fixed order: one dV product of block tq - 1, then its share of
-            // the exponentials of block tq
+            dv_operands(v - 1, bb);
+            // fixed order: one dV product of visit v - 1, then its share of
+            // the exponentials of visit v
 #pragma unroll
             for (int m = 0; m < 2 * kDT; ++m) {
               const int dt = m % kDT;
@@ -441,26 +469,35 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
           }
-          const bool full = wave_keys_full && i0 + kKvQB - 1 <= N - 1 && tile_full(i0, i1, kw0, kw1, lo, hi);
+          bool full_set;
+          if constexpr (TWO)
+            full_set = set_full(i0, i1, kw0, kw1, dset);
+          else
+            full_set = tile_full(i0, i1, kw0, kw1, lo, hi);
+          const bool full = wave_keys_full && i0 + kKvQB - 1 <= N - 1 && full_set;
           if (!full) {
             // band applied by selection (P may overflow out of band)
             const int mb = kj + lo - i0;  // query row r is in band iff 0 <= r - mb <= hi - lo
             const uint32_t width = (uint32_t)(hi - lo);
+            const int mb2 = kj + dset.nlo - i0;
+            const uint32_t width2 = (uint32_t)(dset.nhi - dset.nlo);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int r = perm_reg_row(i, g);
-              const bool ok = key_ok && i0 + r < N && (uint32_t)(r - mb) <= width;
+              bool in = (uint32_t)(r - mb) <= width;
+              if constexpr (TWO) in = in || (uint32_t)(r - mb2) <= width2;
+              const bool ok = key_ok && i0 + r < N && in;
               pv[i] = ok ? pv[i] : 0.f;
             }
           }
-          f16x8* dst = (f16x8*)&pbuf[(tq - tq_begin) & 1][kw][lane][0];
+          f16x8* dst = (f16x8*)&pbuf[v & 1][kw][lane][0];
           dst[0] = pack8_f16(&pv[0]);
           dst[1] = pack8_f16(&pv[8]);
           pp0 = pack8(&pv[0]);
           pp1 = pack8(&pv[8]);
         } else if (act_prev) {
           bf16x8 bb[2 * kDT];
-          dv_operands(tq - 1, bb);
+          dv_operands(v - 1, bb);
           __builtin_amdgcn_sched_barrier(0);
           dv_update(bb, pp0, pp1);
         }
@@ -469,7 +506,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       __syncthreads();  // matches the dS waves' final barrier
       if (act_prev) {
         bf16x8 bb[2 * kDT];
-        dv_operands(tq_end - 1, bb);
+        dv_operands(n_visit - 1, bb);
         __builtin_amdgcn_sched_barrier(0);
         dv_update(bb, pp0, pp1);
       }
@@ -478,26 +515,26 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) dp_prev[i] = 0.f;
       bool act_prev = false;
-      for (int tq = tq_begin; tq < tq_end; ++tq) {
-        block_start(tq);
-        const bool act = block_act(tq);
+      for (int v = 0; v < n_visit; ++v) {
+        block_start(v);
+        const bool act = block_act(v);
         f32x16 dp_cur;
 #pragma unroll
         for (int i = 0; i < 16; ++i) dp_cur[i] = 0.f;
         if (act) {
-          const bf16* dos = smem + ((tq - tq_begin) % kKvStages) * 2 * kTile + kTile;
+          const bf16* dos = smem + (v % kKvStages) * 2 * kTile + kTile;
           bf16x8 aa[kKK];
 #pragma unroll
           for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(dos, prow, 16 * kk + 8 * g);
           __builtin_amdgcn_sched_barrier(0);
           dp_cur = mfma_ksum<kKK, 1>(aa, bop);
         }
-        if (act_prev) ds_dk(tq - 1, dp_prev);
+        if (act_prev) ds_dk(v - 1, dp_prev);
         dp_prev = dp_cur;
         act_prev = act;
       }
       __syncthreads();  // P of the last block visible
-      if (act_prev) ds_dk(tq_end - 1, dp_prev);
+      if (act_prev) ds_dk(n_visit - 1, dp_prev);
     }
   }
 
@@ -531,6 +568,7 @@ static BwdArgs make_args(const void* q, const void* k, const void* v, const void
   a.H = H;
   a.N = N;
   a.n_tiles = 0;
+  a.local_window = 0;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   a.bands = bands;
@@ -538,30 +576,44 @@ static BwdArgs make_args(const void* q, const void* k, const void* v, const void
 }
 
 int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                       void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, float scale,
-                       float* dvec, hipStream_t stream) {
+                       void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
+                       float scale, float* dvec, hipStream_t stream) {
   BwdArgs a = make_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, grad_f32, bands, scale, dvec);
   a.n_tiles = (N + kDqBQ - 1) / kDqBQ;
+  a.local_window = local_window;
   const long long total = (long long)B * H * a.n_tiles;
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
-  if (d == 128)
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)total), dim3(kThreads), 0, stream, a);
+  const dim3 grid((unsigned)total), block(kThreads);
+  const bool two = local_window > 0;
+  if (d == 128 && !two)
+    hipLaunchKernelGGL((bwd_dq_kernel<128, false>), grid, block, 0, stream, a);
+  else if (d == 128)
+    hipLaunchKernelGGL((bwd_dq_kernel<128, true>), grid, block, 0, stream, a);
+  else if (!two)
+    hipLaunchKernelGGL((bwd_dq_kernel<64, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)total), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<64, true>), grid, block, 0, stream, a);
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
 }
 
 int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
-                         void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, float scale,
-                         float* dvec, hipStream_t stream) {
+                         void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
+                         float scale, float* dvec, hipStream_t stream) {
   BwdArgs a = make_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, grad_f32, bands, scale, dvec);
   a.n_tiles = (N + kKvBK - 1) / kKvBK;
+  a.local_window = local_window;
   const long long total = (long long)B * H * a.n_tiles;
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
-  if (d == 128)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)total), dim3(kKvThreads), 0, stream, a);
+  const dim3 grid((unsigned)total), block(kKvThreads);
+  const bool two = local_window > 0;
+  if (d == 128 && !two)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), grid, block, 0, stream, a);
+  else if (d == 128)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), grid, block, 0, stream, a);
+  else if (!two)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)total), dim3(kKvThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), grid, block, 0, stream, a);
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
 }
 

@@ -339,6 +339,15 @@ __device__ __forceinline__ void band_mask(float* x, int base, int width) {
     x[i] = (uint32_t)(base - c) <= (uint32_t)width ? x[i] : -__builtin_inff();
   }
 }
+// Same with a second distance range: base2 = iq - kb - 8 g - lo2, width2 = hi2 - lo2.
+__device__ __forceinline__ void band_mask2(float* x, int base, int width, int base2, int width2) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = ((i >> 3) << 4) + (i & 7);
+    const bool in = (uint32_t)(base - c) <= (uint32_t)width || (uint32_t)(base2 - c) <= (uint32_t)width2;
+    x[i] = in ? x[i] : -__builtin_inff();
+  }
+}
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   bf16x8 r;
@@ -448,6 +457,81 @@ __host__ __device__ __forceinline__ bool tile_meets(int i_min, int i_max, int j_
   if (hi < lo) return false;
   // distances covered: [i_min - j_max, i_max - j_min]; need overlap with [lo, hi]
   return (i_max - j_min >= lo) && (i_min - j_max <= hi);
+}
+
+// Distance set of one head with the shared local window of "Making Every
+// Head Count" (Figure 2 caption: the exclusive-band ablation is the method
+// with local sharing removed): the band [lo, hi] joined with [0, w - 1].
+// The union is kept as a primary range plus, when the window stays below the
+// band with a gap, a second disjoint range [nlo, nhi]; otherwise the second
+// range is empty, encoded as a single impossible distance so that the
+// unsigned range test "(dist - nlo) <= nhi - nlo" never passes.
+struct DistSet {
+  int lo, hi;
+  int nlo, nhi;
+};
+constexpr int kNoDistance = -(1 << 30);
+__host__ __device__ __forceinline__ DistSet dist_set(int lo, int hi, int w) {
+  DistSet s{lo, hi, kNoDistance, kNoDistance};
+  if (w > 0) {
+    const int wh = w - 1;
+    if (hi < lo) {
+      s.lo = 0;
+      s.hi = wh;
+    } else if (wh >= lo - 1) {
+      s.lo = 0;
+      s.hi = hi > wh ? hi : wh;
+    } else {
+      s.nlo = 0;
+      s.nhi = wh;
+    }
+  }
+  return s;
+}
+__host__ __device__ __forceinline__ bool has_second(const DistSet& s) { return s.nhi != kNoDistance; }
+
+// Tiles to visit: up to two ascending runs of tile indices, the second
+// starting past the first (runs that overlap or touch are merged).  Virtual
+// index v in [0, n) maps to tile at(v).
+struct TileWalk {
+  int a0, na, b0, n;
+  __host__ __device__ __forceinline__ int at(int v) const { return v < na ? a0 + v : b0 + (v - na); }
+};
+__host__ __device__ __forceinline__ TileWalk tile_walk(KeySpan s1, KeySpan s2, int tile) {
+  const bool e1 = s1.last < s1.first, e2 = s2.last < s2.first;
+  TileWalk w{0, 0, 0, 0};
+  if (e1 && e2) return w;
+  if (e1 || e2) {
+    const KeySpan s = e1 ? s2 : s1;
+    w.a0 = s.first / tile;
+    w.na = w.n = s.last / tile - w.a0 + 1;
+    return w;
+  }
+  int a0 = s1.first / tile, a1 = s1.last / tile, b0 = s2.first / tile, b1 = s2.last / tile;
+  if (b0 < a0) {
+    int t = a0; a0 = b0; b0 = t;
+    t = a1; a1 = b1; b1 = t;
+  }
+  if (b0 <= a1 + 1) {
+    w.a0 = a0;
+    w.na = w.n = (a1 > b1 ? a1 : b1) - a0 + 1;
+  } else {
+    w.a0 = a0;
+    w.na = a1 - a0 + 1;
+    w.b0 = b0;
+    w.n = w.na + b1 - b0 + 1;
+  }
+  return w;
+}
+// Tile tests over the whole distance set (an empty second range never meets
+// and is never full).
+__host__ __device__ __forceinline__ bool set_meets(int i_min, int i_max, int j_min, int j_max, const DistSet& s) {
+  return tile_meets(i_min, i_max, j_min, j_max, s.lo, s.hi) ||
+         (has_second(s) && tile_meets(i_min, i_max, j_min, j_max, s.nlo, s.nhi));
+}
+__host__ __device__ __forceinline__ bool set_full(int i_min, int i_max, int j_min, int j_max, const DistSet& s) {
+  return tile_full(i_min, i_max, j_min, j_max, s.lo, s.hi) ||
+         (has_second(s) && tile_full(i_min, i_max, j_min, j_max, s.nlo, s.nhi));
 }
 
 // Workgroup -> logical work item, so that consecutive logical items land on

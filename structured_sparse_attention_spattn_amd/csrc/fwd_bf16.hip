@@ -44,9 +44,24 @@ struct FwdArgs {
   float* lse;
   int B, H, N;
   int n_qt;
+  int local_window;  // shared local window width (0: exclusive bands)
   float scale_log2;
   Bands bands;
 };
+
+// Element mask of a tile for query iq against key block kb:
+// base = iq - kb - 8 g - lo, width = hi - lo, and the same for the second
+// distance range when there is one.
+struct MaskArgs {
+  int base, width, base2, width2;
+};
+template <bool TWO>
+__device__ __forceinline__ void apply_mask(float* x, const MaskArgs& m, int shift) {
+  if constexpr (TWO)
+    band_mask2(x, m.base - shift, m.width, m.base2 - shift, m.width2);
+  else
+    band_mask(x, m.base - shift, m.width);
+}
 
 // Online-softmax state of one wave: O^T accumulator blocks, the reference
 // maximum of every query column (raw score units) and this lane's share of
@@ -124,10 +139,10 @@ __device__ __forceinline__ void pv(OnlineState<D>& st, const bf16x8* va, bf16x8 
 // those of half 1 between the PV MFMAs of half 0.  When `masked` (a
 // wave-uniform flag) the band mask is applied to both halves; the mask sits
 // between phases, so its branch does not split an interleaved phase.
-template <int D>
+template <int D, bool TWO>
 __device__ __forceinline__ void tile_pair(OnlineState<D>& st, const bf16* ks, const bf16* vs,
                                           const LaneOffsets<D>& off, const bf16x8* qreg, float sl2, bool masked,
-                                          int mbase, int width) {
+                                          const MaskArgs& mk) {
   constexpr int kKK = D / 16, kDT = D / 32;
   // Phase boundaries are pinned (sched_barrier) so that operand reads of a
   // later phase are not hoisted into an earlier one, where they would only
@@ -141,7 +156,7 @@ __device__ __forceinline__ void tile_pair(OnlineState<D>& st, const bf16* ks, co
   float x0[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) x0[i] = s0[i];
-  if (masked) band_mask(x0, mbase, width);
+  if (masked) apply_mask<TWO>(x0, mk, 0);
   float alpha0, nms0;
   bool moved0;
   reference_update(x0, st.m_ref, sl2, alpha0, moved0, nms0);
@@ -161,7 +176,7 @@ __device__ __forceinline__ void tile_pair(OnlineState<D>& st, const bf16* ks, co
   float x1[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) x1[i] = s1[i];
-  if (masked) band_mask(x1, mbase - 32, width);
+  if (masked) apply_mask<TWO>(x1, mk, 32);
   float alpha1, nms1;
   bool moved1;
   reference_update(x1, st.m_ref, sl2, alpha1, moved1, nms1);
@@ -183,10 +198,10 @@ __device__ __forceinline__ void tile_pair(OnlineState<D>& st, const bf16* ks, co
 }
 
 // Only half m of the tile meets the wave's rows (always masked).
-template <int D>
+template <int D, bool TWO>
 __device__ __forceinline__ void tile_half(OnlineState<D>& st, const bf16* ks, const bf16* vs,
-                                          const LaneOffsets<D>& off, const bf16x8* qreg, float sl2, int m, int mbase,
-                                          int width) {
+                                          const LaneOffsets<D>& off, const bf16x8* qreg, float sl2, int m,
+                                          const MaskArgs& mk) {
   constexpr int kKK = D / 16, kDT = D / 32;
   bf16x8 ka[kKK];
   load_ka<D>(ka, ks, off, 32 * m);
@@ -198,7 +213,7 @@ __device__ __forceinline__ void tile_half(OnlineState<D>& st, const bf16* ks, co
   float x[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = s[i];
-  band_mask(x, mbase - 32 * m, width);
+  apply_mask<TWO>(x, mk, 32 * m);
   float alpha, nms;
   bool moved;
   reference_update(x, st.m_ref, sl2, alpha, moved, nms);
@@ -208,7 +223,7 @@ __device__ __forceinline__ void tile_half(OnlineState<D>& st, const bf16* ks, co
   pv<D>(st, va, p0, p1);
 }
 
-template <int D>
+template <int D, bool TWO>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   constexpr int kTile = kBK * D;  // one K or V tile, bf16 elements
   using Tile = AsyncTile<kBK, D, kThreads / 64>;
@@ -228,8 +243,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   const int bh = item / p.n_qt;
   const int h = bh % p.H;
   const int N = p.N;
-  const int lo = p.bands.lo[h];
-  const int hi = p.bands.hi[h];
+  // the head's distance set: its band, joined with the local window if any
+  const DistSet dset = dist_set(p.bands.lo[h], p.bands.hi[h], TWO ? p.local_window : 0);
+  const int lo = dset.lo;
+  const int hi = dset.hi;
   const size_t base = (size_t)bh * N * D;
   const bf16* __restrict__ qb = p.q + base;
   const bf16* __restrict__ kb = p.k + base;
@@ -240,8 +257,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
 
   const int i_tile0 = t * kBQ;
   const int i_tile1 = min(N - 1, i_tile0 + kBQ - 1);
-  const KeySpan span = band_key_span(i_tile0, i_tile1, lo, hi);
-  if (span.last < span.first) {
+  KeySpan span2{0, -1};
+  if constexpr (TWO)
+    if (has_second(dset)) span2 = band_key_span(i_tile0, i_tile1, dset.nlo, dset.nhi);
+  const TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kBK);
+  if (walk.n == 0) {
     // No row of this tile has a key: output 0, LSE -inf.
     constexpr int kCpr = D / 8;
     for (int c = tid; c < kBQ * kCpr; c += kThreads) {
@@ -252,9 +272,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
       if (i_tile0 + r < N) lb[i_tile0 + r] = ninf;
     return;
   }
-  const int u_begin = span.first / kBK;
-  const int u_end = span.last / kBK + 1;
-
   const int iw0 = i_tile0 + 32 * wave;
   const int iw1 = min(N - 1, iw0 + 31);
   const bool wave_live = iw0 <= N - 1;
@@ -262,8 +279,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
 
   // First K / V tile before the Q loads: the two round trips overlap (the
   // wait for Q covers both).
-  Tile::load(smem, kb, u_begin * kBK, N, wave, lane);
-  Tile::load(smem + kTile, vb, u_begin * kBK, N, wave, lane);
+  Tile::load(smem, kb, walk.at(0) * kBK, N, wave, lane);
+  Tile::load(smem + kTile, vb, walk.at(0) * kBK, N, wave, lane);
 
   // Q^T operand: lane holds Q[iq][16kk + 8g .. +7].
   bf16x8 qreg[kKK];
@@ -282,35 +299,45 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   st.m_ref = ninf;
   st.l_run = 0.f;
   const float sl2 = p.scale_log2;
-  const int width = hi - lo;
 
   // One tile from LDS stage S (a compile-time constant, so every LDS offset
   // is an immediate).
-  auto step = [&](auto stage, int u) {
+  auto step = [&](auto stage, int v) {
     constexpr int S = decltype(stage)::value;
+    const int u = walk.at(v);
     wait_vmcnt<0>();  // this wave's part of tile u has landed
-    __syncthreads();  // ... everyone's, and everyone is done with tile u - 1
-    if (u + 1 < u_end) {
+    __syncthreads();  // ... everyone's, and everyone is done with the previous tile
+    if (v + 1 < walk.n) {
       bf16* nxt = smem + (S ^ 1) * 2 * kTile;
-      Tile::load(nxt, kb, (u + 1) * kBK, N, wave, lane);
-      Tile::load(nxt + kTile, vb, (u + 1) * kBK, N, wave, lane);
+      const int un = walk.at(v + 1);
+      Tile::load(nxt, kb, un * kBK, N, wave, lane);
+      Tile::load(nxt + kTile, vb, un * kBK, N, wave, lane);
     }
     const bf16* ks = smem + S * 2 * kTile;
     const bf16* vs = ks + kTile;
     off.refresh();
     const int jb = u * kBK;
-    const bool a0 = wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi);
-    const bool a1 = wave_live && tile_meets(iw0, iw1, jb + 32, jb + 63, lo, hi);
-    const int mbase = iq - jb - 8 * g - lo;
+    bool a0, a1, full;
+    if constexpr (TWO) {
+      a0 = wave_live && set_meets(iw0, iw1, jb, jb + 31, dset);
+      a1 = wave_live && set_meets(iw0, iw1, jb + 32, jb + 63, dset);
+      full = set_full(iw0, iw1, jb, jb + 63, dset);
+    } else {
+      a0 = wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi);
+      a1 = wave_live && tile_meets(iw0, iw1, jb + 32, jb + 63, lo, hi);
+      full = tile_full(iw0, iw1, jb, jb + 63, lo, hi);
+    }
+    const int rb = iq - jb - 8 * g;
+    const MaskArgs mk{rb - lo, hi - lo, rb - dset.nlo, dset.nhi - dset.nlo};
     if (a0 && a1) {
-      tile_pair<D>(st, ks, vs, off, qreg, sl2, !tile_full(iw0, iw1, jb, jb + 63, lo, hi), mbase, width);
+      tile_pair<D, TWO>(st, ks, vs, off, qreg, sl2, !full, mk);
     } else if (a0 || a1) {
-      tile_half<D>(st, ks, vs, off, qreg, sl2, a0 ? 0 : 1, mbase, width);
+      tile_half<D, TWO>(st, ks, vs, off, qreg, sl2, a0 ? 0 : 1, mk);
     }
   };
-  for (int u = u_begin; u < u_end; u += 2) {
-    step(std::integral_constant<int, 0>{}, u);
-    if (u + 1 < u_end) step(std::integral_constant<int, 1>{}, u + 1);
+  for (int v = 0; v < walk.n; v += 2) {
+    step(std::integral_constant<int, 0>{}, v);
+    if (v + 1 < walk.n) step(std::integral_constant<int, 1>{}, v + 1);
   }
 
   // ---- epilogue: O = acc / l, LSE = scale * m + ln(sum)
@@ -328,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
 }  // namespace
 
 int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                    int N, int d, const Bands& bands, float scale, hipStream_t stream) {
+                    int N, int d, const Bands& bands, int local_window, float scale, hipStream_t stream) {
   FwdArgs a;
   a.q = (const bf16*)q;
   a.k = (const bf16*)k;
@@ -339,15 +366,21 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   a.H = H;
   a.N = N;
   a.n_qt = (N + kBQ - 1) / kBQ;
+  a.local_window = local_window;
   a.scale_log2 = scale * kLog2e;
   a.bands = bands;
   const long long total = (long long)B * H * a.n_qt;
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   dim3 grid((unsigned)total), block(kThreads);
-  if (d == 128)
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, stream, a);
+  const bool two = local_window > 0;
+  if (d == 128 && !two)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
+  else if (d == 128)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
+  else if (d == 64 && !two)
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
   else if (d == 64)
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
   else
     return SPATTN_E_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;

@@ -8,18 +8,18 @@
 
 namespace spattn {
 int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                    const Bands& bands, float scale, hipStream_t stream);
+                    const Bands& bands, int local_window, float scale, hipStream_t stream);
 int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                    const Bands& bands, float scale, hipStream_t stream);
 void fwd_bf16_tiles(int* BQ, int* BK);
 void fwd_f32_tiles(int* BQ, int* BK);
 size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype);
 int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                  void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands, float scale,
-                  void* workspace, hipStream_t stream);
+                  void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
+                  int local_window, float scale, void* workspace, hipStream_t stream);
 int launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
-                    void* dv, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands, float scale,
-                    void* workspace, hipStream_t stream);
+                    void* dv, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
+                    int local_window, float scale, void* workspace, hipStream_t stream);
 
 namespace {
 
@@ -112,17 +112,31 @@ int spattn_band_table(int32_t N, int32_t H, int32_t* lo, int32_t* hi) {
   return SPATTN_OK;
 }
 
-int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H, int32_t N,
-               int32_t d, int32_t dtype, const int32_t* band_lo, const int32_t* band_hi, float scale, void* stream) {
+static int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
+                    int32_t N, int32_t d, int32_t dtype, const int32_t* band_lo, const int32_t* band_hi,
+                    int32_t local_window, float scale, void* stream) {
   int st = check_sizes(B, H, N, d, dtype);
   if (st != SPATTN_OK) return st;
-  if (!q || !k || !v || !o || !lse) return SPATTN_E_ARG;
+  if (!q || !k || !v || !o || !lse || local_window < 0) return SPATTN_E_ARG;
+  if (local_window > 0 && dtype != SPATTN_BF16) return SPATTN_E_UNSUPPORTED;
   Bands bands;
   st = make_bands(N, H, band_lo, band_hi, &bands);
   if (st != SPATTN_OK) return st;
   const float sc = resolve_scale(scale, d);
-  if (dtype == SPATTN_BF16) return launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, bands, sc, (hipStream_t)stream);
+  const int w = local_window < N ? local_window : N;
+  if (dtype == SPATTN_BF16) return launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, bands, w, sc, (hipStream_t)stream);
   return launch_fwd_f32(q, k, v, o, lse, B, H, N, d, bands, sc, (hipStream_t)stream);
+}
+
+int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H, int32_t N,
+               int32_t d, int32_t dtype, const int32_t* band_lo, const int32_t* band_hi, float scale, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, dtype, band_lo, band_hi, 0, scale, stream);
+}
+
+int spattn_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
+                     int32_t N, int32_t d, int32_t dtype, const int32_t* band_lo, const int32_t* band_hi,
+                     int32_t local_window, float scale, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, dtype, band_lo, band_hi, local_window, scale, stream);
 }
 
 size_t spattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype, int32_t grad_dtype) {
@@ -153,8 +167,8 @@ int spattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, co
   int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
   if (st != SPATTN_OK) return st;
   if (!q || !k || !v || !o || !lse || !dout || !dq) return SPATTN_E_ARG;
-  return launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, resolve_scale(scale, d),
-                       workspace, (hipStream_t)stream);
+  return launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, 0,
+                       resolve_scale(scale, d), workspace, (hipStream_t)stream);
 }
 
 int spattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
@@ -165,24 +179,42 @@ int spattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* ls
   int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
   if (st != SPATTN_OK) return st;
   if (!q || !k || !v || !lse || !dout || !dk || !dv) return SPATTN_E_ARG;
-  return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, resolve_scale(scale, d),
-                         workspace, (hipStream_t)stream);
+  return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, 0,
+                         resolve_scale(scale, d), workspace, (hipStream_t)stream);
+}
+
+static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                    void* dq, void* dk, void* dv, int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+                    int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi, int32_t local_window,
+                    float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  Bands bands;
+  int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
+  if (st != SPATTN_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || local_window < 0) return SPATTN_E_ARG;
+  if (local_window > 0 && dtype != SPATTN_BF16) return SPATTN_E_UNSUPPORTED;
+  const float sc = resolve_scale(scale, d);
+  const int w = local_window < N ? local_window : N;
+  st = launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, w, sc, workspace,
+                     (hipStream_t)stream);
+  if (st != SPATTN_OK) return st;
+  return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, w, sc, workspace,
+                         (hipStream_t)stream);
 }
 
 int spattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                void* dq, void* dk, void* dv, int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
                int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi, float scale, void* workspace,
                size_t workspace_bytes, void* stream) {
-  Bands bands;
-  int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
-  if (st != SPATTN_OK) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPATTN_E_ARG;
-  const float sc = resolve_scale(scale, d);
-  st = launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, sc, workspace,
-                     (hipStream_t)stream);
-  if (st != SPATTN_OK) return st;
-  return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, sc, workspace,
-                         (hipStream_t)stream);
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, grad_dtype, band_lo, band_hi, 0, scale,
+                  workspace, workspace_bytes, stream);
+}
+
+int spattn_bwd_local(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+                     int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi, int32_t local_window,
+                     float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, grad_dtype, band_lo, band_hi, local_window,
+                  scale, workspace, workspace_bytes, stream);
 }
 
 int spattn_kernel_tiles(int32_t d, int32_t dtype, int32_t* BQ, int32_t* BK) {

@@ -61,8 +61,10 @@ def dense_bands(N, H):
     return np.zeros(H, dtype=np.int32), np.full(H, N - 1, dtype=np.int32)
 
 
-def fwd(q, k, v, bands=None, scale=None, out=None, lse=None):
-    """Band attention forward.  Returns (o, lse); lse is float32 [B, H, N]."""
+def fwd(q, k, v, bands=None, scale=None, out=None, lse=None, local_window=0):
+    """Band attention forward.  Returns (o, lse); lse is float32 [B, H, N].
+    ``local_window`` > 0 joins the shared local window [0, w - 1] to every
+    head's band (spattn_fwd_local)."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     if out is None:
@@ -73,6 +75,12 @@ def fwd(q, k, v, bands=None, scale=None, out=None, lse=None):
     if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B, H, N]")
     p_lo, p_hi, _keep = _bands_arg(bands, H)
+    if local_window:
+        st = _lib.load().spattn_fwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                          _DT[q.dtype], p_lo, p_hi, int(local_window), float(scale or 0.0),
+                                          _stream_handle(q.device))
+        _lib.check(st, "spattn_fwd_local")
+        return out, lse
     st = _lib.load().spattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, _DT[q.dtype],
                                 p_lo, p_hi, float(scale or 0.0), _stream_handle(q.device))
     _lib.check(st, "spattn_fwd")
@@ -126,12 +134,21 @@ def bwd_dkdv(q, k, v, lse, dout, workspace, bands=None, scale=None, grad_dtype=N
     return out
 
 
-def bwd(q, k, v, o, lse, dout, bands=None, scale=None, grad_dtype=None, workspace=None, out=None):
+def bwd(q, k, v, o, lse, dout, bands=None, scale=None, grad_dtype=None, workspace=None, out=None,
+        local_window=0):
     """Band attention backward.  Returns (dq, dk, dv) of ``grad_dtype``
-    (default: the input dtype); ``out`` may supply preallocated (dq, dk, dv)."""
+    (default: the input dtype); ``out`` may supply preallocated (dq, dk, dv).
+    ``local_window`` as in ``fwd`` (spattn_bwd_local)."""
     B, H, N, d, grad_dtype, workspace, out = _bwd_prep(q, k, v, o, lse, dout, grad_dtype, workspace, out, 3)
     dq, dk, dv = out
     p_lo, p_hi, _keep = _bands_arg(bands, H)
+    if local_window:
+        st = _lib.load().spattn_bwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), B, H, N, d, _DT[q.dtype], _DT[grad_dtype], p_lo,
+                                          p_hi, int(local_window), float(scale or 0.0), _ptr(workspace),
+                                          workspace.numel(), _stream_handle(q.device))
+        _lib.check(st, "spattn_bwd_local")
+        return dq, dk, dv
     st = _lib.load().spattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                 _ptr(dv), B, H, N, d, _DT[q.dtype], _DT[grad_dtype], p_lo, p_hi,
                                 float(scale or 0.0), _ptr(workspace), workspace.numel(),

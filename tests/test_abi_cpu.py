@@ -138,3 +138,22 @@ def test_bwd_stage_validation():
                                ws, need, None) == _lib.E_ARG
     assert lib.spattn_bwd_dkdv(p, p, p, p, p, p, p, 0, 3, 100, 128, _lib.BF16, _lib.BF16, None, None, 0.0,
                                ws, need, None) == _lib.E_ARG
+
+
+def test_local_window_validation_before_launch():
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+
+    def fwd(w, dtype=_lib.BF16):
+        return lib.spattn_fwd_local(p, p, p, p, p, 1, 2, 8, 64, dtype, None, None, w, 0.0, None)
+
+    def bwd(w, dtype=_lib.BF16):
+        need = lib.spattn_bwd_workspace_bytes(1, 2, 8, 64, dtype, dtype)
+        return lib.spattn_bwd_local(p, p, p, p, p, p, p, p, p, 1, 2, 8, 64, dtype, dtype, None, None, w, 0.0,
+                                    ctypes.c_void_p(256), need, None)
+    assert fwd(-1) == _lib.E_ARG
+    assert bwd(-1) == _lib.E_ARG
+    assert fwd(3, dtype=_lib.F32) == _lib.E_UNSUPPORTED   # the local window is bfloat16 only
+    assert bwd(3, dtype=_lib.F32) == _lib.E_UNSUPPORTED
+    ptr0 = ctypes.c_void_p(0)
+    assert lib.spattn_fwd_local(ptr0, p, p, p, p, 1, 2, 8, 64, _lib.BF16, None, None, 3, 0.0, None) == _lib.E_ARG
