@@ -9,8 +9,10 @@ B = 8, H = 16, N = 4096, d = 128, bfloat16 inputs resident in HBM.
 Prints ONE JSON line.  ``value`` is in-band TFLOP/s of fwd+bwd (14 d FLOP per
 attended pair; the heads together attend N(N+1)/2 pairs per sequence).
 Extra keys report the forward alone, the dense-causal kernel of the same
-library at the same shape, the roofline of the dominant kernel and the
-float64 CPU oracle timed on this host.
+library at the same shape, the roofline of the dominant kernel, the float64
+CPU oracle timed on this host and, under "variants", the same shape with the
+band tables of the page's ablation patterns (sliding window, gapped half
+bands) and with a shared local window joined to every band.
 """
 import argparse
 import json
@@ -56,13 +58,27 @@ def measured_traffic(kernel):
     return None if k is None else int(k["traffic_bytes"])
 
 
-def pairs_total(lo, hi):
+def pairs_total(lo, hi, local_window=0):
+    """Attended causal pairs over all heads and the batch: per head, the
+    distances in [lo_h, hi_h] (joined with [0, local_window - 1]), each
+    distance d contributing N - d query rows."""
     tot = 0
     for l, u in zip(lo, hi):
-        l, u = int(l), int(u)
-        if u >= l:
-            w = u - l + 1
-            tot += w * (2 * N - l - u) // 2
+        ranges = []
+        if int(u) >= int(l):
+            ranges.append([int(l), int(u)])
+        if local_window > 0:
+            ranges.append([0, min(N, local_window) - 1])
+        ranges.sort()
+        merged = []
+        for a, b in ranges:
+            if merged and a <= merged[-1][1] + 1:
+                merged[-1][1] = max(merged[-1][1], b)
+            else:
+                merged.append([a, b])
+        for a, b in merged:
+            w = b - a + 1
+            tot += w * (2 * N - a - b) // 2
     return tot * B
 
 
@@ -73,6 +89,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal comparison")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the ablation-pattern and local-window measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -151,7 +169,8 @@ def main():
     T = B * H * N * D * 2
     R = B * H * N * 4
     alg_bytes = {"fwd": 4 * T + R, "bwd_dq": 6 * T + 2 * R, "bwd_dkdv": 6 * T + 2 * R}
-    kern_names = {"fwd": "fwd_bf16_kernel<128>", "bwd_dq": "bwd_dq_kernel<128>", "bwd_dkdv": "bwd_dkdv_kernel<128>"}
+    kern_names = {"fwd": "fwd_bf16_kernel<128, false>", "bwd_dq": "bwd_dq_kernel<128, false>",
+                  "bwd_dkdv": "bwd_dkdv_kernel<128, false>"}
     dom = max(per, key=per.get)
     gbs = alg_bytes[dom] / (per[dom] * 1e-3) / 1e9
     roofline = {
@@ -202,6 +221,45 @@ def main():
             "speedup_fwdbwd": round(dms / ms_per_step, 3), "speedup_fwd": round(dfwd / fwd_ms, 3),
             "dense_tflops_fwdbwd": round(14 * D * pairs_total(dlo, dhi) / (dms * 1e-3) / 1e12, 2),
         }
+
+    if not args.no_variants:
+        def timed_total(bands, lw, steps, warmup):
+            """fwd and bwd (both stages) of the whole batch with these bands /
+            local window; HIP events on the launch stream."""
+            for _ in range(warmup):
+                ops.fwd(q, k, v, bands=bands, out=o, lse=lse, local_window=lw)
+                ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads, local_window=lw)
+            torch.cuda.synchronize()
+            ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+            t0 = time.perf_counter()
+            for e0, e1, e2 in ev:
+                e0.record()
+                ops.fwd(q, k, v, bands=bands, out=o, lse=lse, local_window=lw)
+                e1.record()
+                ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads, local_window=lw)
+                e2.record()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) * 1e3 / steps
+            f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+            b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+            return wall, f, b
+
+        variants = {}
+        nvs = max(3, args.steps // 4)
+        wlo, whi = ops.window_bands(N, H, N // H)
+        glo, ghi = ops.gapped_half_bands(N, H)
+        for name, bands, lw, (plo, phi) in (
+                (f"sliding_window_{N // H}", (wlo, whi), 0, (wlo, whi)),
+                ("gapped_half_bands", (glo, ghi), 0, (glo, ghi)),
+                ("bands_plus_local_window_64", None, 64, (lo, hi))):
+            wall_v, f_v, b_v = timed_total(bands, lw, nvs, 2)
+            pv = pairs_total(plo, phi, lw)
+            variants[name] = {
+                "ms_per_step": round(wall_v, 4), "fwd_ms": round(f_v, 4), "bwd_ms": round(b_v, 4),
+                "attended_pairs": pv,
+                "tflops_fwdbwd": round(14 * D * pv / (wall_v * 1e-3) / 1e12, 2),
+            }
+        out["variants"] = variants
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, lo, hi, fl_all)

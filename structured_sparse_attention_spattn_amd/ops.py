@@ -61,6 +61,26 @@ def dense_bands(N, H):
     return np.zeros(H, dtype=np.int32), np.full(H, N - 1, dtype=np.int32)
 
 
+def window_bands(N, H, window):
+    """Sliding-window pattern ("Making Every Head Count", Figure 2(a)): every
+    head covers distances [0, window - 1] (window 0: empty bands)."""
+    w = max(0, min(int(window), N))
+    if w == 0:
+        return np.full(H, N, dtype=np.int32), np.full(H, N - 1, dtype=np.int32)
+    return np.zeros(H, dtype=np.int32), np.full(H, w - 1, dtype=np.int32)
+
+
+def gapped_half_bands(N, H):
+    """Gapped-bands pattern (same figure, (c)): each head keeps the first half
+    of its Balanced Distance Partitioning band, the half-width rounded down (a
+    width-1 band becomes empty)."""
+    lo, hi = band_table(N, H)
+    half = (hi - lo + 1) // 2
+    lo2 = np.where(half == 0, N, lo).astype(np.int32)
+    hi2 = np.where(half == 0, N - 1, lo + half - 1).astype(np.int32)
+    return lo2, hi2
+
+
 def fwd(q, k, v, bands=None, scale=None, out=None, lse=None, local_window=0):
     """Band attention forward.  Returns (o, lse); lse is float32 [B, H, N].
     ``local_window`` > 0 joins the shared local window [0, w - 1] to every

@@ -157,3 +157,14 @@ def test_local_window_validation_before_launch():
     assert bwd(3, dtype=_lib.F32) == _lib.E_UNSUPPORTED
     ptr0 = ctypes.c_void_p(0)
     assert lib.spattn_fwd_local(ptr0, p, p, p, p, 1, 2, 8, 64, _lib.BF16, None, None, 3, 0.0, None) == _lib.E_ARG
+
+
+@pytest.mark.parametrize("N,H", [(1024, 8), (4096, 16), (7, 3), (5, 9), (10000, 12)])
+def test_pattern_tables_match_oracle(N, H):
+    for w in (0, 1, N // H, N, N + 5):
+        lo, hi = ops.window_bands(N, H, w)
+        olo, ohi = oracle.band_table_sliding_window(N, H, w)
+        assert np.array_equal(lo, olo) and np.array_equal(hi, ohi), w
+    lo, hi = ops.gapped_half_bands(N, H)
+    olo, ohi = oracle.band_table_gapped_half(N, H)
+    assert np.array_equal(lo, olo) and np.array_equal(hi, ohi)
