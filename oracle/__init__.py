@@ -30,7 +30,8 @@ Readings where the pages are silent (each listed in the design notes):
   gives one).
 
 Modules: ``band`` (band table), ``attention`` (forward/backward, three
-independent forms), ``tiles`` (canonical band-tile lists).
+independent forms; optional shared local window), ``tiles`` (canonical
+band-tile lists), ``decode`` (single-query attention over a key/value cache).
 """
 from .band import band_table, band_pairs, band_table_sliding_window, band_table_gapped_half
 from .attention import (
@@ -44,10 +45,11 @@ from .attention import (
     band_attention_bwd_rows,
 )
 from .tiles import query_tile_list, key_tile_list
+from .decode import decode_key_set, decode_attention
 
 __all__ = [
     "band_table", "band_pairs", "band_table_sliding_window", "band_table_gapped_half",
     "masked_attention_literal", "masked_attention_dense", "masked_attention_dense_bwd",
     "band_mask", "band_attention_fwd", "band_attention_bwd", "band_attention_fwd_rows", "band_attention_bwd_rows",
-    "query_tile_list", "key_tile_list",
+    "query_tile_list", "key_tile_list", "decode_key_set", "decode_attention",
 ]
