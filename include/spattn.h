@@ -146,6 +146,29 @@ int spattn_bwd_local(const void* q, const void* k, const void* v, const void* o,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Decode step: one new query per sequence against a key/value cache.  For
+ * sequence b with L_b valid cache rows the query sits at position
+ * i = L_b - 1 and head h attends
+ *     S = { j : 0 <= j <= i, lo_h <= i - j <= hi_h  or  i - j < local_window }
+ * through the same masked-set softmax as spattn_fwd (the method's formula
+ * evaluated for the newest query; the pages measure training only).
+ *   q        device [B,H,d] of dtype; o device [B,H,d] of dtype, written.
+ *   k_cache, v_cache  device [B,H,Nmax,d] of dtype, rows 0 .. L_b - 1 read.
+ *   lse      device [B,H] float32, written (-inf for an empty set).
+ *   lengths  device [B] int32 (values clamped to 0 .. Nmax; 0 gives o = 0,
+ *            lse = -inf), or NULL for L_b = Nmax.
+ *   band_lo, band_hi  host, H int32 each (validated against Nmax as in
+ *            spattn_fwd), or both NULL for the Balanced Distance Partitioning
+ *            table of (Nmax, H).
+ *   local_window  >= 0, as in spattn_fwd_local; float32 and bfloat16 both.
+ * Errors: as spattn_fwd, plus SPATTN_E_ARG for local_window < 0.
+ */
+int spattn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                  float* lse, const int32_t* lengths, int32_t B, int32_t H, int32_t Nmax,
+                  int32_t d, int32_t dtype, const int32_t* band_lo, const int32_t* band_hi,
+                  int32_t local_window, float scale, void* stream);
+
+/*
  * The two stages spattn_bwd runs, exported for callers that schedule them
  * separately (and for per-kernel timing).  Same arguments and checks as
  * spattn_bwd; together they compute exactly what spattn_bwd computes.

@@ -11,6 +11,9 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
                     const Bands& bands, int local_window, float scale, hipStream_t stream);
 int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                    const Bands& bands, float scale, hipStream_t stream);
+int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* lengths, int B,
+                  int H, int Nmax, int d, int dtype, const Bands& bands, int local_window, float scale,
+                  hipStream_t stream);
 void fwd_bf16_tiles(int* BQ, int* BK);
 void fwd_f32_tiles(int* BQ, int* BK);
 size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype);
@@ -215,6 +218,20 @@ int spattn_bwd_local(const void* q, const void* k, const void* v, const void* o,
                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, grad_dtype, band_lo, band_hi, local_window,
                   scale, workspace, workspace_bytes, stream);
+}
+
+int spattn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                  const int32_t* lengths, int32_t B, int32_t H, int32_t Nmax, int32_t d, int32_t dtype,
+                  const int32_t* band_lo, const int32_t* band_hi, int32_t local_window, float scale, void* stream) {
+  int st = check_sizes(B, H, Nmax, d, dtype);
+  if (st != SPATTN_OK) return st;
+  if (!q || !k_cache || !v_cache || !o || !lse || local_window < 0) return SPATTN_E_ARG;
+  Bands bands;
+  st = make_bands(Nmax, H, band_lo, band_hi, &bands);
+  if (st != SPATTN_OK) return st;
+  const int w = local_window < Nmax ? local_window : Nmax;
+  return launch_decode(q, k_cache, v_cache, o, lse, lengths, B, H, Nmax, d, dtype, bands, w,
+                       resolve_scale(scale, d), (hipStream_t)stream);
 }
 
 int spattn_kernel_tiles(int32_t d, int32_t dtype, int32_t* BQ, int32_t* BK) {

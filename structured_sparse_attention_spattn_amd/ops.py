@@ -107,6 +107,32 @@ def fwd(q, k, v, bands=None, scale=None, out=None, lse=None, local_window=0):
     return out, lse
 
 
+def decode(q, k_cache, v_cache, lengths=None, bands=None, local_window=0, scale=None, out=None, lse=None):
+    """Decode step: q [B, H, d] against caches [B, H, Nmax, d]; ``lengths``
+    an int32 device tensor [B] of valid cache rows (None: all Nmax).
+    Returns (o [B, H, d], lse float32 [B, H])."""
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, H, d] and the caches [B, H, Nmax, d]")
+    B, H, Nmax, d = k_cache.shape
+    if q.shape != (B, H, d) or q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise ValueError("q and caches disagree in shape or dtype")
+    for t in (q, k_cache, v_cache):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("tensors must be contiguous and on the GPU")
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.shape != (B,) or not lengths.is_cuda):
+        raise ValueError("lengths must be an int32 GPU tensor of shape [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    p_lo, p_hi, _keep = _bands_arg(bands, H)
+    st = _lib.load().spattn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                   None if lengths is None else _ptr(lengths), B, H, Nmax, d, _DT[q.dtype], p_lo,
+                                   p_hi, int(local_window), float(scale or 0.0), _stream_handle(q.device))
+    _lib.check(st, "spattn_decode")
+    return out, lse
+
+
 def bwd_workspace_bytes(B, H, N, d, dtype, grad_dtype):
     return int(_lib.load().spattn_bwd_workspace_bytes(B, H, N, d, _DT[dtype], _DT[grad_dtype]))
 

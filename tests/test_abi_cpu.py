@@ -168,3 +168,16 @@ def test_pattern_tables_match_oracle(N, H):
     lo, hi = ops.gapped_half_bands(N, H)
     olo, ohi = oracle.band_table_gapped_half(N, H)
     assert np.array_equal(lo, olo) and np.array_equal(hi, ohi)
+
+
+def test_decode_validation_before_launch():
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+
+    def dec(w=0, d=128, dtype=_lib.BF16, B=2, ptr=p):
+        return lib.spattn_decode(ptr, p, p, p, p, None, B, 4, 64, d, dtype, None, None, w, 0.0, None)
+    assert dec(w=-1) == _lib.E_ARG
+    assert dec(d=96) == _lib.E_UNSUPPORTED
+    assert dec(dtype=9) == _lib.E_UNSUPPORTED
+    assert dec(B=0) == _lib.E_ARG
+    assert dec(ptr=ctypes.c_void_p(0)) == _lib.E_ARG
