@@ -261,6 +261,40 @@ def main():
             }
         out["variants"] = variants
 
+        # decode step (one new query per sequence) over a full key/value cache
+        # of the same head layout; the caches come from a seeded device
+        # generator (synthetic N(0, 1), quantised to bfloat16)
+        dB = 64
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(SEED)
+        qd = torch.randn((dB, H, D), generator=gen, device=dev).to(torch.bfloat16)
+        kc = torch.randn((dB, H, N, D), generator=gen, device=dev).to(torch.bfloat16)
+        vc = torch.randn((dB, H, N, D), generator=gen, device=dev).to(torch.bfloat16)
+        od = torch.empty_like(qd)
+        ld = torch.empty((dB, H), dtype=torch.float32, device=dev)
+        for _ in range(5):
+            ops.decode(qd, kc, vc, out=od, lse=ld)
+        torch.cuda.synchronize()
+        n_dec = 50
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_dec):
+            ops.decode(qd, kc, vc, out=od, lse=ld)
+        e1.record()
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / n_dec
+        keys = sum(min(N - 1, int(u)) - int(l_) + 1 for l_, u in zip(lo, hi) if int(u) >= int(l_))  # at i = N - 1
+        dec_bytes = dB * (keys * 2 * D * 2 + H * (2 * D * 2 + 4))
+        out["decode"] = {
+            "workload": f"decode, bf16, B={dB} H={H} cache={N} d={D}, BDP bands, full caches",
+            "us_per_step": round(dec_ms * 1e3, 2),
+            "tokens_per_s": round(dB / (dec_ms * 1e-3), 1),
+            "gather_bytes": dec_bytes,
+            "gbs": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        del kc, vc
+
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, lo, hi, fl_all)
 
