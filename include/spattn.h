@@ -131,8 +131,7 @@ int spattn_bwd(const void* q, const void* k, const void* v, const void* o,
  * i.e. its band joined with the distances [0, local_window - 1] that every
  * head shares.  local_window = 0 is exactly spattn_fwd / spattn_bwd; widths
  * above N act as N.  Arguments, outputs and errors as spattn_fwd and
- * spattn_bwd, plus SPATTN_E_ARG for local_window < 0 and SPATTN_E_UNSUPPORTED
- * for local_window > 0 with float32 inputs (bfloat16 only).
+ * spattn_bwd, plus SPATTN_E_ARG for local_window < 0.  Both dtypes.
  */
 int spattn_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
                      int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,

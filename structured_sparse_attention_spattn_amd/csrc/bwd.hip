@@ -60,6 +60,7 @@ struct BwdF32Args {
   float* dk;
   float* dv;
   int B, H, N;
+  int local_window;  // shared local window width (0: exclusive bands)
   float scale;
   Bands bands;
 };
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dq_kernel(BwdF32Args p) {
   const int i = (int)(row % p.N);
   const long long bh = row / p.N;
   const int h = (int)(bh % p.H);
-  const int lo = p.bands.lo[h], hi = p.bands.hi[h];
+  const DistSet ds_ = dist_set(p.bands.lo[h], p.bands.hi[h], p.local_window);
   const size_t base = (size_t)bh * p.N * D;
   float qi[kE], di[kE], acc[kE];
 #pragma unroll
@@ -85,8 +86,11 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dq_kernel(BwdF32Args p) {
     acc[e] = 0.f;
   }
   const float lse = p.lse[row], dd = p.dvec[row];
-  const KeySpan ks = band_key_span(i, i, lo, hi);
-  for (int j = ks.first; j <= ks.last; ++j) {
+  // keys of row i: the primary range, then the disjoint second range if any
+  KeySpan spans[2] = {band_key_span(i, i, ds_.lo, ds_.hi), KeySpan{0, -1}};
+  if (has_second(ds_)) spans[1] = band_key_span(i, i, ds_.nlo, ds_.nhi);
+  for (int sp = 0; sp < 2; ++sp)
+  for (int j = spans[sp].first; j <= spans[sp].last; ++j) {
     float kj[kE], vj[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dkdv_kernel(BwdF32Args p) {
   const int j = (int)(row % p.N);
   const long long bh = row / p.N;
   const int h = (int)(bh % p.H);
-  const int lo = p.bands.lo[h], hi = p.bands.hi[h];
+  const DistSet ds_ = dist_set(p.bands.lo[h], p.bands.hi[h], p.local_window);
   const size_t base = (size_t)bh * p.N * D;
   const size_t lbase = (size_t)bh * p.N;
   float kj[kE], vj[kE], dk[kE], dv[kE];
@@ -126,8 +130,11 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dkdv_kernel(BwdF32Args p) {
     dk[e] = 0.f;
     dv[e] = 0.f;
   }
-  const KeySpan qs = band_query_span(j, j, lo, hi, p.N);
-  for (int i = qs.first; i <= qs.last; ++i) {
+  // queries reaching key j: the primary range, then the disjoint second range if any
+  KeySpan spans[2] = {band_query_span(j, j, ds_.lo, ds_.hi, p.N), KeySpan{0, -1}};
+  if (has_second(ds_)) spans[1] = band_query_span(j, j, ds_.nlo, ds_.nhi, p.N);
+  for (int sp = 0; sp < 2; ++sp)
+  for (int i = spans[sp].first; i <= spans[sp].last; ++i) {
     float qi[kE], di[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
@@ -169,7 +176,8 @@ int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const floa
                          float scale, float* dvec, hipStream_t stream);
 
 static BwdF32Args f32_args(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
-                           void* dk, void* dv, int B, int H, int N, const Bands& bands, float scale, float* dvec) {
+                           void* dk, void* dv, int B, int H, int N, const Bands& bands, int local_window,
+                           float scale, float* dvec) {
   BwdF32Args a;
   a.q = (const float*)q;
   a.k = (const float*)k;
@@ -183,6 +191,7 @@ static BwdF32Args f32_args(const void* q, const void* k, const void* v, const fl
   a.B = B;
   a.H = H;
   a.N = N;
+  a.local_window = local_window;
   a.scale = scale;
   a.bands = bands;
   return a;
@@ -196,7 +205,6 @@ int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, co
   if (dtype == SPATTN_BF16)
     return launch_bwd_dq_bf16(q, k, v, o, lse, dout, dq, B, H, N, d, grad_dtype == SPATTN_F32, bands, local_window,
                               scale, dvec, stream);
-  if (local_window > 0) return SPATTN_E_UNSUPPORTED;
   const long long rows = (long long)B * H * N;
   {
     const long long threads = rows * (d / 8);
@@ -209,7 +217,7 @@ int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, co
                          dvec, rows);
     if (hipGetLastError() != hipSuccess) return SPATTN_E_HIP;
   }
-  BwdF32Args a = f32_args(q, k, v, lse, dout, dq, nullptr, nullptr, B, H, N, bands, scale, dvec);
+  BwdF32Args a = f32_args(q, k, v, lse, dout, dq, nullptr, nullptr, B, H, N, bands, local_window, scale, dvec);
   dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);
   if (d == 128)
     hipLaunchKernelGGL(bwd_f32_dq_kernel<128>, grid, block, 0, stream, a);
@@ -226,9 +234,8 @@ int launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* ls
   if (dtype == SPATTN_BF16)
     return launch_bwd_dkdv_bf16(q, k, v, lse, dout, dk, dv, B, H, N, d, grad_dtype == SPATTN_F32, bands,
                                 local_window, scale, dvec, stream);
-  if (local_window > 0) return SPATTN_E_UNSUPPORTED;
   const long long rows = (long long)B * H * N;
-  BwdF32Args a = f32_args(q, k, v, lse, dout, nullptr, dk, dv, B, H, N, bands, scale, dvec);
+  BwdF32Args a = f32_args(q, k, v, lse, dout, nullptr, dk, dv, B, H, N, bands, local_window, scale, dvec);
   dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);
   if (d == 128)
     hipLaunchKernelGGL(bwd_f32_dkdv_kernel<128>, grid, block, 0, stream, a);

@@ -26,6 +26,7 @@ struct FwdF32Args {
   float* lse;
   int B, H, N;
   int n_qt;
+  int local_window;  // shared local window width (0: exclusive bands)
   float scale_log2;
   Bands bands;
 };
@@ -58,8 +59,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
   const int bh = item / p.n_qt;
   const int h = bh % p.H;
   const int N = p.N;
-  const int lo = p.bands.lo[h];
-  const int hi = p.bands.hi[h];
+  // the head's distance set: its band, joined with the local window if any
+  const DistSet dset = dist_set(p.bands.lo[h], p.bands.hi[h], p.local_window);
+  const int lo = dset.lo;
+  const int hi = dset.hi;
   const size_t base = (size_t)bh * N * D;
   const float* __restrict__ qb = p.q + base;
   const float* __restrict__ kb = p.k + base;
@@ -70,8 +73,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
 
   const int i_tile0 = t * kBQ;
   const int i_tile1 = min(N - 1, i_tile0 + kBQ - 1);
-  const KeySpan span = band_key_span(i_tile0, i_tile1, lo, hi);
-  if (span.last < span.first) {
+  KeySpan span2{0, -1};
+  if (has_second(dset)) span2 = band_key_span(i_tile0, i_tile1, dset.nlo, dset.nhi);
+  const TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kBK);
+  if (walk.n == 0) {
     for (int c = tid; c < kBQ * (D / 4); c += kThreads) {
       const int r = c / (D / 4), cc = c % (D / 4);
       if (i_tile0 + r < N) *(f32x4*)(ob + (size_t)(i_tile0 + r) * D + cc * 4) = f32x4{0, 0, 0, 0};
@@ -80,9 +85,6 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
       if (i_tile0 + r < N) lb[i_tile0 + r] = ninf;
     return;
   }
-  const int u_begin = span.first / kBK;
-  const int u_end = span.last / kBK + 1;
-
   const int iw0 = i_tile0 + 32 * wave;
   const int iw1 = min(N - 1, iw0 + 31);
   const bool wave_live = iw0 <= N - 1;
@@ -127,18 +129,18 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
   float m_run = ninf, l_run = 0.f;
   const float sl2 = p.scale_log2;
 
-  load_tile(u_begin);
+  load_tile(walk.at(0));
   store_tile(0);
   __syncthreads();
 
-  for (int u = u_begin; u < u_end; ++u) {
-    const int s = (u - u_begin) & 1;
-    const bool has_next = u + 1 < u_end;
-    if (has_next) load_tile(u + 1);
+  for (int v = 0; v < walk.n; ++v) {
+    const int s = v & 1;
+    const bool has_next = v + 1 < walk.n;
+    if (has_next) load_tile(walk.at(v + 1));
     const float* ks = smem + s * SM::kStage;
     const float* vs = ks + SM::kKStage;
-    const int jb = u * kBK;
-    const bool act = wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi);
+    const int jb = walk.at(v) * kBK;
+    const bool act = wave_live && set_meets(iw0, iw1, jb, jb + 31, dset);
     if (act) {
       f32x16 sacc;
 #pragma unroll
@@ -146,12 +148,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
 #pragma unroll
       for (int kk = 0; kk < kKK; ++kk) sacc = mfma32_f32(ks[c32 * SM::kKRow + 2 * kk + g], qreg[kk], sacc);
       float x[16];
-      const bool full = tile_full(iw0, iw1, jb, jb + 31, lo, hi);
+      const bool full = set_full(iw0, iw1, jb, jb + 31, dset);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int j = jb + 8 * (i >> 2) + 4 * g + (i & 3);
         const int dist = iq - j;
-        x[i] = (full || (dist >= lo && dist <= hi)) ? sacc[i] * sl2 : ninf;
+        const bool in = (dist >= lo && dist <= hi) || (dist >= dset.nlo && dist <= dset.nhi);
+        x[i] = (full || in) ? sacc[i] * sl2 : ninf;
       }
       float mx = ninf;
 #pragma unroll
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
 }  // namespace
 
 int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                   int N, int d, const Bands& bands, float scale, hipStream_t stream) {
+                   int N, int d, const Bands& bands, int local_window, float scale, hipStream_t stream) {
   FwdF32Args a;
   a.q = (const float*)q;
   a.k = (const float*)k;
@@ -213,6 +216,7 @@ int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
   a.H = H;
   a.N = N;
   a.n_qt = (N + kBQ - 1) / kBQ;
+  a.local_window = local_window;
   a.scale_log2 = scale * kLog2e;
   a.bands = bands;
   const long long total = (long long)B * H * a.n_qt;

@@ -10,7 +10,7 @@ namespace spattn {
 int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                     const Bands& bands, int local_window, float scale, hipStream_t stream);
 int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                   const Bands& bands, float scale, hipStream_t stream);
+                   const Bands& bands, int local_window, float scale, hipStream_t stream);
 int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* lengths, int B,
                   int H, int Nmax, int d, int dtype, const Bands& bands, int local_window, float scale,
                   hipStream_t stream);
@@ -121,14 +121,13 @@ static int fwd_impl(const void* q, const void* k, const void* v, void* o, float*
   int st = check_sizes(B, H, N, d, dtype);
   if (st != SPATTN_OK) return st;
   if (!q || !k || !v || !o || !lse || local_window < 0) return SPATTN_E_ARG;
-  if (local_window > 0 && dtype != SPATTN_BF16) return SPATTN_E_UNSUPPORTED;
   Bands bands;
   st = make_bands(N, H, band_lo, band_hi, &bands);
   if (st != SPATTN_OK) return st;
   const float sc = resolve_scale(scale, d);
   const int w = local_window < N ? local_window : N;
   if (dtype == SPATTN_BF16) return launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, bands, w, sc, (hipStream_t)stream);
-  return launch_fwd_f32(q, k, v, o, lse, B, H, N, d, bands, sc, (hipStream_t)stream);
+  return launch_fwd_f32(q, k, v, o, lse, B, H, N, d, bands, w, sc, (hipStream_t)stream);
 }
 
 int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H, int32_t N,
@@ -194,7 +193,6 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
   if (st != SPATTN_OK) return st;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || local_window < 0) return SPATTN_E_ARG;
-  if (local_window > 0 && dtype != SPATTN_BF16) return SPATTN_E_UNSUPPORTED;
   const float sc = resolve_scale(scale, d);
   const int w = local_window < N ? local_window : N;
   st = launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, w, sc, workspace,

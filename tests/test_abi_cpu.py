@@ -153,8 +153,7 @@ def test_local_window_validation_before_launch():
                                     ctypes.c_void_p(256), need, None)
     assert fwd(-1) == _lib.E_ARG
     assert bwd(-1) == _lib.E_ARG
-    assert fwd(3, dtype=_lib.F32) == _lib.E_UNSUPPORTED   # the local window is bfloat16 only
-    assert bwd(3, dtype=_lib.F32) == _lib.E_UNSUPPORTED
+    assert fwd(-2, dtype=_lib.F32) == _lib.E_ARG
     ptr0 = ctypes.c_void_p(0)
     assert lib.spattn_fwd_local(ptr0, p, p, p, p, 1, 2, 8, 64, _lib.BF16, None, None, 3, 0.0, None) == _lib.E_ARG
 

@@ -192,3 +192,33 @@ def test_local_full_closed_form_zero_queries():
             err = np.max(np.abs(o_h[b, h] - mean))
             assert err <= TOL, (h, b, err)
             assert np.max(np.abs(lse_h[b, h] - np.log(cnt))) <= 1e-3, h
+
+
+LOCAL_F32 = [
+    # (B, H, N, d, window, bands, seed): float32 inputs and gradients, bar 1e-4 max-abs
+    (1, 4, 300, 64, 16, "bdp", 121),
+    (2, 3, 257, 128, 120, "bdp", 122),
+    (1, 9, 7, 64, 2, "bdp", 123),
+    (1, 5, 200, 64, 7, "odd", 124),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,w,bk,seed", LOCAL_F32)
+def test_local_f32_vs_oracle(B, H, N, d, w, bk, seed):
+    _say(f"local window f32 B={B} H={H} N={N} d={d} w={w} {bk} seed={seed}")
+    inp = make_inputs(B, H, N, d, dtype="f32", seed=seed, with_dout=True)
+    band_arg, (lo, hi) = _bands(bk, N, H)
+    x = {n: t.to(DEV) for n, t in inp.items()}
+    o, lse = ops.fwd(x["q"], x["k"], x["v"], bands=band_arg, local_window=w)
+    dq, dk, dv = ops.bwd(x["q"], x["k"], x["v"], o, lse, x["dout"], bands=band_arg, local_window=w)
+    torch.cuda.synchronize()
+    q, k, v, do = (as_f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    ro, rl = oracle.band_attention_fwd(q, k, v, lo, hi, local_window=w)
+    rq, rk, rv, _, _ = oracle.band_attention_bwd(q, k, v, do, lo, hi, local_window=w)
+    lse_h = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(lse_h), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert np.max(np.abs(lse_h[fin] - rl[fin]), initial=0) <= 1e-4
+    for got, ref, nm in ((o, ro, "O"), (dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        err = float(np.max(np.abs(got.cpu().numpy().astype(np.float64) - ref)))
+        assert err <= 1e-4, f"{nm}: max-abs {err:.3e}"
