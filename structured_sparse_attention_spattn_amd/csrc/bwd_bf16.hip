@@ -367,8 +367,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         out[12 + e] = d[e];
       }
     };
-    // dS wave, visit v (one iteration late): dS = P (dP - D) scale and
-    // dK += dS^T Q.  P comes masked from the P wave (0 outside the band and
+    // dS wave, visit v (one iteration late): dS = P (dP - D) and
+    // dK += dS^T Q (the scale is applied to dK once, after the walk).  P comes masked from the P wave (0 outside the band and
     // on rows past N), so no mask is needed here.
     auto ds_dk = [&](int v, const f32x16& dpv) {
       const int st = v % kKvStages;
@@ -385,8 +385,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       const f16x8 pa = src[0], pb = src[1];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        ds[i] = (float)pa[i] * __builtin_fmaf(dpv[i], scl, -dd[i] * scl);
-        ds[8 + i] = (float)pb[i] * __builtin_fmaf(dpv[8 + i], scl, -dd[8 + i] * scl);
+        ds[i] = (float)pa[i] * (dpv[i] - dd[i]);
+        ds[8 + i] = (float)pb[i] * (dpv[8 + i] - dd[8 + i]);
       }
       const bf16x8 op0 = pack8(&ds[0]), op1 = pack8(&ds[8]);
       __builtin_amdgcn_sched_barrier(0);
@@ -418,123 +418,142 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         return wave_live && tile_meets(i0, i1, kw0, kw1, lo, hi);
     };
 
+    // Both roles run every visit of the walk with the same straight-line
+    // body: a block whose rows miss this wave's keys gets P = 0 from the P
+    // wave (so the dS wave's dK update adds zeros), instead of branching
+    // around the products -- branches there made the compiler shuttle the
+    // 32 x d accumulators between register sets on every block.
     if (pwave) {
       // dV += P^T dO runs one block late as well, so the exponentials of
-      // block tq issue between the dV products of block tq - 1 (whose dO tile
+      // block v issue between the dV products of block v - 1 (whose dO tile
       // the ring still holds for the dS wave's Q).
       LaneOffsets<D> off(lane);
       bf16x8 pp0{}, pp1{};  // packed P of the previous block
-      bool act_prev = false;
       auto dv_operands = [&](int v, bf16x8* bb) {
         const bf16* dos = smem + (v % kKvStages) * 2 * kTile + kTile;
         load_va<D>(bb, dos, off, 0);
       };
-      auto dv_update = [&](const bf16x8* bb, bf16x8 p0, bf16x8 p1) {
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(p0, bb[2 * dt], acc[dt]);
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(p1, bb[2 * dt + 1], acc[dt]);
-      };
-      for (int v = 0; v < n_visit; ++v) {
+      // within-tile row offset of accumulator register i, less 8 g
+      auto creg = [](int i) { return ((i >> 3) << 4) + (i & 7); };
+      auto p_block = [&](int v, auto has_prev) {
         block_start(v);
         off.refresh();
+        const int s = v % kKvStages;
+        const bf16* qs = smem + s * 2 * kTile;
+        const int i0 = walk.at(v) * kKvQB;
+        const int i1 = min(N - 1, i0 + kKvQB - 1);
+        // block flags first: their branches then sit before the products,
+        // not between the exponentials and the products they interleave with
         const bool act = block_act(v);
-        if (act) {
-          const int s = v % kKvStages;
-          const bf16* qs = smem + s * 2 * kTile;
-          const int i0 = walk.at(v) * kKvQB;
-          const int i1 = min(N - 1, i0 + kKvQB - 1);
-          bf16x8 aa[kKK];
-          load_ka<D>(aa, qs, off, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          const f32x16 sc_ = mfma_ksum<kKK, 1>(aa, bop);
-          __builtin_amdgcn_sched_barrier(0);
-          float nl[16], pv[16];
-          rows16(&rowv[s][wave][0], nl);
-          if (act_prev) {
-            bf16x8 bb[2 * kDT];
-            dv_operands(v - 1, bb);
-            // fixed order: one dV product of visit v - 1, then its share of
-            // the exponentials of visit v
-#pragma unroll
-            for (int m = 0; m < 2 * kDT; ++m) {
-              const int dt = m % kDT;
-              acc[dt] = mfma32(m < kDT ? pp0 : pp1, bb[2 * dt + (m < kDT ? 0 : 1)], acc[dt]);
-#pragma unroll
-              for (int i = m * 16 / (2 * kDT); i < (m + 1) * 16 / (2 * kDT); ++i)
-                pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
-          }
-          bool full_set;
-          if constexpr (TWO)
-            full_set = set_full(i0, i1, kw0, kw1, dset);
-          else
-            full_set = tile_full(i0, i1, kw0, kw1, lo, hi);
-          const bool full = wave_keys_full && i0 + kKvQB - 1 <= N - 1 && full_set;
-          if (!full) {
-            // band applied by selection (P may overflow out of band)
-            const int mb = kj + lo - i0;  // query row r is in band iff 0 <= r - mb <= hi - lo
-            const uint32_t width = (uint32_t)(hi - lo);
-            const int mb2 = kj + dset.nlo - i0;
-            const uint32_t width2 = (uint32_t)(dset.nhi - dset.nlo);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = perm_reg_row(i, g);
-              bool in = (uint32_t)(r - mb) <= width;
-              if constexpr (TWO) in = in || (uint32_t)(r - mb2) <= width2;
-              const bool ok = key_ok && i0 + r < N && in;
-              pv[i] = ok ? pv[i] : 0.f;
-            }
-          }
-          f16x8* dst = (f16x8*)&pbuf[v & 1][kw][lane][0];
-          dst[0] = pack8_f16(&pv[0]);
-          dst[1] = pack8_f16(&pv[8]);
-          pp0 = pack8(&pv[0]);
-          pp1 = pack8(&pv[8]);
-        } else if (act_prev) {
+        bool full_set;
+        if constexpr (TWO)
+          full_set = set_full(i0, i1, kw0, kw1, dset);
+        else
+          full_set = tile_full(i0, i1, kw0, kw1, lo, hi);
+        const bool full = act && wave_keys_full && i0 + kKvQB - 1 <= N - 1 && full_set;
+        bf16x8 aa[kKK];
+        load_ka<D>(aa, qs, off, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x16 sc_ = mfma_ksum<kKK, 1>(aa, bop);
+        __builtin_amdgcn_sched_barrier(0);
+        float nl[16], pv[16];
+        rows16(&rowv[s][wave][0], nl);
+        if constexpr (decltype(has_prev)::value) {
           bf16x8 bb[2 * kDT];
           dv_operands(v - 1, bb);
-          __builtin_amdgcn_sched_barrier(0);
-          dv_update(bb, pp0, pp1);
+          // fixed order: one dV product of block v - 1, then its share of
+          // the exponentials of block v
+#pragma unroll
+          for (int m = 0; m < 2 * kDT; ++m) {
+            const int dt = m % kDT;
+            acc[dt] = mfma32(m < kDT ? pp0 : pp1, bb[2 * dt + (m < kDT ? 0 : 1)], acc[dt]);
+#pragma unroll
+            for (int i = m * 16 / (2 * kDT); i < (m + 1) * 16 / (2 * kDT); ++i)
+              pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
         }
-        act_prev = act;
-      }
+        if (!full) {
+          // Element mask: query row r = creg(i) + 8 g of the block is kept iff
+          // it is below N and its distance to key kj lies in a range of the
+          // set, i.e. 0 <= r - (kj + lo - i0) <= hi - lo (and likewise for
+          // the second range); nothing is kept on a lane whose key is past N
+          // or in a block that misses the wave's keys.  Moving 8 g to the
+          // per-lane bounds leaves one compare per range and element.
+          const bool keep = act && key_ok;
+          const int rlim = N - i0 - 8 * g;  // creg(i) < rlim  <=>  row below N
+          const int mb = kj + lo - i0 - 8 * g;
+          const uint32_t width = (uint32_t)(hi - lo);
+          int mb2 = kNoDistance;  // no second range: the test below never passes
+          uint32_t width2 = 0;
+          if constexpr (TWO) {
+            if (has_second(dset)) {
+              mb2 = kj + dset.nlo - i0 - 8 * g;
+              width2 = (uint32_t)(dset.nhi - dset.nlo);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            bool in = (uint32_t)(creg(i) - mb) <= width;
+            if constexpr (TWO) in = in | ((uint32_t)(creg(i) - mb2) <= width2);
+            in = in & keep & (creg(i) < rlim);
+            pv[i] = in ? pv[i] : 0.f;
+          }
+        }
+        f16x8* dst = (f16x8*)&pbuf[v & 1][kw][lane][0];
+        dst[0] = pack8_f16(&pv[0]);
+        dst[1] = pack8_f16(&pv[8]);
+        pp0 = pack8(&pv[0]);
+        pp1 = pack8(&pv[8]);
+      };
+      p_block(0, Flag<false>{});
+      for (int v = 1; v < n_visit; ++v) p_block(v, Flag<true>{});
       __syncthreads();  // matches the dS waves' final barrier
-      if (act_prev) {
+      {
         bf16x8 bb[2 * kDT];
         dv_operands(n_visit - 1, bb);
         __builtin_amdgcn_sched_barrier(0);
-        dv_update(bb, pp0, pp1);
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(pp0, bb[2 * dt], acc[dt]);
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(pp1, bb[2 * dt + 1], acc[dt]);
       }
     } else {
-      f32x16 dp_prev;  // dP of the previous block
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dp_prev[i] = 0.f;
-      bool act_prev = false;
-      for (int v = 0; v < n_visit; ++v) {
+      // dP of block v into dp_new, then dS and dK of block v - 1 from dp_old;
+      // the two dP registers alternate (loop unrolled by two), so nothing is
+      // copied between blocks.
+      auto d_block = [&](int v, f32x16& dp_new, const f32x16& dp_old, auto has_prev) {
         block_start(v);
-        const bool act = block_act(v);
-        f32x16 dp_cur;
+        const bf16* dos = smem + (v % kKvStages) * 2 * kTile + kTile;
+        bf16x8 aa[kKK];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dp_cur[i] = 0.f;
-        if (act) {
-          const bf16* dos = smem + (v % kKvStages) * 2 * kTile + kTile;
-          bf16x8 aa[kKK];
-#pragma unroll
-          for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(dos, prow, 16 * kk + 8 * g);
-          __builtin_amdgcn_sched_barrier(0);
-          dp_cur = mfma_ksum<kKK, 1>(aa, bop);
-        }
-        if (act_prev) ds_dk(v - 1, dp_prev);
-        dp_prev = dp_cur;
-        act_prev = act;
+        for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(dos, prow, 16 * kk + 8 * g);
+        __builtin_amdgcn_sched_barrier(0);
+        dp_new = mfma_ksum<kKK, 1>(aa, bop);
+        if constexpr (decltype(has_prev)::value) ds_dk(v - 1, dp_old);
+      };
+      f32x16 dpa, dpb;
+      d_block(0, dpa, dpb, Flag<false>{});
+      int v = 1;
+      for (; v + 1 < n_visit; v += 2) {
+        d_block(v, dpb, dpa, Flag<true>{});
+        d_block(v + 1, dpa, dpb, Flag<true>{});
       }
-      __syncthreads();  // P of the last block visible
-      if (act_prev) ds_dk(n_visit - 1, dp_prev);
+      if (v < n_visit) {
+        d_block(v, dpb, dpa, Flag<true>{});
+        __syncthreads();  // P of the last block visible
+        ds_dk(v, dpb);
+      } else {
+        __syncthreads();  // P of the last block visible
+        ds_dk(v - 1, dpa);
+      }
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= scl;  // dK = scale dS^T Q
     }
   }
 

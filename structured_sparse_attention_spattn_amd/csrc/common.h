@@ -246,6 +246,12 @@ struct AsyncTile {
   }
 };
 
+// Compile-time flag passed to generic lambdas (one body, two instantiations).
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 // Make the compiler complete the load that produced x here (it inserts the
 // vector-memory wait before this empty statement), so no such wait is left
 // inside a loop that also has direct LDS loads in flight.
