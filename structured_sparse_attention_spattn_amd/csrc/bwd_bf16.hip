@@ -93,7 +93,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   if constexpr (TWO)
     if (has_second(dset)) span2 = band_key_span(i_tile0, i_tile1, dset.nlo, dset.nhi);
   // key tiles to visit, in order; the ring holds visit v in stage v % kDqStages
-  const TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kDqBK);
+  TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kDqBK);
+  align_walk(walk, i_tile0 - hi, i_tile0 + kDqBQ - 1 - lo, kDqBK);
   const int n_visit = walk.n;
   auto issue = [&](int v) {
     bf16* st = smem + (v % kDqStages) * 2 * kTile;
@@ -107,30 +108,49 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   for (int i = 0; i < kDqStages - 1; ++i)
     if (i < n_visit) issue(i);
 
-  // Q and dO operands; D_i = dO_i . O_i from the same lanes.
+  // Q and dO operands; D_i = dO_i . O_i from the same lanes.  All row
+  // chunks are requested before the first is used, so the prologue costs one
+  // memory round trip, not one per chunk.  A tile none of whose rows has a
+  // key loads nothing: its D (never used with a nonzero P) and dQ are 0.
   bf16x8 qreg[kKK], doreg[kKK];
-  float dpart = 0.f;
+  float dval = 0.f, nlse2 = 0.f;  // nlse2: P = exp2(s * sl2 + nlse2), nlse2 = -LSE log2(e)
+  if (n_visit > 0) {
+    const int ir = min(iq, N - 1);  // rows past N read the last row, then count as zero
+    const size_t roff = base + (size_t)ir * D + 8 * g;
+    bf16x8 oreg[kKK];
 #pragma unroll
-  for (int kk = 0; kk < kKK; ++kk) {
-    const size_t off = base + (size_t)iq * D + 16 * kk + 8 * g;
-    if (row_ok) {
-      qreg[kk] = *(const bf16x8*)(p.q + off);
-      doreg[kk] = *(const bf16x8*)(p.dout + off);
-      const bf16x8 ov = *(const bf16x8*)(p.o + off);
+    for (int kk = 0; kk < kKK; ++kk) {
+      qreg[kk] = *(const bf16x8*)(p.q + roff + 16 * kk);
+      doreg[kk] = *(const bf16x8*)(p.dout + roff + 16 * kk);
+      oreg[kk] = *(const bf16x8*)(p.o + roff + 16 * kk);
+    }
+    const float lse_i = p.lse[(size_t)bh * N + ir];
+    float dpart = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dpart += (float)doreg[kk][e] * (float)ov[e];
-    } else {
+    for (int kk = 0; kk < kKK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart += (float)doreg[kk][e] * (float)oreg[kk][e];
+    dpart += __shfl_xor(dpart, 32);  // lanes l and l ^ 32 hold the two halves of one row
+    dval = row_ok ? dpart : 0.f;
+    nlse2 = row_ok ? -lse_i * kLog2e : 0.f;
+    if (!row_ok) {
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) {
+        qreg[kk] = bf16x8{};
+        doreg[kk] = bf16x8{};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
       qreg[kk] = bf16x8{};
       doreg[kk] = bf16x8{};
     }
   }
-  const float dval = dpart + __shfl_xor(dpart, 32);
   if (row_ok && g == 0) p.dvec[(size_t)bh * N + iq] = dval;
   const float sl2 = p.scale_log2;
   const float scl = p.scale;
   const float ndsc = -dval * scl;
-  // exponent offset: P = exp2(s * sl2 - lse2), lse2 = LSE * log2(e)
-  const float nlse2 = row_ok ? -p.lse[(size_t)bh * N + iq] * kLog2e : 0.f;
 #pragma unroll
   for (int kk = 0; kk < kKK; ++kk) {
     settle(qreg[kk]);
@@ -509,8 +529,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         pp0 = pack8(&pv[0]);
         pp1 = pack8(&pv[8]);
       };
-      p_block(0, Flag<false>{});
-      for (int v = 1; v < n_visit; ++v) p_block(v, Flag<true>{});
+      p_block(0, std::false_type{});
+      for (int v = 1; v < n_visit; ++v) p_block(v, std::true_type{});
       __syncthreads();  // matches the dS waves' final barrier
       {
         bf16x8 bb[2 * kDT];
@@ -536,14 +556,14 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         if constexpr (decltype(has_prev)::value) ds_dk(v - 1, dp_old);
       };
       f32x16 dpa, dpb;
-      d_block(0, dpa, dpb, Flag<false>{});
+      d_block(0, dpa, dpb, std::false_type{});
       int v = 1;
       for (; v + 1 < n_visit; v += 2) {
-        d_block(v, dpb, dpa, Flag<true>{});
-        d_block(v + 1, dpa, dpb, Flag<true>{});
+        d_block(v, dpb, dpa, std::true_type{});
+        d_block(v + 1, dpa, dpb, std::true_type{});
       }
       if (v < n_visit) {
-        d_block(v, dpb, dpa, Flag<true>{});
+        d_block(v, dpb, dpa, std::true_type{});
         __syncthreads();  // P of the last block visible
         ds_dk(v, dpb);
       } else {

@@ -246,12 +246,6 @@ struct AsyncTile {
   }
 };
 
-// Compile-time flag passed to generic lambdas (one body, two instantiations).
-template <bool B>
-struct Flag {
-  static constexpr bool value = B;
-};
-
 // Make the compiler complete the load that produced x here (it inserts the
 // vector-memory wait before this empty statement), so no such wait is left
 // inside a loop that also has direct LDS loads in flight.
@@ -501,11 +495,18 @@ __host__ __device__ __forceinline__ bool has_second(const DistSet& s) { return s
 // index v in [0, n) maps to tile at(v).
 struct TileWalk {
   int a0, na, b0, n;
-  __host__ __device__ __forceinline__ int at(int v) const { return v < na ? a0 + v : b0 + (v - na); }
+  int rot;  // a single run starts at tile a0 + rot and wraps around (align_walk)
+  __host__ __device__ __forceinline__ int at(int v) const {
+    if (v < na) {
+      const int t = v + rot;
+      return a0 + (t < na ? t : t - na);
+    }
+    return b0 + (v - na);
+  }
 };
 __host__ __device__ __forceinline__ TileWalk tile_walk(KeySpan s1, KeySpan s2, int tile) {
   const bool e1 = s1.last < s1.first, e2 = s2.last < s2.first;
-  TileWalk w{0, 0, 0, 0};
+  TileWalk w{0, 0, 0, 0, 0};
   if (e1 && e2) return w;
   if (e1 || e2) {
     const KeySpan s = e1 ? s2 : s1;
@@ -529,6 +530,25 @@ __host__ __device__ __forceinline__ TileWalk tile_walk(KeySpan s1, KeySpan s2, i
   }
   return w;
 }
+__host__ __device__ __forceinline__ int floor_div(int x, int t) { return x >= 0 ? x / t : -((-x + t - 1) / t); }
+
+// Visit order shared by neighbouring workgroups.  Consecutive tiles of one
+// head need overlapping runs of the other operand (with the band's lag), and
+// an ascending walk makes each workgroup read a shared tile several steps
+// before or after its neighbour, long enough for the tile to leave L2 in
+// between.  Instead a single run starts at the tile whose index is 0 modulo
+// m, the length of an unclipped run (rows [r0, r1] before clipping to the
+// sequence), and wraps around: every workgroup with a full run then visits
+// tile x at step x mod m, so workgroups that share x read it at the same step.
+// The order of tiles does not change what is summed.
+__host__ __device__ __forceinline__ void align_walk(TileWalk& w, int r0, int r1, int tile) {
+  if (w.n < 2 || w.na != w.n) return;
+  const int m = floor_div(r1, tile) - floor_div(r0, tile) + 1;
+  if (m < 2) return;
+  const int k = (m - w.a0 % m) % m;
+  w.rot = k < w.n ? k : 0;
+}
+
 // Tile tests over the whole distance set (an empty second range never meets
 // and is never full).
 __host__ __device__ __forceinline__ bool set_meets(int i_min, int i_max, int j_min, int j_max, const DistSet& s) {

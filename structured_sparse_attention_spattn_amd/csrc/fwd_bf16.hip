@@ -260,7 +260,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   KeySpan span2{0, -1};
   if constexpr (TWO)
     if (has_second(dset)) span2 = band_key_span(i_tile0, i_tile1, dset.nlo, dset.nhi);
-  const TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kBK);
+  TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kBK);
+  align_walk(walk, i_tile0 - hi, i_tile0 + kBQ - 1 - lo, kBK);
   if (walk.n == 0) {
     // No row of this tile has a key: output 0, LSE -inf.
     constexpr int kCpr = D / 8;
