@@ -427,7 +427,24 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       else
         wait_vmcnt<0>();
       __syncthreads();
+    };
+    // The ring loads of visit v + kKvAhead are issued in the middle of a
+    // dependent MFMA chain (score or dP), whose stalls absorb their issue cost.
+    auto prefetch = [&](int v) {
       if (v + kKvAhead < n_visit) issue(v + kKvAhead);
+    };
+    // sum over kk of a[kk] x b[kk] as one dependent chain, with the prefetch
+    // of visit v after the first half of the products
+    auto chain_with_prefetch = [&](const bf16x8* a, int v) {
+      f32x16 c;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < kKK / 2; ++kk) c = mfma32(a[kk], bop[kk], c);
+      prefetch(v);
+#pragma unroll
+      for (int kk = kKK / 2; kk < kKK; ++kk) c = mfma32(a[kk], bop[kk], c);
+      return c;
     };
     auto block_act = [&](int v) {
       const int i0 = walk.at(v) * kKvQB;
@@ -474,7 +491,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         bf16x8 aa[kKK];
         load_ka<D>(aa, qs, off, 0);
         __builtin_amdgcn_sched_barrier(0);
-        const f32x16 sc_ = mfma_ksum<kKK, 1>(aa, bop);
+        const f32x16 sc_ = chain_with_prefetch(aa, v);
         __builtin_amdgcn_sched_barrier(0);
         float nl[16], pv[16];
         rows16(&rowv[s][wave][0], nl);
@@ -552,7 +569,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(dos, prow, 16 * kk + 8 * g);
         __builtin_amdgcn_sched_barrier(0);
-        dp_new = mfma_ksum<kKK, 1>(aa, bop);
+        dp_new = chain_with_prefetch(aa, v);
         if constexpr (decltype(has_prev)::value) ds_dk(v - 1, dp_old);
       };
       f32x16 dpa, dpb;
