@@ -246,6 +246,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
     }
   }
 
+  if (n_visit == 0) {  // no keys: zero rows, written directly
+    if (wave_live) store_zero_rows<D>(p.dq, (size_t)bh * N + iw0, min(32, N - iw0), p.grad_f32 != 0, lane);
+    return;
+  }
   __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
   if (wave_live) {
     float* stg = (float*)smem + wave * 32 * D;
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       }
     };
     // dS wave, visit v (one iteration late): dS = P (dP - D) and
-    // dK += dS^T Q (the scale is applied to dK once, after the walk).  P comes masked from the P wave (0 outside the band and
+    // dK^T += Q^T dS (the scale is applied to dK once, at the store).  P comes masked from the P wave (0 outside the band and
     // on rows past N), so no mask is needed here.
     auto ds_dk = [&](int v, const f32x16& dpv) {
       const int st = v % kKvStages;
@@ -411,9 +415,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       const bf16x8 op0 = pack8(&ds[0]), op1 = pack8(&ds[8]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op0, bb[2 * dt], acc[dt]);
+      for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(bb[2 * dt], op0, acc[dt]);
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(op1, bb[2 * dt + 1], acc[dt]);
+      for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(bb[2 * dt + 1], op1, acc[dt]);
     };
 
     // Top of every iteration, for both roles (same barrier sequence): wait for
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
           for (int m = 0; m < 2 * kDT; ++m) {
             const int dt = m % kDT;
-            acc[dt] = mfma32(m < kDT ? pp0 : pp1, bb[2 * dt + (m < kDT ? 0 : 1)], acc[dt]);
+            acc[dt] = mfma32(bb[2 * dt + (m < kDT ? 0 : 1)], m < kDT ? pp0 : pp1, acc[dt]);
 #pragma unroll
             for (int i = m * 16 / (2 * kDT); i < (m + 1) * 16 / (2 * kDT); ++i)
               pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
@@ -554,9 +558,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         dv_operands(n_visit - 1, bb);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(pp0, bb[2 * dt], acc[dt]);
+        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(bb[2 * dt], pp0, acc[dt]);
 #pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(pp1, bb[2 * dt + 1], acc[dt]);
+        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(bb[2 * dt + 1], pp1, acc[dt]);
       }
     } else {
       // dP of block v into dp_new, then dS and dK of block v - 1 from dp_old;
@@ -587,19 +591,23 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         __syncthreads();  // P of the last block visible
         ds_dk(v - 1, dpa);
       }
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] *= scl;  // dK = scale dS^T Q
     }
   }
 
-  // dV (P waves) or dK (dS waves) rows kw0 .. kw0 + 31
+  // dV (P waves) or dK = scale dS^T Q (dS waves), rows kw0 .. kw0 + 31; the
+  // accumulators hold the transposed products dV^T and (dK / scale)^T.  A
+  // tile without queries writes its zero rows directly.
+  void* const dst = pwave ? p.dv : p.dk;
+  const int nrows = min(32, N - kw0);
+  if (n_visit == 0) {
+    if (wave_live) store_zero_rows<D>(dst, (size_t)bh * N + kw0, nrows, p.grad_f32 != 0, lane);
+    return;
+  }
   __syncthreads();  // ring and P buffers no longer read: the ring becomes the output staging area
   if (wave_live) {
     float* stg = (float*)smem + wave * 32 * D;
-    stage_direct<D>(stg, acc, lane);
-    store_staged<D>(stg, pwave ? p.dv : p.dk, (size_t)bh * N + kw0, min(32, N - kw0), p.grad_f32 != 0, lane);
+    stage_transposed<D>(stg, acc, pwave ? 1.f : p.scale, lane);
+    store_staged<D>(stg, dst, (size_t)bh * N + kw0, nrows, p.grad_f32 != 0, lane);
   }
 }
 

@@ -416,6 +416,28 @@ __device__ __forceinline__ void store_staged(const float* st, void* dst, size_t 
   }
 }
 
+// Zero rows 0 .. nrows - 1 of dst + row0 * D, in the store pattern of
+// store_staged (no staging needed for a tile that received no products).
+template <int D>
+__device__ __forceinline__ void store_zero_rows(void* dst, size_t row0, int nrows, bool f32, int lane) {
+  constexpr int kLpr = D / 8;
+  constexpr int kRpp = 64 / kLpr;
+#pragma unroll
+  for (int pass = 0; pass < 32 / kRpp; ++pass) {
+    const int r = pass * kRpp + lane / kLpr;
+    const int c = 8 * (lane % kLpr);
+    if (r < nrows) {
+      const size_t idx = (row0 + r) * D + c;
+      if (f32) {
+        *(f32x4*)((float*)dst + idx) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)((float*)dst + idx + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        *(u32x4*)((bf16*)dst + idx) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ scheduler
 struct KeySpan {
   int first, last;  // inclusive; empty when last < first
