@@ -145,6 +145,41 @@ int spattn_bwd_local(const void* q, const void* k, const void* v, const void* o,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Packed variable-length batches.  n_seqs sequences of different lengths are
+ * stored back to back along the token axis: q, k, v, o, dout, dq, dk, dv are
+ * [H, total, d] and lse is [H, total] (the [B, H, N, d] layout with B = 1 and
+ * N = total).  Sequence s owns tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1,
+ * and positions restart at 0 in every sequence.  Attention never crosses a
+ * sequence boundary: token i of sequence s attends the keys j of s with
+ * i - j in its head's set, as in spattn_fwd_local.
+ *   cu_seqlens  device int32 [n_seqs + 1], non-decreasing, cu_seqlens[0] = 0,
+ *               cu_seqlens[n_seqs] = total; read by the kernels (not checked).
+ *   max_seqlen  an upper bound on every sequence's length.  It sizes the
+ *               grid, and tokens past it in a longer sequence are not computed.
+ *   band_lo, band_hi  host, H int32 each, validated against max_seqlen as in
+ *               spattn_fwd and clipped to each sequence's length; or both
+ *               NULL for each sequence's own Balanced Distance Partitioning
+ *               table ("Making Every Head Count", Figure 1 caption: the bands
+ *               partition the distances of that sequence).
+ *   local_window  >= 0 as in spattn_fwd_local.
+ * The backward workspace is spattn_bwd_workspace_bytes(1, H, total, d, dtype,
+ * grad_dtype) bytes.  Both dtypes; d in {64, 128}.
+ * Errors: SPATTN_E_ARG for NULL pointers, n_seqs, max_seqlen or total < 1, or
+ * local_window < 0, and otherwise as spattn_fwd / spattn_bwd.
+ */
+int spattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                      int32_t total, int32_t H, int32_t d, int32_t dtype,
+                      const int32_t* band_lo, const int32_t* band_hi,
+                      int32_t local_window, float scale, void* stream);
+int spattn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                      int32_t total, int32_t H, int32_t d, int32_t dtype, int32_t grad_dtype,
+                      const int32_t* band_lo, const int32_t* band_hi, int32_t local_window,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode step: one new query per sequence against a key/value cache.  For
  * sequence b with L_b valid cache rows the query sits at position
  * i = L_b - 1 and head h attends

@@ -31,7 +31,8 @@ Readings where the pages are silent (each listed in the design notes):
 
 Modules: ``band`` (band table), ``attention`` (forward/backward, three
 independent forms; optional shared local window), ``tiles`` (canonical
-band-tile lists), ``decode`` (single-query attention over a key/value cache).
+band-tile lists), ``decode`` (single-query attention over a key/value cache),
+``varlen`` (packed batches of sequences of different lengths).
 """
 from .band import band_table, band_pairs, band_table_sliding_window, band_table_gapped_half
 from .attention import (
@@ -46,10 +47,12 @@ from .attention import (
 )
 from .tiles import query_tile_list, key_tile_list
 from .decode import decode_key_set, decode_attention
+from .varlen import seq_bands, varlen_fwd, varlen_bwd
 
 __all__ = [
     "band_table", "band_pairs", "band_table_sliding_window", "band_table_gapped_half",
     "masked_attention_literal", "masked_attention_dense", "masked_attention_dense_bwd",
     "band_mask", "band_attention_fwd", "band_attention_bwd", "band_attention_fwd_rows", "band_attention_bwd_rows",
     "query_tile_list", "key_tile_list", "decode_key_set", "decode_attention",
+    "seq_bands", "varlen_fwd", "varlen_bwd",
 ]

@@ -16,6 +16,7 @@ MAX_HEADS = 256
 EXPORTS = (
     "spattn_band_table", "spattn_fwd", "spattn_bwd_workspace_bytes", "spattn_bwd",
     "spattn_bwd_dq", "spattn_bwd_dkdv", "spattn_fwd_local", "spattn_bwd_local", "spattn_decode",
+    "spattn_fwd_varlen", "spattn_bwd_varlen",
     "spattn_kernel_tiles", "spattn_tile_list", "spattn_status_string",
 )
 
@@ -61,6 +62,12 @@ def load():
     lib.spattn_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32, _i32,
                                   ctypes.c_float, _p]
     lib.spattn_decode.restype = ctypes.c_int
+    lib.spattn_fwd_varlen.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32,
+                                      _i32, ctypes.c_float, _p]
+    lib.spattn_fwd_varlen.restype = ctypes.c_int
+    lib.spattn_bwd_varlen.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _pi32, _pi32, _i32, ctypes.c_float, _p, ctypes.c_size_t, _p]
+    lib.spattn_bwd_varlen.restype = ctypes.c_int
     lib.spattn_bwd_dq.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _pi32, _pi32, ctypes.c_float, _p, ctypes.c_size_t, _p]
     lib.spattn_bwd_dq.restype = ctypes.c_int

@@ -59,9 +59,12 @@ struct BwdF32Args {
   float* dq;
   float* dk;
   float* dv;
-  int B, H, N;
+  int B, H, N;  // sequences (B), heads, tokens per sequence (the longest, when packed)
   int local_window;  // shared local window width (0: exclusive bands)
   float scale;
+  const int32_t* cu;  // packed sequence offsets [B + 1] (device), or null
+  int T;              // packed: tokens per head
+  int own_bdp;        // packed: each sequence's own BDP bands
   Bands bands;
 };
 
@@ -76,8 +79,10 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dq_kernel(BwdF32Args p) {
   const int i = (int)(row % p.N);
   const long long bh = row / p.N;
   const int h = (int)(bh % p.H);
-  const DistSet ds_ = dist_set(p.bands.lo[h], p.bands.hi[h], p.local_window);
-  const size_t base = (size_t)bh * p.N * D;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, (int)(bh / p.H), h);
+  if (i >= sh.n) return;  // past the end of a packed sequence
+  const DistSet ds_ = dist_set(sh.lo, sh.hi, p.local_window);
+  const size_t base = sh.row0 * D;
   float qi[kE], di[kE], acc[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dq_kernel(BwdF32Args p) {
     di[e] = p.dout[base + (size_t)i * D + lane + 64 * e];
     acc[e] = 0.f;
   }
-  const float lse = p.lse[row], dd = p.dvec[row];
+  const float lse = p.lse[sh.row0 + i], dd = p.dvec[sh.row0 + i];
   // keys of row i: the primary range, then the disjoint second range if any
   KeySpan spans[2] = {band_key_span(i, i, ds_.lo, ds_.hi), KeySpan{0, -1}};
   if (has_second(ds_)) spans[1] = band_key_span(i, i, ds_.nlo, ds_.nhi);
@@ -119,9 +124,12 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dkdv_kernel(BwdF32Args p) {
   const int j = (int)(row % p.N);
   const long long bh = row / p.N;
   const int h = (int)(bh % p.H);
-  const DistSet ds_ = dist_set(p.bands.lo[h], p.bands.hi[h], p.local_window);
-  const size_t base = (size_t)bh * p.N * D;
-  const size_t lbase = (size_t)bh * p.N;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, (int)(bh / p.H), h);
+  if (j >= sh.n) return;  // past the end of a packed sequence
+  const DistSet ds_ = dist_set(sh.lo, sh.hi, p.local_window);
+  const int N = sh.n;
+  const size_t base = sh.row0 * D;
+  const size_t lbase = sh.row0;
   float kj[kE], vj[kE], dk[kE], dv[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
@@ -131,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dkdv_kernel(BwdF32Args p) {
     dv[e] = 0.f;
   }
   // queries reaching key j: the primary range, then the disjoint second range if any
-  KeySpan spans[2] = {band_query_span(j, j, ds_.lo, ds_.hi, p.N), KeySpan{0, -1}};
-  if (has_second(ds_)) spans[1] = band_query_span(j, j, ds_.nlo, ds_.nhi, p.N);
+  KeySpan spans[2] = {band_query_span(j, j, ds_.lo, ds_.hi, N), KeySpan{0, -1}};
+  if (has_second(ds_)) spans[1] = band_query_span(j, j, ds_.nlo, ds_.nhi, N);
   for (int sp = 0; sp < 2; ++sp)
   for (int i = spans[sp].first; i <= spans[sp].last; ++i) {
     float qi[kE], di[kE];
@@ -170,14 +178,14 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype
 
 int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                        void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
-                       float scale, float* dvec, hipStream_t stream);
+                       float scale, float* dvec, const Packed& pk, hipStream_t stream);
 int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                          void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
-                         float scale, float* dvec, hipStream_t stream);
+                         float scale, float* dvec, const Packed& pk, hipStream_t stream);
 
 static BwdF32Args f32_args(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
                            void* dk, void* dv, int B, int H, int N, const Bands& bands, int local_window,
-                           float scale, float* dvec) {
+                           float scale, float* dvec, const Packed& pk) {
   BwdF32Args a;
   a.q = (const float*)q;
   a.k = (const float*)k;
@@ -193,6 +201,9 @@ static BwdF32Args f32_args(const void* q, const void* k, const void* v, const fl
   a.N = N;
   a.local_window = local_window;
   a.scale = scale;
+  a.cu = pk.cu;
+  a.T = pk.T;
+  a.own_bdp = pk.own_bdp;
   a.bands = bands;
   return a;
 }
@@ -200,24 +211,25 @@ static BwdF32Args f32_args(const void* q, const void* k, const void* v, const fl
 // Stage 1: D_i = dO_i . O_i into the workspace, and dQ.
 int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                   void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
-                  int local_window, float scale, void* workspace, hipStream_t stream) {
+                  int local_window, float scale, const Packed& pk, void* workspace, hipStream_t stream) {
   float* dvec = (float*)workspace;
   if (dtype == SPATTN_BF16)
     return launch_bwd_dq_bf16(q, k, v, o, lse, dout, dq, B, H, N, d, grad_dtype == SPATTN_F32, bands, local_window,
-                              scale, dvec, stream);
-  const long long rows = (long long)B * H * N;
+                              scale, dvec, pk, stream);
+  const long long rows = (long long)B * H * N;  // one wave per (sequence, head, row); packed: padded to N
   {
-    const long long threads = rows * (d / 8);
+    const long long data_rows = pk.cu != nullptr ? (long long)H * pk.T : rows;  // rows held in the tensors
+    const long long threads = data_rows * (d / 8);
     dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
     if (d == 128)
       hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, block, 0, stream, (const float*)o, (const float*)dout,
-                         dvec, rows);
+                         dvec, data_rows);
     else
       hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, block, 0, stream, (const float*)o, (const float*)dout,
-                         dvec, rows);
+                         dvec, data_rows);
     if (hipGetLastError() != hipSuccess) return SPATTN_E_HIP;
   }
-  BwdF32Args a = f32_args(q, k, v, lse, dout, dq, nullptr, nullptr, B, H, N, bands, local_window, scale, dvec);
+  BwdF32Args a = f32_args(q, k, v, lse, dout, dq, nullptr, nullptr, B, H, N, bands, local_window, scale, dvec, pk);
   dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);
   if (d == 128)
     hipLaunchKernelGGL(bwd_f32_dq_kernel<128>, grid, block, 0, stream, a);
@@ -229,13 +241,13 @@ int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, co
 // Stage 2: dK and dV, reading D from the workspace written by stage 1.
 int launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                     void* dv, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
-                    int local_window, float scale, void* workspace, hipStream_t stream) {
+                    int local_window, float scale, const Packed& pk, void* workspace, hipStream_t stream) {
   float* dvec = (float*)workspace;
   if (dtype == SPATTN_BF16)
     return launch_bwd_dkdv_bf16(q, k, v, lse, dout, dk, dv, B, H, N, d, grad_dtype == SPATTN_F32, bands,
-                                local_window, scale, dvec, stream);
-  const long long rows = (long long)B * H * N;
-  BwdF32Args a = f32_args(q, k, v, lse, dout, nullptr, dk, dv, B, H, N, bands, local_window, scale, dvec);
+                                local_window, scale, dvec, pk, stream);
+  const long long rows = (long long)B * H * N;  // one wave per (sequence, head, row); packed: padded to N
+  BwdF32Args a = f32_args(q, k, v, lse, dout, nullptr, dk, dv, B, H, N, bands, local_window, scale, dvec, pk);
   dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);
   if (d == 128)
     hipLaunchKernelGGL(bwd_f32_dkdv_kernel<128>, grid, block, 0, stream, a);

@@ -41,6 +41,9 @@ struct BwdArgs {
   int grad_f32;
   int B, H, N;
   int n_tiles;  // query tiles (bwd_dq) or key tiles (bwd_dkdv) per (b, h)
+  const int32_t* cu;  // packed sequence offsets [B + 1] (device), or null
+  int T;              // packed: tokens per head
+  int own_bdp;        // packed: each sequence's own BDP bands
   int local_window;  // shared local window width (0: exclusive bands)
   float scale;
   float scale_log2;
@@ -72,12 +75,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const int t = item % p.n_tiles;
   const int bh = item / p.n_tiles;
   const int h = bh % p.H;
-  const int N = p.N;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, bh / p.H, h);
+  const int N = sh.n;
+  if (t * kDqBQ >= N) return;  // past the end of a packed sequence
   // the head's distance set: its band, joined with the local window if any
-  const DistSet dset = dist_set(p.bands.lo[h], p.bands.hi[h], TWO ? p.local_window : 0);
+  const DistSet dset = dist_set(sh.lo, sh.hi, TWO ? p.local_window : 0);
   const int lo = dset.lo;
   const int hi = dset.hi;
-  const size_t base = (size_t)bh * N * D;
+  const size_t base = sh.row0 * D;
   const bf16* __restrict__ kb = p.k + base;
   const bf16* __restrict__ vb = p.v + base;
 
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
       doreg[kk] = *(const bf16x8*)(p.dout + roff + 16 * kk);
       oreg[kk] = *(const bf16x8*)(p.o + roff + 16 * kk);
     }
-    const float lse_i = p.lse[(size_t)bh * N + ir];
+    const float lse_i = p.lse[sh.row0 + ir];
     float dpart = 0.f;
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk)
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
       doreg[kk] = bf16x8{};
     }
   }
-  if (row_ok && g == 0) p.dvec[(size_t)bh * N + iq] = dval;
+  if (row_ok && g == 0) p.dvec[sh.row0 + iq] = dval;
   const float sl2 = p.scale_log2;
   const float scl = p.scale;
   const float ndsc = -dval * scl;
@@ -247,14 +252,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   }
 
   if (n_visit == 0) {  // no keys: zero rows, written directly
-    if (wave_live) store_zero_rows<D>(p.dq, (size_t)bh * N + iw0, min(32, N - iw0), p.grad_f32 != 0, lane);
+    if (wave_live) store_zero_rows<D>(p.dq, sh.row0 + iw0, min(32, N - iw0), p.grad_f32 != 0, lane);
     return;
   }
   __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
   if (wave_live) {
     float* stg = (float*)smem + wave * 32 * D;
     stage_transposed<D>(stg, acc, 1.f, lane);
-    store_staged<D>(stg, p.dq, (size_t)bh * N + iw0, min(32, N - iw0), p.grad_f32 != 0, lane);
+    store_staged<D>(stg, p.dq, sh.row0 + iw0, min(32, N - iw0), p.grad_f32 != 0, lane);
   }
 }
 
@@ -319,16 +324,18 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   const int ut = item % p.n_tiles;
   const int bh = item / p.n_tiles;
   const int h = bh % p.H;
-  const int N = p.N;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, bh / p.H, h);
+  const int N = sh.n;
+  if (ut * kKvBK >= N) return;  // past the end of a packed sequence
   // the head's distance set: its band, joined with the local window if any
-  const DistSet dset = dist_set(p.bands.lo[h], p.bands.hi[h], TWO ? p.local_window : 0);
+  const DistSet dset = dist_set(sh.lo, sh.hi, TWO ? p.local_window : 0);
   const int lo = dset.lo;
   const int hi = dset.hi;
-  const size_t base = (size_t)bh * N * D;
+  const size_t base = sh.row0 * D;
   const bf16* __restrict__ qb = p.q + base;
   const bf16* __restrict__ dob = p.dout + base;
-  const float* __restrict__ lseb = p.lse + (size_t)bh * N;
-  const float* __restrict__ ddb = p.dvec + (size_t)bh * N;
+  const float* __restrict__ lseb = p.lse + sh.row0;
+  const float* __restrict__ ddb = p.dvec + sh.row0;
 
   const int j0 = ut * kKvBK;
   const int j1 = min(N - 1, j0 + kKvBK - 1);
@@ -600,14 +607,14 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   void* const dst = pwave ? p.dv : p.dk;
   const int nrows = min(32, N - kw0);
   if (n_visit == 0) {
-    if (wave_live) store_zero_rows<D>(dst, (size_t)bh * N + kw0, nrows, p.grad_f32 != 0, lane);
+    if (wave_live) store_zero_rows<D>(dst, sh.row0 + kw0, nrows, p.grad_f32 != 0, lane);
     return;
   }
   __syncthreads();  // ring and P buffers no longer read: the ring becomes the output staging area
   if (wave_live) {
     float* stg = (float*)smem + wave * 32 * D;
     stage_transposed<D>(stg, acc, pwave ? 1.f : p.scale, lane);
-    store_staged<D>(stg, dst, (size_t)bh * N + kw0, nrows, p.grad_f32 != 0, lane);
+    store_staged<D>(stg, dst, sh.row0 + kw0, nrows, p.grad_f32 != 0, lane);
   }
 }
 
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 
 static BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, bool grad_f32,
-                         const Bands& bands, float scale, float* dvec) {
+                         const Bands& bands, float scale, float* dvec, const Packed& pk) {
   BwdArgs a;
   a.q = (const bf16*)q;
   a.k = (const bf16*)k;
@@ -632,6 +639,9 @@ static BwdArgs make_args(const void* q, const void* k, const void* v, const void
   a.H = H;
   a.N = N;
   a.n_tiles = 0;
+  a.cu = pk.cu;
+  a.T = pk.T;
+  a.own_bdp = pk.own_bdp;
   a.local_window = 0;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
@@ -641,8 +651,8 @@ static BwdArgs make_args(const void* q, const void* k, const void* v, const void
 
 int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                        void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
-                       float scale, float* dvec, hipStream_t stream) {
-  BwdArgs a = make_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, grad_f32, bands, scale, dvec);
+                       float scale, float* dvec, const Packed& pk, hipStream_t stream) {
+  BwdArgs a = make_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, grad_f32, bands, scale, dvec, pk);
   a.n_tiles = (N + kDqBQ - 1) / kDqBQ;
   a.local_window = local_window;
   const long long total = (long long)B * H * a.n_tiles;
@@ -662,8 +672,8 @@ int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* 
 
 int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                          void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
-                         float scale, float* dvec, hipStream_t stream) {
-  BwdArgs a = make_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, grad_f32, bands, scale, dvec);
+                         float scale, float* dvec, const Packed& pk, hipStream_t stream) {
+  BwdArgs a = make_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, grad_f32, bands, scale, dvec, pk);
   a.n_tiles = (N + kKvBK - 1) / kKvBK;
   a.local_window = local_window;
   const long long total = (long long)B * H * a.n_tiles;

@@ -34,6 +34,51 @@ struct Bands {
   int32_t hi[SPATTN_MAX_HEADS];
 };
 
+// ------------------------------------------------------------ sequences
+// The rows one (sequence, head) owns.  Fixed length (cu == nullptr): B
+// sequences of N tokens in a [B, H, N, d] tensor, head h of sequence b at rows
+// (b H + h) N + i.  Packed variable length: sequence s holds tokens cu[s] ..
+// cu[s+1] - 1 of a [H, T, d] tensor (T tokens in all), head h of it at rows
+// h T + cu[s] + i; N is then the longest sequence and only sizes the grid.
+// The band is the caller's table (clipped to a packed sequence's length) or,
+// for packed sequences without one (own_bdp), the Balanced Distance
+// Partitioning table of the sequence's own length ("Making Every Head Count",
+// Figure 1 caption: widths floor(n/H) or ceil(n/H), the wider ones first).
+// Host side: the packed layout of a launch (cu == nullptr: fixed length).
+struct Packed {
+  const int32_t* cu;
+  int T;
+  int own_bdp;
+};
+struct SeqHead {
+  size_t row0;  // row of token 0
+  int n;        // tokens in the sequence
+  int lo, hi;   // the head's band
+};
+__device__ __forceinline__ SeqHead seq_head(const int32_t* cu, int T, int own_bdp, int H, int N, const Bands& b,
+                                            int s, int h) {
+  SeqHead r;
+  if (cu == nullptr) {
+    r.row0 = ((size_t)s * H + h) * N;
+    r.n = N;
+    r.lo = b.lo[h];
+    r.hi = b.hi[h];
+    return r;
+  }
+  const int o = cu[s];
+  r.n = cu[s + 1] - o;
+  r.row0 = (size_t)h * T + o;
+  if (own_bdp) {
+    const int base = r.n / H, extra = r.n % H;
+    r.lo = h * base + (h < extra ? h : extra);
+    r.hi = r.lo + base + (h < extra ? 1 : 0) - 1;
+  } else {
+    r.lo = b.lo[h] < r.n ? b.lo[h] : r.n;
+    r.hi = b.hi[h] < r.n - 1 ? b.hi[h] : r.n - 1;
+  }
+  return r;
+}
+
 // ----------------------------------------------------------------- MFMA
 // 32x32x16 bf16 -> f32.  Operand layout (lane l, group g = l / 32):
 //   A: row l % 32, k-slots 8g .. 8g+7;   B: column l % 32, k-slots 8g .. 8g+7

@@ -42,8 +42,11 @@ struct FwdArgs {
   const bf16* v;
   bf16* o;
   float* lse;
-  int B, H, N;
+  int B, H, N;  // sequences (B), heads, tokens per sequence (the longest, when packed)
   int n_qt;
+  const int32_t* cu;  // packed sequence offsets [B + 1] (device), or null
+  int T;              // packed: tokens per head
+  int own_bdp;        // packed: each sequence's own BDP bands
   int local_window;  // shared local window width (0: exclusive bands)
   float scale_log2;
   Bands bands;
@@ -242,17 +245,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   const int t = item % p.n_qt;
   const int bh = item / p.n_qt;
   const int h = bh % p.H;
-  const int N = p.N;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, bh / p.H, h);
+  const int N = sh.n;
+  if (t * kBQ >= N) return;  // past the end of a packed sequence
   // the head's distance set: its band, joined with the local window if any
-  const DistSet dset = dist_set(p.bands.lo[h], p.bands.hi[h], TWO ? p.local_window : 0);
+  const DistSet dset = dist_set(sh.lo, sh.hi, TWO ? p.local_window : 0);
   const int lo = dset.lo;
   const int hi = dset.hi;
-  const size_t base = (size_t)bh * N * D;
+  const size_t base = sh.row0 * D;
   const bf16* __restrict__ qb = p.q + base;
   const bf16* __restrict__ kb = p.k + base;
   const bf16* __restrict__ vb = p.v + base;
   bf16* __restrict__ ob = p.o + base;
-  float* __restrict__ lb = p.lse + (size_t)bh * N;
+  float* __restrict__ lb = p.lse + sh.row0;
   const float ninf = -__builtin_inff();
 
   const int i_tile0 = t * kBQ;
@@ -349,14 +354,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   if (wave_live) {
     float* stg = (float*)smem + wave * 32 * D;
     stage_transposed<D>(stg, st.acc, inv, lane);
-    store_staged<D>(stg, p.o, (size_t)bh * N + iw0, min(32, N - iw0), false, lane);
+    store_staged<D>(stg, p.o, sh.row0 + iw0, min(32, N - iw0), false, lane);
   }
 }
 
 }  // namespace
 
 int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                    int N, int d, const Bands& bands, int local_window, float scale, hipStream_t stream) {
+                    int N, int d, const Bands& bands, int local_window, float scale, const Packed& pk,
+                    hipStream_t stream) {
   FwdArgs a;
   a.q = (const bf16*)q;
   a.k = (const bf16*)k;
@@ -367,6 +373,9 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   a.H = H;
   a.N = N;
   a.n_qt = (N + kBQ - 1) / kBQ;
+  a.cu = pk.cu;
+  a.T = pk.T;
+  a.own_bdp = pk.own_bdp;
   a.local_window = local_window;
   a.scale_log2 = scale * kLog2e;
   a.bands = bands;

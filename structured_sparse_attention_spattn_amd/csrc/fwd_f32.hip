@@ -24,10 +24,13 @@ struct FwdF32Args {
   const float* v;
   float* o;
   float* lse;
-  int B, H, N;
+  int B, H, N;  // sequences (B), heads, tokens per sequence (the longest, when packed)
   int n_qt;
   int local_window;  // shared local window width (0: exclusive bands)
   float scale_log2;
+  const int32_t* cu;  // packed sequence offsets [B + 1] (device), or null
+  int T;              // packed: tokens per head
+  int own_bdp;        // packed: each sequence's own BDP bands
   Bands bands;
 };
 
@@ -58,17 +61,19 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
   const int t = item % p.n_qt;
   const int bh = item / p.n_qt;
   const int h = bh % p.H;
-  const int N = p.N;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, bh / p.H, h);
+  const int N = sh.n;
+  if (t * kBQ >= N) return;  // past the end of a packed sequence
   // the head's distance set: its band, joined with the local window if any
-  const DistSet dset = dist_set(p.bands.lo[h], p.bands.hi[h], p.local_window);
+  const DistSet dset = dist_set(sh.lo, sh.hi, p.local_window);
   const int lo = dset.lo;
   const int hi = dset.hi;
-  const size_t base = (size_t)bh * N * D;
+  const size_t base = sh.row0 * D;
   const float* __restrict__ qb = p.q + base;
   const float* __restrict__ kb = p.k + base;
   const float* __restrict__ vb = p.v + base;
   float* __restrict__ ob = p.o + base;
-  float* __restrict__ lb = p.lse + (size_t)bh * N;
+  float* __restrict__ lb = p.lse + sh.row0;
   const float ninf = -__builtin_inff();
 
   const int i_tile0 = t * kBQ;
@@ -205,7 +210,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
 }  // namespace
 
 int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                   int N, int d, const Bands& bands, int local_window, float scale, hipStream_t stream) {
+                   int N, int d, const Bands& bands, int local_window, float scale, const Packed& pk,
+                   hipStream_t stream) {
   FwdF32Args a;
   a.q = (const float*)q;
   a.k = (const float*)k;
@@ -216,6 +222,9 @@ int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
   a.H = H;
   a.N = N;
   a.n_qt = (N + kBQ - 1) / kBQ;
+  a.cu = pk.cu;
+  a.T = pk.T;
+  a.own_bdp = pk.own_bdp;
   a.local_window = local_window;
   a.scale_log2 = scale * kLog2e;
   a.bands = bands;

@@ -8,9 +8,9 @@
 
 namespace spattn {
 int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                    const Bands& bands, int local_window, float scale, hipStream_t stream);
+                    const Bands& bands, int local_window, float scale, const Packed& pk, hipStream_t stream);
 int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                   const Bands& bands, int local_window, float scale, hipStream_t stream);
+                   const Bands& bands, int local_window, float scale, const Packed& pk, hipStream_t stream);
 int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* lengths, int B,
                   int H, int Nmax, int d, int dtype, const Bands& bands, int local_window, float scale,
                   hipStream_t stream);
@@ -19,10 +19,12 @@ void fwd_f32_tiles(int* BQ, int* BK);
 size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype);
 int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                   void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
-                  int local_window, float scale, void* workspace, hipStream_t stream);
+                  int local_window, float scale, const Packed& pk, void* workspace, hipStream_t stream);
 int launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                     void* dv, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
-                    int local_window, float scale, void* workspace, hipStream_t stream);
+                    int local_window, float scale, const Packed& pk, void* workspace, hipStream_t stream);
+
+constexpr Packed kFixed{nullptr, 0, 0};  // fixed-length [B, H, N, d] layout
 
 namespace {
 
@@ -126,8 +128,9 @@ static int fwd_impl(const void* q, const void* k, const void* v, void* o, float*
   if (st != SPATTN_OK) return st;
   const float sc = resolve_scale(scale, d);
   const int w = local_window < N ? local_window : N;
-  if (dtype == SPATTN_BF16) return launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, bands, w, sc, (hipStream_t)stream);
-  return launch_fwd_f32(q, k, v, o, lse, B, H, N, d, bands, w, sc, (hipStream_t)stream);
+  if (dtype == SPATTN_BF16)
+    return launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, bands, w, sc, kFixed, (hipStream_t)stream);
+  return launch_fwd_f32(q, k, v, o, lse, B, H, N, d, bands, w, sc, kFixed, (hipStream_t)stream);
 }
 
 int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H, int32_t N,
@@ -170,7 +173,7 @@ int spattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, co
   if (st != SPATTN_OK) return st;
   if (!q || !k || !v || !o || !lse || !dout || !dq) return SPATTN_E_ARG;
   return launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, 0,
-                       resolve_scale(scale, d), workspace, (hipStream_t)stream);
+                       resolve_scale(scale, d), kFixed, workspace, (hipStream_t)stream);
 }
 
 int spattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
@@ -182,7 +185,7 @@ int spattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* ls
   if (st != SPATTN_OK) return st;
   if (!q || !k || !v || !lse || !dout || !dk || !dv) return SPATTN_E_ARG;
   return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, 0,
-                         resolve_scale(scale, d), workspace, (hipStream_t)stream);
+                         resolve_scale(scale, d), kFixed, workspace, (hipStream_t)stream);
 }
 
 static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -195,11 +198,11 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || local_window < 0) return SPATTN_E_ARG;
   const float sc = resolve_scale(scale, d);
   const int w = local_window < N ? local_window : N;
-  st = launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, w, sc, workspace,
+  st = launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, w, sc, kFixed, workspace,
                      (hipStream_t)stream);
   if (st != SPATTN_OK) return st;
-  return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, w, sc, workspace,
-                         (hipStream_t)stream);
+  return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, w, sc, kFixed,
+                         workspace, (hipStream_t)stream);
 }
 
 int spattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -216,6 +219,63 @@ int spattn_bwd_local(const void* q, const void* k, const void* v, const void* o,
                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, grad_dtype, band_lo, band_hi, local_window,
                   scale, workspace, workspace_bytes, stream);
+}
+
+// Packed variable-length batches: n_seqs sequences in [H, total, d] tensors
+// (LSE [H, total]), sequence s at tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1.
+static int varlen_check(const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen, int32_t total, int32_t H,
+                        int32_t d, int32_t dtype, const int32_t* band_lo, const int32_t* band_hi,
+                        int32_t local_window, Bands* bands, Packed* pk) {
+  if (cu_seqlens == nullptr || n_seqs < 1 || max_seqlen < 1 || total < 1 || local_window < 0) return SPATTN_E_ARG;
+  int st = check_sizes(1, H, total, d, dtype);
+  if (st != SPATTN_OK) return st;
+  st = make_bands(max_seqlen, H, band_lo, band_hi, bands);
+  if (st != SPATTN_OK) return st;
+  pk->cu = cu_seqlens;
+  pk->T = total;
+  pk->own_bdp = band_lo == nullptr ? 1 : 0;
+  return SPATTN_OK;
+}
+
+int spattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+                      int32_t n_seqs, int32_t max_seqlen, int32_t total, int32_t H, int32_t d, int32_t dtype,
+                      const int32_t* band_lo, const int32_t* band_hi, int32_t local_window, float scale,
+                      void* stream) {
+  Bands bands;
+  Packed pk;
+  int st = varlen_check(cu_seqlens, n_seqs, max_seqlen, total, H, d, dtype, band_lo, band_hi, local_window, &bands,
+                        &pk);
+  if (st != SPATTN_OK) return st;
+  if (!q || !k || !v || !o || !lse) return SPATTN_E_ARG;
+  const float sc = resolve_scale(scale, d);
+  const int w = local_window < max_seqlen ? local_window : max_seqlen;
+  if (dtype == SPATTN_BF16)
+    return launch_fwd_bf16(q, k, v, o, lse, n_seqs, H, max_seqlen, d, bands, w, sc, pk, (hipStream_t)stream);
+  return launch_fwd_f32(q, k, v, o, lse, n_seqs, H, max_seqlen, d, bands, w, sc, pk, (hipStream_t)stream);
+}
+
+int spattn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, const int32_t* cu_seqlens, int32_t n_seqs,
+                      int32_t max_seqlen, int32_t total, int32_t H, int32_t d, int32_t dtype, int32_t grad_dtype,
+                      const int32_t* band_lo, const int32_t* band_hi, int32_t local_window, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  Bands bands;
+  Packed pk;
+  int st = varlen_check(cu_seqlens, n_seqs, max_seqlen, total, H, d, dtype, band_lo, band_hi, local_window, &bands,
+                        &pk);
+  if (st != SPATTN_OK) return st;
+  if (grad_dtype != SPATTN_F32 && grad_dtype != dtype) return SPATTN_E_UNSUPPORTED;
+  const size_t need = bwd_workspace_bytes(1, H, total, d, dtype, grad_dtype);
+  if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return SPATTN_E_WORKSPACE;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPATTN_E_ARG;
+  const float sc = resolve_scale(scale, d);
+  const int w = local_window < max_seqlen ? local_window : max_seqlen;
+  st = launch_bwd_dq(q, k, v, o, lse, dout, dq, n_seqs, H, max_seqlen, d, dtype, grad_dtype, bands, w, sc, pk,
+                     workspace, (hipStream_t)stream);
+  if (st != SPATTN_OK) return st;
+  return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, n_seqs, H, max_seqlen, d, dtype, grad_dtype, bands, w, sc, pk,
+                         workspace, (hipStream_t)stream);
 }
 
 int spattn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

@@ -107,6 +107,71 @@ def fwd(q, k, v, bands=None, scale=None, out=None, lse=None, local_window=0):
     return out, lse
 
 
+def _varlen_prep(q, cu_seqlens, max_seqlen):
+    """Packed tensors [H, T, d]; cu_seqlens an int32 GPU tensor [S + 1]."""
+    if q.dim() != 3:
+        raise ValueError("packed tensors must be [H, total, d]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
+        raise ValueError("cu_seqlens must be an int32 GPU tensor [n_seqs + 1]")
+    if not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be contiguous with at least two entries")
+    H, T, d = q.shape
+    return H, T, d, cu_seqlens.numel() - 1, int(max_seqlen)
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, bands=None, scale=None, out=None, lse=None, local_window=0):
+    """Forward over a packed batch (spattn_fwd_varlen): q, k, v [H, T, d], the
+    sequences at cu_seqlens (int32 GPU [S + 1]); bands None gives every
+    sequence its own Balanced Distance Partitioning table.  Returns (o, lse);
+    lse float32 [H, T]."""
+    H, T, d, S, M = _varlen_prep(q, cu_seqlens, max_seqlen)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    for t in (k, v, out):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v, o must be contiguous GPU tensors of one shape and dtype")
+    if q.dtype not in _DT or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q must be a contiguous float32 or bfloat16 GPU tensor")
+    if lse.dtype != torch.float32 or lse.shape != (H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [H, T]")
+    p_lo, p_hi, _keep = _bands_arg(bands, H)
+    st = _lib.load().spattn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), S, M, T,
+                                       H, d, _DT[q.dtype], p_lo, p_hi, int(local_window), float(scale or 0.0),
+                                       _stream_handle(q.device))
+    _lib.check(st, "spattn_fwd_varlen")
+    return out, lse
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, bands=None, scale=None, grad_dtype=None,
+               workspace=None, out=None, local_window=0):
+    """Backward over a packed batch (spattn_bwd_varlen).  Returns (dq, dk, dv)."""
+    H, T, d, S, M = _varlen_prep(q, cu_seqlens, max_seqlen)
+    for t in (k, v, o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v, o, dout must be contiguous GPU tensors of one shape and dtype")
+    if lse.dtype != torch.float32 or lse.shape != (H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [H, T]")
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
+    need = bwd_workspace_bytes(1, H, T, d, q.dtype, grad_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = tuple(torch.empty(q.shape, dtype=grad_dtype, device=q.device) for _ in range(3))
+    for t in out:
+        if t.shape != q.shape or t.dtype != grad_dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("gradient buffers must be contiguous GPU tensors of q's shape and grad_dtype")
+    p_lo, p_hi, _keep = _bands_arg(bands, H)
+    dq, dk, dv = out
+    st = _lib.load().spattn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _ptr(cu_seqlens), S, M, T, H, d, _DT[q.dtype],
+                                       _DT[grad_dtype], p_lo, p_hi, int(local_window), float(scale or 0.0),
+                                       _ptr(workspace), workspace.numel(), _stream_handle(q.device))
+    _lib.check(st, "spattn_bwd_varlen")
+    return dq, dk, dv
+
+
 def decode(q, k_cache, v_cache, lengths=None, bands=None, local_window=0, scale=None, out=None, lse=None):
     """Decode step: q [B, H, d] against caches [B, H, Nmax, d]; ``lengths``
     an int32 device tensor [B] of valid cache rows (None: all Nmax).

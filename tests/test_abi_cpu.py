@@ -180,3 +180,33 @@ def test_decode_validation_before_launch():
     assert dec(dtype=9) == _lib.E_UNSUPPORTED
     assert dec(B=0) == _lib.E_ARG
     assert dec(ptr=ctypes.c_void_p(0)) == _lib.E_ARG
+
+
+def test_varlen_validation_before_launch():
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+    I2 = lambda a, b: (ctypes.c_int32 * 2)(a, b)
+
+    def fwd(cu=p, S=2, M=8, T=12, H=2, d=64, dtype=_lib.BF16, lo=None, hi=None, w=0, ptr=p):
+        return lib.spattn_fwd_varlen(ptr, p, p, p, p, cu, S, M, T, H, d, dtype, lo, hi, w, 0.0, None)
+
+    def bwd(ws=ctypes.c_void_p(256), nbytes=None, gdt=_lib.BF16, S=2, ptr=p):
+        need = lib.spattn_bwd_workspace_bytes(1, 2, 12, 64, _lib.BF16, gdt)
+        return lib.spattn_bwd_varlen(ptr, p, p, p, p, p, p, p, p, p, S, 8, 12, 2, 64, _lib.BF16, gdt, None, None,
+                                     0, 0.0, ws, need if nbytes is None else nbytes, None)
+    assert fwd(cu=None) == _lib.E_ARG
+    assert fwd(S=0) == _lib.E_ARG
+    assert fwd(M=0) == _lib.E_ARG
+    assert fwd(T=0) == _lib.E_ARG
+    assert fwd(H=0) == _lib.E_ARG
+    assert fwd(w=-1) == _lib.E_ARG
+    assert fwd(d=96) == _lib.E_UNSUPPORTED
+    assert fwd(dtype=5) == _lib.E_UNSUPPORTED
+    assert fwd(ptr=ctypes.c_void_p(0)) == _lib.E_ARG
+    assert fwd(lo=I2(0, 4), hi=I2(3, 8)) == _lib.E_ARG   # hi beyond max_seqlen - 1
+    assert fwd(lo=I2(0, 4), hi=None) == _lib.E_ARG       # only one array
+    assert bwd(S=0) == _lib.E_ARG
+    assert bwd(ws=ctypes.c_void_p(0)) == _lib.E_WORKSPACE
+    assert bwd(nbytes=16) == _lib.E_WORKSPACE
+    assert bwd(gdt=7) == _lib.E_UNSUPPORTED
+    assert bwd(ptr=ctypes.c_void_p(0)) == _lib.E_ARG
