@@ -65,10 +65,10 @@ struct Vec8<float> {
 constexpr int kDecThreads = 256;
 
 template <typename T, int D>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(kDecThreads, 4) void decode_kernel(DecodeArgs p) {
   constexpr int kLpr = D / 8;                       // lanes per cache row
   constexpr int kRpi = 64 / kLpr;                   // rows per wave step
-  constexpr int kSteps = sizeof(T) == 2 ? 16 : 8;   // steps per chunk (register budget)
+  constexpr int kSteps = sizeof(T) == 2 ? 8 : 4;    // steps per chunk (register budget: 4 waves per SIMD)
   constexpr int kChunk = kSteps * kRpi;             // rows per chunk
   constexpr int kWaves = kDecThreads / 64;
   __shared__ float red_m[kWaves], red_l[kWaves];
