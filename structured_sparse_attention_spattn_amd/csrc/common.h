@@ -86,12 +86,6 @@ __device__ __forceinline__ SeqHead seq_head(const int32_t* cu, int T, int own_bd
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-// 16x16x32 bf16 -> f32.  Operand layout (lane l, group q = l / 16):
-//   A: row l % 16, k-slots 8q .. 8q+7;   B: column l % 16, k-slots 8q .. 8q+7
-//   C: column l % 16, register r holds row 4q + r.
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 // 32x32x2 f32: A row l % 32, k-slot g; B column l % 32, k-slot g; C as above.
 __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -150,19 +144,6 @@ __device__ __forceinline__ bf16x8 kmajor_operand(const bf16* tile, int kbase, in
   const int grp = lane >> 4, j = lane & 15, g = lane >> 5;
   const int r = kbase + 8 * g + (j >> 2);
   const int col = n0 + 16 * (grp & 1) + 4 * (j & 3);
-  const bf16x4 a = lds_read_tr4(tile + tile_off<D>(r, col));
-  const bf16x4 b = lds_read_tr4(tile + tile_off<D>(r + 4, col));
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// 16x16x32 operand whose k index runs down the rows of a swizzled tile: lane
-// l (group q = l/16) receives rows kbase + 8q .. kbase + 8q + 7 of column
-// n0 + (l % 16), i.e. the k-slots 8q .. 8q+7 of MFMA row/column l % 16.
-template <int D>
-__device__ __forceinline__ bf16x8 kmajor16_operand(const bf16* tile, int kbase, int n0, int lane) {
-  const int q = lane >> 4, j = lane & 15;
-  const int r = kbase + 8 * q + (j >> 2);
-  const int col = n0 + 4 * (j & 3);
   const bf16x4 a = lds_read_tr4(tile + tile_off<D>(r, col));
   const bf16x4 b = lds_read_tr4(tile + tile_off<D>(r + 4, col));
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -306,11 +287,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Sum over kk of a[kk] x b[kk] (32x32 output, k = 16 per product) with the
-// products spread over up to four independent accumulators: a chain of
-// dependent MFMAs waits the full MFMA latency per step, four chains keep the
-// matrix pipe issuing back to back.
-template <int KK, int CH = 4>
+// Sum over kk of a[kk] x b[kk] (32x32 output, k = 16 per product), the
+// products spread over CH independent accumulators that are added at the end.
+// On gfx950 one dependent chain issues as fast as several (8 dependent
+// 32x32x16 products measured at 258.6 cycles, the same as 4 chains), so the
+// kernels use CH = 1 and save the reduction's VALU work and registers.
+template <int KK, int CH = 1>
 __device__ __forceinline__ f32x16 mfma_ksum(const bf16x8* a, const bf16x8* b) {
   constexpr int kCh = KK < CH ? KK : CH;
   f32x16 part[kCh];
@@ -423,16 +405,6 @@ __device__ __forceinline__ void stage_transposed(float* st, const f32x16* acc, f
     for (int a = 0; a < 4; ++a)
       *(f32x4*)&st[stage_off<D>(r, 32 * dt + 8 * a + 4 * g)] =
           f32x4{acc[dt][4 * a] * mul, acc[dt][4 * a + 1] * mul, acc[dt][4 * a + 2] * mul, acc[dt][4 * a + 3] * mul};
-}
-// Accumulators of X itself (column l % 32 = column 32 dt + l % 32 of X,
-// register i = row 8 (i / 4) + 4 g + i % 4) into the staging tile.
-template <int D>
-__device__ __forceinline__ void stage_direct(float* st, const f32x16* acc, int lane) {
-  const int g = lane >> 5, c = lane & 31;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st[stage_off<D>(8 * (i >> 2) + 4 * g + (i & 3), 32 * dt + c)] = acc[dt][i];
 }
 // Rows 0 .. nrows - 1 of the staging tile to dst + row0 * D (row-major,
 // bfloat16 or float32): every lane moves 8 consecutive values of one row, so

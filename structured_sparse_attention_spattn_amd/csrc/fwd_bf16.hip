@@ -85,10 +85,7 @@ constexpr float kRescaleLog2 = 8.0f;
 
 // Independent accumulator chains of the score product: one chain needs no
 // adds afterwards, and the interleaved softmax work covers its latency.
-#ifndef SPATTN_FWD_CHAINS
-#define SPATTN_FWD_CHAINS 1
-#endif
-constexpr int kChains = SPATTN_FWD_CHAINS;
+constexpr int kChains = 1;
 
 // Row maximum of one 32-key half, new reference, correction factor for the
 // state accumulated so far (1 when the reference is kept) and the exponent
