@@ -28,6 +28,7 @@ B, H, N, D = 8, 16, 4096, 128
 SEED = 1005
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
+FP32_PEAK_TFLOPS = 157.3  # fp32 matrix (and vector) peak
 
 
 def kernel_source_hash():
@@ -58,10 +59,13 @@ def measured_traffic(kernel):
     return None if k is None else int(k["traffic_bytes"])
 
 
-def pairs_total(lo, hi, local_window=0):
+def pairs_total(lo, hi, local_window=0, seq_len=None, batch=None):
     """Attended causal pairs over all heads and the batch: per head, the
     distances in [lo_h, hi_h] (joined with [0, local_window - 1]), each
-    distance d contributing N - d query rows."""
+    distance d contributing N - d query rows (N, B: the bench workload's
+    unless given)."""
+    N = seq_len if seq_len is not None else globals()["N"]
+    B = batch if batch is not None else globals()["B"]
     tot = 0
     for l, u in zip(lo, hi):
         ranges = []
@@ -91,6 +95,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal comparison")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the ablation-pattern and local-window measurements")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload forward measurements (workloads 1-4)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -240,6 +246,46 @@ def main():
             "speedup_fwdbwd": round(dms / ms_per_step, 3), "speedup_fwd": round(dfwd / fwd_ms, 3),
             "dense_tflops_fwdbwd": round(14 * D * pairs_total(dlo, dhi) / (dms * 1e-3) / 1e12, 2),
         }
+
+    if not args.no_configs:
+        # forward throughput of the other workloads (the fp32 N = 1024 one and
+        # the bf16 N = 4096 / 8192 / 10000 ones), seeded inputs of their shapes
+        from structured_sparse_attention_spattn_amd.workloads import WORKLOADS, seed_for
+        per_cfg = {}
+        for idx in (1, 2, 3, 4):
+            w = WORKLOADS[idx]
+            cB, cH, cN, cd = w["B"], w["H"], w["N"], w["d"]
+            cinp = make_inputs(cB, cH, cN, cd, dtype=w["dtype"], seed=seed_for(idx), scale=w["scale"])
+            cq, ck, cv = (cinp[n].to(dev) for n in ("q", "k", "v"))
+            co = torch.empty_like(cq)
+            cl = torch.empty((cB, cH, cN), dtype=torch.float32, device=dev)
+            for _ in range(3):
+                ops.fwd(cq, ck, cv, out=co, lse=cl)
+            torch.cuda.synchronize()
+            reps = 20
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                ops.fwd(cq, ck, cv, out=co, lse=cl)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            clo, chi = ops.band_table(cN, cH)
+            cpairs = pairs_total(clo, chi, seq_len=cN, batch=cB)
+            tf = 4 * cd * cpairs / (ms * 1e-3) / 1e12
+            esz = 4 if w["dtype"] == "f32" else 2
+            act = cB * sum(max(0, cN - int(l)) for l in clo)
+            rowb, allr = cd * esz, cB * cH * cN
+            min_bytes = 3 * rowb * act + (rowb + 4) * allr
+            peak = FP32_PEAK_TFLOPS if w["dtype"] == "f32" else BF16_PEAK_TFLOPS
+            per_cfg[w["name"]] = {
+                "fwd_us": round(ms * 1e3, 2), "inband_pairs": cpairs,
+                "pairs_per_s": round(cpairs / (ms * 1e-3), 1), "tflops": round(tf, 2),
+                "pct_peak": round(100 * tf / peak, 2), "peak_tflops": peak,
+                "hbm_frac_minimal_io": round(min_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            }
+            del cq, ck, cv, co, cl, cinp
+        out["configs"] = per_cfg
 
     if not args.no_variants:
         def timed_total(bands, lw, steps, warmup):
