@@ -26,6 +26,7 @@ namespace spattn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kZeroGroup = 4;  // query tiles without keys zeroed by one dQ workgroup
 
 struct BwdArgs {
   const bf16* q;
@@ -82,6 +83,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const DistSet dset = dist_set(sh.lo, sh.hi, TWO ? p.local_window : 0);
   const int lo = dset.lo;
   const int hi = dset.hi;
+  // Query tiles without keys (a prefix of the tiles) only get zero rows of dQ
+  // and D (D = 0 keeps a later dK/dV block that overlaps these rows finite):
+  // the first of every kZeroGroup of them writes the group, the others exit.
+  {
+    const int md = min_dist(dset, N);
+    const int tiles = (N + kDqBQ - 1) / kDqBQ;
+    const int n_inact = md >= N ? tiles : md / kDqBQ;
+    if (t < n_inact) {
+      if (t % kZeroGroup != 0) return;
+      for (int tt = t; tt < min(t + kZeroGroup, n_inact); ++tt) {
+        const int r0 = tt * kDqBQ + 32 * wave;
+        if (r0 > N - 1) continue;
+        store_zero_rows<D>(p.dq, sh.row0 + r0, min(32, N - r0), p.grad_f32 != 0, lane);
+        if (lane < 32 && r0 + lane < N) p.dvec[sh.row0 + r0 + lane] = 0.f;
+      }
+      return;
+    }
+  }
   const size_t base = sh.row0 * D;
   const bf16* __restrict__ kb = p.k + base;
   const bf16* __restrict__ vb = p.v + base;

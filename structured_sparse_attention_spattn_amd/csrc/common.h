@@ -588,6 +588,15 @@ __host__ __device__ __forceinline__ void align_walk(TileWalk& w, int r0, int r1,
   w.rot = k < w.n ? k : 0;
 }
 
+// Smallest distance of the set, or n (no distance in [0, n - 1]) when the set
+// is empty.  Key j has a query iff j <= n - 1 - min_dist; query i has a key
+// iff i >= min_dist.  So the tiles without work are a suffix of the key tiles
+// and a prefix of the query tiles.
+__host__ __device__ __forceinline__ int min_dist(const DistSet& s, int n) {
+  if (has_second(s)) return s.nlo < s.lo ? s.nlo : s.lo;
+  return s.hi >= s.lo && s.lo <= n - 1 ? s.lo : n;
+}
+
 // Tile tests over the whole distance set (an empty second range never meets
 // and is never full).
 __host__ __device__ __forceinline__ bool set_meets(int i_min, int i_max, int j_min, int j_max, const DistSet& s) {
