@@ -8,8 +8,9 @@ B = 8, H = 16, N = 4096, d = 128, bfloat16 inputs resident in HBM.
 
 Prints ONE JSON line.  ``value`` is in-band TFLOP/s of fwd+bwd (14 d FLOP per
 attended pair; the heads together attend N(N+1)/2 pairs per sequence).
-Extra keys report the forward alone, the dense-causal kernel of the same
-library at the same shape, the roofline of the dominant kernel, the float64
+Extra keys report the forward alone, per-kernel medians, the same kernels
+with L2 and MALL flushed before each launch ("cold"), the dense-causal kernel
+of the same library at the same shape, the roofline of the dominant kernel, the float64
 CPU oracle timed on this host and, under "variants", the same shape with the
 band tables of the page's ablation patterns (sliding window, gapped half
 bands) and with a shared local window joined to every band.
@@ -97,6 +98,8 @@ def main():
                     help="skip the ablation-pattern and local-window measurements")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload forward measurements (workloads 1-4)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the flushed-cache (cold) per-kernel timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -137,8 +140,9 @@ def main():
         ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads)
 
     def timed(bands, steps, warmup):
-        """Wall time of `steps` full steps, plus per-kernel HIP-event averages
-        (every event is recorded on the stream the kernels are launched on)."""
+        """Wall time of `steps` full steps, plus per-kernel HIP-event means and
+        medians (every event is recorded on the stream the kernels are launched
+        on)."""
         for _ in range(warmup):
             step(bands)
         torch.cuda.synchronize()
@@ -157,9 +161,11 @@ def main():
         wall = time.perf_counter() - t0
         per = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
                for i, name in enumerate(("fwd", "bwd_dq", "bwd_dkdv"))}
-        return wall, per
+        med = {name: float(np.median([e[i].elapsed_time(e[i + 1]) for e in ev]))
+               for i, name in enumerate(("fwd", "bwd_dq", "bwd_dkdv"))}
+        return wall, per, med
 
-    wall, per = timed(None, args.steps, args.warmup)
+    wall, per, per_median = timed(None, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
     fwd_ms, bwd_ms = per["fwd"], per["bwd_dq"] + per["bwd_dkdv"]
     pairs = pairs_total(lo, hi)
@@ -236,9 +242,42 @@ def main():
         "roofline": roofline,
     }
 
+    out["kernel_ms_median"] = {kname: round(t, 4) for kname, t in per_median.items()}
+
+    if not args.no_cold:
+        # Cold caches: before every kernel a 512 MiB fill (outside the events)
+        # evicts the inputs from L2 and the MALL; medians over the repeats.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        n_cold = max(5, args.steps // 2)
+        calls = (("fwd", lambda: ops.fwd(q, k, v, out=o, lse=lse)),
+                 ("bwd_dq", lambda: ops.bwd_dq(q, k, v, o, lse, do, ws, out=grads[0])),
+                 ("bwd_dkdv", lambda: ops.bwd_dkdv(q, k, v, lse, do, ws, out=grads[1:])))
+        evs = []
+        for _ in range(n_cold):
+            for name, call in calls:
+                flush.zero_()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call()
+                e1.record()
+                evs.append((name, e0, e1))
+        torch.cuda.synchronize()
+        cold = {name: float(np.median([a.elapsed_time(b) for n_, a, b in evs if n_ == name]))
+                for name, _ in calls}
+        cold_step = sum(cold.values())
+        out["cold"] = {
+            "repeats": n_cold,
+            "kernel_ms_median": {kname: round(t, 4) for kname, t in cold.items()},
+            "ms_per_step": round(cold_step, 4),
+            "tflops_fwdbwd": round(fl_all / (cold_step * 1e-3) / 1e12, 2),
+            "kernel_hbm_frac": {kname: round(alg_bytes[kname] / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                                for kname, t in cold.items()},
+        }
+        del flush
+
     if not args.no_dense:
         dlo, dhi = ops.dense_bands(N, H)
-        dwall, dper = timed((dlo, dhi), max(2, args.steps // 5), 1)
+        dwall, dper, _ = timed((dlo, dhi), max(2, args.steps // 5), 1)
         dms = dwall * 1e3 / max(2, args.steps // 5)
         dfwd, dbwd = dper["fwd"], dper["bwd_dq"] + dper["bwd_dkdv"]
         out["dense_causal"] = {
@@ -310,19 +349,19 @@ def main():
             return wall, f, b
 
         variants = {}
-        nvs = max(3, args.steps // 4)
+        nvs = max(5, args.steps // 2)
         wlo, whi = ops.window_bands(N, H, N // H)
         glo, ghi = ops.gapped_half_bands(N, H)
         for name, bands, lw, (plo, phi) in (
                 (f"sliding_window_{N // H}", (wlo, whi), 0, (wlo, whi)),
                 ("gapped_half_bands", (glo, ghi), 0, (glo, ghi)),
                 ("bands_plus_local_window_64", None, 64, (lo, hi))):
-            wall_v, f_v, b_v = timed_total(bands, lw, nvs, 2)
+            wall_v, f_v, b_v = timed_total(bands, lw, nvs, 3)
             pv = pairs_total(plo, phi, lw)
             variants[name] = {
-                "ms_per_step": round(wall_v, 4), "fwd_ms": round(f_v, 4), "bwd_ms": round(b_v, 4),
-                "attended_pairs": pv,
-                "tflops_fwdbwd": round(14 * D * pv / (wall_v * 1e-3) / 1e12, 2),
+                "ms_per_step": round(f_v + b_v, 4), "fwd_ms": round(f_v, 4), "bwd_ms": round(b_v, 4),
+                "wall_ms_per_step": round(wall_v, 4), "attended_pairs": pv,
+                "tflops_fwdbwd": round(14 * D * pv / ((f_v + b_v) * 1e-3) / 1e12, 2),
             }
         out["variants"] = variants
 
