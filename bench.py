@@ -277,8 +277,9 @@ def main():
 
     if not args.no_dense:
         dlo, dhi = ops.dense_bands(N, H)
-        dwall, dper, _ = timed((dlo, dhi), max(2, args.steps // 5), 1)
-        dms = dwall * 1e3 / max(2, args.steps // 5)
+        n_dense = max(5, args.steps // 2)
+        dwall, dper, _ = timed((dlo, dhi), n_dense, 2)
+        dms = dwall * 1e3 / n_dense
         dfwd, dbwd = dper["fwd"], dper["bwd_dq"] + dper["bwd_dkdv"]
         out["dense_causal"] = {
             "ms_per_step": round(dms, 4), "fwd_ms": round(dfwd, 4), "bwd_ms": round(dbwd, 4),
