@@ -295,6 +295,33 @@ def test_bwd_full_workload_sampled_and_invariants():
                 assert err <= BF16_TOL, f"{nm} b={b} h={h}: max-abs {err:.3e}"
 
 
+def test_full_workload_repeatable_bitwise():
+    """Every output of the forward and of both backward stages is the same
+    bit for bit over repeated launches at the bench workload size: no atomics,
+    no order-dependent reductions, and a race on LDS or on the workspace
+    would show up as a differing bit."""
+    w = WORKLOADS[5]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    _say(f"repeatability at {w['name']}")
+    inp = _to_dev(make_inputs(B, H, N, d, dtype="bf16", seed=seed_for(5) + 7, with_dout=True))
+    ws = torch.empty(ops.bwd_workspace_bytes(B, H, N, d, torch.bfloat16, torch.bfloat16), dtype=torch.uint8,
+                     device=DEV)
+    first = None
+    for rep in range(3):
+        o, lse = ops.fwd(inp["q"], inp["k"], inp["v"])
+        dq = ops.bwd_dq(inp["q"], inp["k"], inp["v"], o, lse, inp["dout"], ws)
+        dk, dv = ops.bwd_dkdv(inp["q"], inp["k"], inp["v"], lse, inp["dout"], ws)
+        torch.cuda.synchronize()
+        outs = (o, lse, dq, dk, dv)
+        if first is None:
+            first = outs
+            continue
+        for a, b_, nm in zip(first, outs, ("O", "LSE", "dQ", "dK", "dV")):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_.view(torch.int32)), \
+                f"{nm} differs on repeat {rep}"
+
+
 @pytest.mark.parametrize("dtype,gdt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
 def test_bwd_stages_equal_combined(dtype, gdt):
     """spattn_bwd_dq then spattn_bwd_dkdv reproduce spattn_bwd bit for bit."""
