@@ -207,6 +207,198 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
   }
 }
 
+
+// Small problems, where there are too few 128-row query tiles to occupy the
+// chip: one workgroup per 32-row query tile, and its four waves split the
+// key tiles of the tile's walk (wave w takes tiles w, w + 4, ...).  Each wave
+// stages its own K / V tile in its own LDS area and keeps its own online
+// softmax state; at the end the four (maximum, sum, output) triples are merged
+// through LDS, the same merge as across the chunks of a single wave.
+constexpr int kSplitBQ = 32;
+constexpr int kSplitMaxTiles = 512;  // 128-row tiles below which the key split is used (2 per CU)
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_f32_split_kernel(FwdF32Args p) {
+  using SM = F32Smem<D>;
+  constexpr int kDT = D / 32;
+  constexpr int kKK = D / 2;
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kWaveLoads = kBK * D / 4 / 64;  // float4 loads per lane per tensor (a wave loads a tile)
+  constexpr int kRedRow = D + 4;                // merge rows: 16-byte aligned, spread over banks
+  static_assert(kWaves * 32 * kRedRow + 2 * kWaves * 32 <= kWaves * SM::kStage, "merge area");
+  __shared__ float smem[kWaves * SM::kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+
+  const int total = p.B * p.H * p.n_qt;
+  const int item = xcd_remap(blockIdx.x, total);
+  const int t = item % p.n_qt;
+  const int bh = item / p.n_qt;
+  const int h = bh % p.H;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, bh / p.H, h);
+  const int N = sh.n;
+  if (t * kSplitBQ >= N) return;  // past the end of a packed sequence
+  const DistSet dset = dist_set(sh.lo, sh.hi, p.local_window);
+  const int lo = dset.lo;
+  const int hi = dset.hi;
+  const size_t base = sh.row0 * D;
+  const float* __restrict__ qb = p.q + base;
+  const float* __restrict__ kb = p.k + base;
+  const float* __restrict__ vb = p.v + base;
+  float* __restrict__ ob = p.o + base;
+  float* __restrict__ lb = p.lse + sh.row0;
+  const float ninf = -__builtin_inff();
+
+  const int i0 = t * kSplitBQ;
+  const int i1 = min(N - 1, i0 + kSplitBQ - 1);
+  KeySpan span2{0, -1};
+  if (has_second(dset)) span2 = band_key_span(i0, i1, dset.nlo, dset.nhi);
+  const TileWalk walk = tile_walk(band_key_span(i0, i1, lo, hi), span2, kBK);
+  if (walk.n == 0) {
+    for (int c = tid; c < kSplitBQ * (D / 4); c += kThreads) {
+      const int r = c / (D / 4), cc = c % (D / 4);
+      if (i0 + r < N) *(f32x4*)(ob + (size_t)(i0 + r) * D + cc * 4) = f32x4{0, 0, 0, 0};
+    }
+    if (tid < kSplitBQ && i0 + tid < N) lb[i0 + tid] = ninf;
+    return;
+  }
+  const int iq = i0 + c32;
+
+  float qreg[kKK];
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) qreg[kk] = iq < N ? qb[(size_t)iq * D + 2 * kk + g] : 0.f;
+
+  float* ks = smem + wave * SM::kStage;
+  float* vs = ks + SM::kKStage;
+  // One tensor's tile (rows jb .. jb + 31) into this wave's LDS area.
+  auto stage = [&](const float* src, float* dst, int row_stride, int jb) {
+    f32x4 r4[kWaveLoads];
+#pragma unroll
+    for (int r = 0; r < kWaveLoads; ++r) {
+      const int c = lane + 64 * r;
+      const int j = jb + c / (D / 4);
+      r4[r] = j < N ? *(const f32x4*)(src + (size_t)j * D + (c % (D / 4)) * 4) : f32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < kWaveLoads; ++r) {
+      const int c = lane + 64 * r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(c / (D / 4)) * row_stride + (c % (D / 4)) * 4 + e] = r4[r][e];
+    }
+  };
+  // Orders this wave's LDS writes before its reads (and reads before the next
+  // writes): LDS instructions of one wave complete in order, so only the
+  // compiler's ordering has to be pinned.
+  auto wave_sync = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  f32x16 acc[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  float m_run = ninf, l_run = 0.f;
+  const float sl2 = p.scale_log2;
+
+  for (int v = wave; v < walk.n; v += kWaves) {
+    const int jb = walk.at(v) * kBK;
+    if (!set_meets(i0, i1, jb, jb + kBK - 1, dset)) continue;
+    wave_sync();  // the previous tile's reads are issued before it is overwritten
+    stage(kb, ks, SM::kKRow, jb);
+    stage(vb, vs, SM::kVRow, jb);
+    wave_sync();
+    f32x16 sacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) sacc = mfma32_f32(ks[c32 * SM::kKRow + 2 * kk + g], qreg[kk], sacc);
+    float x[16];
+    const bool full = set_full(i0, i1, jb, jb + kBK - 1, dset);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = jb + 8 * (i >> 2) + 4 * g + (i & 3);
+      const int dist = iq - j;
+      const bool in = (dist >= lo && dist <= hi) || (dist >= dset.nlo && dist <= dset.nhi);
+      x[i] = (full || in) ? sacc[i] * sl2 : ninf;
+    }
+    float mx = ninf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == ninf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] = fast_exp2(x[i] - m_use);
+      psum += x[i];
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = 8 * (i >> 2) + 4 * g + (i & 3);
+        acc[dt] = mfma32_f32(vs[j * SM::kVRow + 32 * dt + c32], x[i], acc[dt]);
+      }
+    }
+  }
+
+  // ---- merge the four waves' partial results (query row c32 of each)
+  __syncthreads();  // every wave is done with its tiles: the LDS becomes the merge area
+  float* red_o = smem;                             // [wave][row][kRedRow]
+  float* red_m = smem + kWaves * 32 * kRedRow;     // [wave][row]
+  float* red_l = red_m + kWaves * 32;              // [wave][row]
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      red_o[(wave * 32 + c32) * kRedRow + 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)] = acc[dt][i];
+  const float l_w = l_run + __shfl_xor(l_run, 32);
+  if (g == 0) {
+    red_m[wave * 32 + c32] = m_run;
+    red_l[wave * 32 + c32] = l_w;
+  }
+  __syncthreads();
+  for (int c = tid; c < kSplitBQ * (D / 4); c += kThreads) {
+    const int r = c / (D / 4), col = c % (D / 4);
+    const int i = i0 + r;
+    if (i >= N) continue;
+    float M = ninf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w * 32 + r]);
+    float L = 0.f;
+    f32x4 o4{0, 0, 0, 0};
+    if (M != ninf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = red_m[w * 32 + r];
+        const float f = mw == ninf ? 0.f : fast_exp2(mw - M);
+        L += red_l[w * 32 + r] * f;
+        const f32x4 pw = *(const f32x4*)&red_o[(w * 32 + r) * kRedRow + 4 * col];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] += pw[e] * f;
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] *= inv;
+    *(f32x4*)(ob + (size_t)i * D + 4 * col) = o4;
+    if (col == 0) lb[i] = L > 0.f ? (M + fast_log2(L)) * kLn2 : ninf;
+  }
+}
+
 }  // namespace
 
 int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -222,6 +414,8 @@ int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
   a.H = H;
   a.N = N;
   a.n_qt = (N + kBQ - 1) / kBQ;
+  const bool split = (long long)B * H * a.n_qt < kSplitMaxTiles;
+  if (split) a.n_qt = (N + kSplitBQ - 1) / kSplitBQ;
   a.cu = pk.cu;
   a.T = pk.T;
   a.own_bdp = pk.own_bdp;
@@ -231,7 +425,11 @@ int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
   const long long total = (long long)B * H * a.n_qt;
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   dim3 grid((unsigned)total), block(kThreads);
-  if (d == 128)
+  if (d == 128 && split)
+    hipLaunchKernelGGL(fwd_f32_split_kernel<128>, grid, block, 0, stream, a);
+  else if (d == 64 && split)
+    hipLaunchKernelGGL(fwd_f32_split_kernel<64>, grid, block, 0, stream, a);
+  else if (d == 128)
     hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, block, 0, stream, a);
   else if (d == 64)
     hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block, 0, stream, a);

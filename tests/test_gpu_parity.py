@@ -124,6 +124,10 @@ FWD_SMALL = [
     (2, 3, 333, 128, "f32", "bdp", 11, 1.0),
     (1, 5, 3, 64, "f32", "bdp", 12, 1.0),          # H > N: empty heads
     (2, 4, 190, 64, "f32", "dense", 13, 1.0),
+    (4, 16, 1024, 64, "f32", "bdp", 14, 1.0),      # 512 query tiles of 128: the undivided float32 kernel
+    (2, 32, 1024, 128, "f32", "bdp", 15, 1.0),     # same, d = 128
+    (1, 6, 640, 64, "f32", "bdp", 16, 8.0),        # large scores: rescaling inside and across the key split
+    (2, 4, 300, 64, "f32", "odd", 17, 1.0),
     (2, 5, 300, 64, "bf16", "bdp", 21, 1.0),
     (1, 12, 1000, 128, "bf16", "bdp", 22, 1.0),
     (2, 3, 257, 128, "bf16", "bdp", 23, 1.0),
