@@ -299,6 +299,39 @@ def test_bwd_full_workload_sampled_and_invariants():
                 assert err <= BF16_TOL, f"{nm} b={b} h={h}: max-abs {err:.3e}"
 
 
+def test_long_sequence_sampled():
+    """A long sequence (N = 32768, eight heads: bands 4096 wide, 66 key tiles
+    per query tile): forward and both gradients on sampled rows, each row from
+    the definition, plus the empty-row positions on every row."""
+    B, H, N, d = 1, 8, 32768, 128
+    _say(f"long sequence B={B} H={H} N={N} d={d}")
+    inp = make_inputs(B, H, N, d, dtype="bf16", seed=4242, with_dout=True)
+    dv_ = _to_dev(inp)
+    o, lse = ops.fwd(dv_["q"], dv_["k"], dv_["v"])
+    dq, dk, dv = ops.bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dv_["dout"], grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    lo, hi = oracle.band_table(N, H)
+    lse_h = lse.cpu().numpy()
+    empty = np.arange(N)[None, None, :] < lo[None, :, None]
+    assert np.array_equal(np.isneginf(lse_h), np.broadcast_to(empty, lse_h.shape))
+    o_h = o.float().cpu().numpy()
+    dq_h, dk_h, dv_h = (x.cpu().numpy().astype(np.float64) for x in (dq, dk, dv))
+    q64, k64, v64, d64 = (inp[n].float().numpy() for n in ("q", "k", "v", "dout"))
+    rng = np.random.default_rng(4242)
+    for h in range(H):
+        rows = _sample_rows(N, int(lo[h]), int(hi[h]), rng)
+        ro, rl = oracle.band_attention_fwd_rows(q64, k64, v64, lo, hi, 0, h, rows)
+        _check(o_h[0, h, rows], ro, "bf16", f"O h={h}")
+        _check_lse(lse_h[0, h, rows], rl, "bf16", f"LSE h={h}")
+    for h in (0, H - 1):
+        rows = _sample_rows(N, int(lo[h]), int(hi[h]), rng)[:6]
+        krows = sorted({int(rng.integers(0, N - int(lo[h]))), N - 1 - int(lo[h])})
+        rq, rk, rv = oracle.band_attention_bwd_rows(q64, k64, v64, d64, lo, hi, 0, h, rows, krows)
+        for got, ref, nm in ((dq_h[0, h, rows], rq, "dQ"), (dk_h[0, h, krows], rk, "dK"), (dv_h[0, h, krows], rv, "dV")):
+            err = np.max(np.abs(got - ref))
+            assert err <= BF16_TOL, f"{nm} h={h}: max-abs {err:.3e}"
+
+
 def test_full_workload_repeatable_bitwise():
     """Every output of the forward and of both backward stages is the same
     bit for bit over repeated launches at the bench workload size: no atomics,
