@@ -292,3 +292,30 @@ def tile_list(N, lo, hi, BQ=0, BK=0, device="cuda"):
     torch.cuda.current_stream(row_ptr.device).synchronize()
     n = int(n_out.item())
     return row_ptr.cpu().numpy(), tiles[:n].cpu().numpy(), kind[:n].cpu().numpy()
+
+
+class _BandAttention(torch.autograd.Function):
+    """Autograd node over fwd / bwd: saves O and LSE, no recomputation here."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, bands, local_window, scale):
+        o, lse = fwd(q, k, v, bands=bands, scale=scale, local_window=local_window)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.bands, ctx.local_window, ctx.scale = bands, local_window, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, dout.contiguous(), bands=ctx.bands, scale=ctx.scale,
+                         local_window=ctx.local_window)
+        return dq, dk, dv, None, None, None
+
+
+def band_attention(q, k, v, bands=None, local_window=0, scale=None):
+    """Differentiable band attention: O = fwd(q, k, v) with a backward through
+    bwd.  q, k, v are [B, H, N, d] bfloat16 or float32 on the GPU; ``bands``
+    is None (the Balanced Distance Partitioning table of (N, H)) or host
+    (lo[H], hi[H]); ``local_window`` joins [0, w - 1] to every band.  Gradients
+    come out in the input dtype."""
+    return _BandAttention.apply(q.contiguous(), k.contiguous(), v.contiguous(), bands, int(local_window), scale)
