@@ -328,7 +328,10 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   // [stage][wave][LSE of the 32 rows | D of the 32 rows]: every wave loads its own copy
   __shared__ __attribute__((aligned(16))) float rowv[kKvStages][kWaves][2 * kKvQB];
   // P from P wave w to dS wave w + kKvPairs: [block parity][w][lane][16 values]
-  __shared__ __attribute__((aligned(16))) f16 pbuf[2][kKvPairs][64][16];
+  // [block parity][pair][half][lane]: each half of a lane's 16 values is one
+  // 1 KB contiguous row of 16-byte pieces, so writes and reads are single
+  // conflict-free sweeps.
+  __shared__ __attribute__((aligned(16))) f16 pbuf[2][kKvPairs][2][64][8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -431,8 +434,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       }
       float dd[16], ds[16];
       rows16(&rowv[st][wave][kKvQB], dd);
-      const f16x8* src = (const f16x8*)&pbuf[v & 1][kw][lane][0];
-      const f16x8 pa = src[0], pb = src[1];
+      const f16x8 pa = *(const f16x8*)&pbuf[v & 1][kw][0][lane][0];
+      const f16x8 pb = *(const f16x8*)&pbuf[v & 1][kw][1][lane][0];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         ds[i] = (float)pa[i] * (dpv[i] - dd[i]);
@@ -570,9 +573,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
             pv[i] = in ? pv[i] : 0.f;
           }
         }
-        f16x8* dst = (f16x8*)&pbuf[v & 1][kw][lane][0];
-        dst[0] = pack8_f16(&pv[0]);
-        dst[1] = pack8_f16(&pv[8]);
+        *(f16x8*)&pbuf[v & 1][kw][0][lane][0] = pack8_f16(&pv[0]);
+        *(f16x8*)&pbuf[v & 1][kw][1][lane][0] = pack8_f16(&pv[8]);
         pp0 = pack8(&pv[0]);
         pp1 = pack8(&pv[8]);
       };
