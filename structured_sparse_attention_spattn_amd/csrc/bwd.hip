@@ -173,15 +173,23 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype
   (void)dtype;
   (void)grad_dtype;
   const size_t rows = (size_t)B * H * N;
-  return (rows * sizeof(float) + 255) / 256 * 256;  // the D vector
+  return 2 * ((rows * sizeof(float) + 255) / 256 * 256);  // D, then -LSE * log2(e)
 }
 
 int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                        void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
-                       float scale, float* dvec, const Packed& pk, hipStream_t stream);
+                       float scale, float* dvec, float* nl2, const Packed& pk, hipStream_t stream);
 int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                          void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
-                         float scale, float* dvec, const Packed& pk, hipStream_t stream);
+                         float scale, float* dvec, float* nl2, const Packed& pk, hipStream_t stream);
+
+// The workspace holds two float vectors over the rows of the tensors, each
+// starting on a 256-byte boundary: D_i, then -LSE_i * log2(e) (the bfloat16
+// kernels' exponent offset, written by the dQ kernel for the dK/dV kernel).
+static float* row_vector(void* workspace, int which, int B, int H, int N, const Packed& pk) {
+  const size_t rows = pk.cu != nullptr ? (size_t)H * pk.T : (size_t)B * H * N;
+  return (float*)workspace + which * ((rows + 63) / 64 * 64);
+}
 
 static BwdF32Args f32_args(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
                            void* dk, void* dv, int B, int H, int N, const Bands& bands, int local_window,
@@ -212,10 +220,10 @@ static BwdF32Args f32_args(const void* q, const void* k, const void* v, const fl
 int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                   void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
                   int local_window, float scale, const Packed& pk, void* workspace, hipStream_t stream) {
-  float* dvec = (float*)workspace;
+  float* dvec = row_vector(workspace, 0, B, H, N, pk);
   if (dtype == SPATTN_BF16)
     return launch_bwd_dq_bf16(q, k, v, o, lse, dout, dq, B, H, N, d, grad_dtype == SPATTN_F32, bands, local_window,
-                              scale, dvec, pk, stream);
+                              scale, dvec, row_vector(workspace, 1, B, H, N, pk), pk, stream);
   const long long rows = (long long)B * H * N;  // one wave per (sequence, head, row); packed: padded to N
   {
     const long long data_rows = pk.cu != nullptr ? (long long)H * pk.T : rows;  // rows held in the tensors
@@ -242,10 +250,10 @@ int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, co
 int launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                     void* dv, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
                     int local_window, float scale, const Packed& pk, void* workspace, hipStream_t stream) {
-  float* dvec = (float*)workspace;
+  float* dvec = row_vector(workspace, 0, B, H, N, pk);
   if (dtype == SPATTN_BF16)
     return launch_bwd_dkdv_bf16(q, k, v, lse, dout, dk, dv, B, H, N, d, grad_dtype == SPATTN_F32, bands,
-                                local_window, scale, dvec, pk, stream);
+                                local_window, scale, dvec, row_vector(workspace, 1, B, H, N, pk), pk, stream);
   const long long rows = (long long)B * H * N;  // one wave per (sequence, head, row); packed: padded to N
   BwdF32Args a = f32_args(q, k, v, lse, dout, nullptr, dk, dv, B, H, N, bands, local_window, scale, dvec, pk);
   dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);

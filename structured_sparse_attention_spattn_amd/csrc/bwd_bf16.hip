@@ -35,7 +35,8 @@ struct BwdArgs {
   const bf16* o;
   const bf16* dout;
   const float* lse;
-  float* dvec;  // written by bwd_dq, read by bwd_dkdv
+  float* dvec;  // D_i = dO_i . O_i: written by bwd_dq, read by bwd_dkdv
+  float* nl2;   // -LSE_i * log2(e): written by bwd_dq, read by bwd_dkdv
   void* dq;
   void* dk;
   void* dv;
@@ -97,6 +98,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
         if (r0 > N - 1) continue;
         store_zero_rows<D>(p.dq, sh.row0 + r0, min(32, N - r0), p.grad_f32 != 0, lane);
         if (lane < 32 && r0 + lane < N) p.dvec[sh.row0 + r0 + lane] = 0.f;
+        if (lane < 32 && r0 + lane < N) p.nl2[sh.row0 + r0 + lane] = 0.f;
       }
       return;
     }
@@ -171,7 +173,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
       doreg[kk] = bf16x8{};
     }
   }
-  if (row_ok && g == 0) p.dvec[sh.row0 + iq] = dval;
+  if (row_ok && g == 0) {
+    p.dvec[sh.row0 + iq] = dval;
+    p.nl2[sh.row0 + iq] = nlse2;
+  }
   const float sl2 = p.scale_log2;
   const float scl = p.scale;
   const float ndsc = -dval * scl;
@@ -356,7 +361,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   const size_t base = sh.row0 * D;
   const bf16* __restrict__ qb = p.q + base;
   const bf16* __restrict__ dob = p.dout + base;
-  const float* __restrict__ lseb = p.lse + sh.row0;
+  const float* __restrict__ nl2b = p.nl2 + sh.row0;
   const float* __restrict__ ddb = p.dvec + sh.row0;
 
   const int j0 = ut * kKvBK;
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       Tile::load(t, qb, tq * kKvQB, N, wave, lane);
       Tile::load(t + kTile, dob, tq * kKvQB, N, wave, lane);
       const int i = min(tq * kKvQB + (lane & 31), N - 1);
-      const float* src = lane < 32 ? lseb + i : ddb + i;
+      const float* src = lane < 32 ? nl2b + i : ddb + i;
       lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr(&rowv[st][wave][0])), src);
     };
     // Ring prefill first: its round trip overlaps that of the row loads below.
@@ -539,12 +544,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
             acc[dt] = mfma32(bb[2 * dt + (m < kDT ? 0 : 1)], m < kDT ? pp0 : pp1, acc[dt]);
 #pragma unroll
             for (int i = m * 16 / (2 * kDT); i < (m + 1) * 16 / (2 * kDT); ++i)
-              pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
+              pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, nl[i]));
             __builtin_amdgcn_sched_barrier(0);
           }
         } else {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, -nl[i] * kLog2e));
+          for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sc_[i], sl2, nl[i]));
         }
         if (!full) {
           // Element mask: query row r = creg(i) + 8 g of the block is kept iff
@@ -643,7 +648,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 
 static BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, bool grad_f32,
-                         const Bands& bands, float scale, float* dvec, const Packed& pk) {
+                         const Bands& bands, float scale, float* dvec, float* nl2, const Packed& pk) {
   BwdArgs a;
   a.q = (const bf16*)q;
   a.k = (const bf16*)k;
@@ -652,6 +657,7 @@ static BwdArgs make_args(const void* q, const void* k, const void* v, const void
   a.dout = (const bf16*)dout;
   a.lse = lse;
   a.dvec = dvec;
+  a.nl2 = nl2;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -672,8 +678,8 @@ static BwdArgs make_args(const void* q, const void* k, const void* v, const void
 
 int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                        void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
-                       float scale, float* dvec, const Packed& pk, hipStream_t stream) {
-  BwdArgs a = make_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, grad_f32, bands, scale, dvec, pk);
+                       float scale, float* dvec, float* nl2, const Packed& pk, hipStream_t stream) {
+  BwdArgs a = make_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, grad_f32, bands, scale, dvec, nl2, pk);
   a.n_tiles = (N + kDqBQ - 1) / kDqBQ;
   a.local_window = local_window;
   const long long total = (long long)B * H * a.n_tiles;
@@ -693,8 +699,8 @@ int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* 
 
 int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                          void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
-                         float scale, float* dvec, const Packed& pk, hipStream_t stream) {
-  BwdArgs a = make_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, grad_f32, bands, scale, dvec, pk);
+                         float scale, float* dvec, float* nl2, const Packed& pk, hipStream_t stream) {
+  BwdArgs a = make_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, grad_f32, bands, scale, dvec, nl2, pk);
   a.n_tiles = (N + kKvBK - 1) / kKvBK;
   a.local_window = local_window;
   const long long total = (long long)B * H * a.n_tiles;

@@ -86,7 +86,7 @@ def test_bwd_validation_and_workspace():
     p = ctypes.c_void_p(1)
     need = lib.spattn_bwd_workspace_bytes(2, 3, 100, 128, _lib.BF16, _lib.BF16)
     rows = 2 * 3 * 100
-    assert need == (rows * 4 + 255) // 256 * 256  # the float32 D vector
+    assert need == 2 * ((rows * 4 + 255) // 256 * 256)  # float32 D and -LSE log2(e), 256-byte aligned
     assert lib.spattn_bwd_workspace_bytes(2, 3, 100, 128, _lib.BF16, _lib.F32) == need
     assert lib.spattn_bwd_workspace_bytes(0, 3, 100, 128, _lib.BF16, _lib.BF16) == 0
     assert lib.spattn_bwd_workspace_bytes(1, 3, 100, 96, _lib.BF16, _lib.BF16) == 0
