@@ -93,8 +93,8 @@ int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace spattn_bwd needs for these sizes: two float32
- * row vectors [B,H,N], each rounded up to 256 bytes: D_i = dO_i . O_i, then
- * -LSE_i log2(e), the exponent offset the dK/dV kernel recomputes P with.
+ * row vectors [B,H,N], each rounded up to 256 bytes: -D_i = -dO_i . O_i,
+ * then -LSE_i log2(e), the exponent offset the dK/dV kernel recomputes P with.
  * Returns 0 for invalid sizes.
  */
 size_t spattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d,
@@ -207,7 +207,7 @@ int spattn_decode(const void* q, const void* k_cache, const void* v_cache, void*
  * The two stages spattn_bwd runs, exported for callers that schedule them
  * separately (and for per-kernel timing).  Same arguments and checks as
  * spattn_bwd; together they compute exactly what spattn_bwd computes.
- *   spattn_bwd_dq    writes D_i = dO_i . O_i (and -LSE_i log2(e)) into the
+ *   spattn_bwd_dq    writes -D_i = -dO_i . O_i (and -LSE_i log2(e)) into the
  *                    workspace, and dq.
  *   spattn_bwd_dkdv  reads them from the workspace and writes dk, dv; it must run
  *                    after spattn_bwd_dq with the same workspace, bands and

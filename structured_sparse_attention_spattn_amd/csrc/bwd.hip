@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const T* __restrict__
   }
 #pragma unroll
   for (int off = kLanes / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && part == 0) dvec[row] = s;
+  if (row < rows && part == 0) dvec[row] = -s;  // the workspace holds -D
 }
 
 // ------------------------------------------------------------ f32 path
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dq_kernel(BwdF32Args p) {
     di[e] = p.dout[base + (size_t)i * D + lane + 64 * e];
     acc[e] = 0.f;
   }
-  const float lse = p.lse[sh.row0 + i], dd = p.dvec[sh.row0 + i];
+  const float lse = p.lse[sh.row0 + i], nd = p.dvec[sh.row0 + i];  // nd = -D_i
   // keys of row i: the primary range, then the disjoint second range if any
   KeySpan spans[2] = {band_key_span(i, i, ds_.lo, ds_.hi), KeySpan{0, -1}};
   if (has_second(ds_)) spans[1] = band_key_span(i, i, ds_.nlo, ds_.nhi);
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dq_kernel(BwdF32Args p) {
     const float s = wave_dot<D>(qi, kj, lane) * p.scale;
     const float pij = expf(s - lse);
     const float dp = wave_dot<D>(di, vj, lane);
-    const float ds = pij * (dp - dd);
+    const float ds = pij * (dp + nd);
 #pragma unroll
     for (int e = 0; e < kE; ++e) acc[e] += ds * kj[e];
   }
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_dkdv_kernel(BwdF32Args p) {
     const float s = wave_dot<D>(qi, kj, lane) * p.scale;
     const float pij = expf(s - p.lse[lbase + i]);
     const float dp = wave_dot<D>(di, vj, lane);
-    const float ds = pij * (dp - p.dvec[lbase + i]);
+    const float ds = pij * (dp + p.dvec[lbase + i]);  // dvec holds -D
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
       dk[e] += ds * qi[e];
@@ -173,7 +173,7 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype
   (void)dtype;
   (void)grad_dtype;
   const size_t rows = (size_t)B * H * N;
-  return 2 * ((rows * sizeof(float) + 255) / 256 * 256);  // D, then -LSE * log2(e)
+  return 2 * ((rows * sizeof(float) + 255) / 256 * 256);  // -D, then -LSE * log2(e)
 }
 
 int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -184,7 +184,8 @@ int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const floa
                          float scale, float* dvec, float* nl2, const Packed& pk, hipStream_t stream);
 
 // The workspace holds two float vectors over the rows of the tensors, each
-// starting on a 256-byte boundary: D_i, then -LSE_i * log2(e) (the bfloat16
+// starting on a 256-byte boundary: -D_i (so dP - D is dP plus a stored value,
+// or an MFMA chain started from it), then -LSE_i * log2(e) (the bfloat16
 // kernels' exponent offset, written by the dQ kernel for the dK/dV kernel).
 static float* row_vector(void* workspace, int which, int B, int H, int N, const Packed& pk) {
   const size_t rows = pk.cu != nullptr ? (size_t)H * pk.T : (size_t)B * H * N;

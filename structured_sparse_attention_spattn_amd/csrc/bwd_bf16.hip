@@ -35,7 +35,7 @@ struct BwdArgs {
   const bf16* o;
   const bf16* dout;
   const float* lse;
-  float* dvec;  // D_i = dO_i . O_i: written by bwd_dq, read by bwd_dkdv
+  float* dvec;  // -D_i = -dO_i . O_i: written by bwd_dq, read by bwd_dkdv
   float* nl2;   // -LSE_i * log2(e): written by bwd_dq, read by bwd_dkdv
   void* dq;
   void* dk;
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
     }
   }
   if (row_ok && g == 0) {
-    p.dvec[sh.row0 + iq] = dval;
+    p.dvec[sh.row0 + iq] = -dval;
     p.nl2[sh.row0 + iq] = nlse2;
   }
   const float sl2 = p.scale_log2;
@@ -425,7 +425,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         out[12 + e] = d[e];
       }
     };
-    // dS wave, visit v (one iteration late): dS = P (dP - D) and
+    // dS wave, visit v (one iteration late): dS = P (dP - D), dP - D coming
+    // straight out of the dP chain, and
     // dK^T += Q^T dS (the scale is applied to dK once, at the store).  P comes masked from the P wave (0 outside the band and
     // on rows past N), so no mask is needed here.
     auto ds_dk = [&](int v, const f32x16& dpv) {
@@ -437,14 +438,13 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         bb[2 * dt] = kmajor_operand<D>(qs, 0, 32 * dt, lane);
         bb[2 * dt + 1] = kmajor_operand<D>(qs, 16, 32 * dt, lane);
       }
-      float dd[16], ds[16];
-      rows16(&rowv[st][wave][kKvQB], dd);
+      float ds[16];
       const f16x8 pa = *(const f16x8*)&pbuf[v & 1][kw][0][lane][0];
       const f16x8 pb = *(const f16x8*)&pbuf[v & 1][kw][1][lane][0];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        ds[i] = (float)pa[i] * (dpv[i] - dd[i]);
-        ds[8 + i] = (float)pb[i] * (dpv[8 + i] - dd[8 + i]);
+        ds[i] = (float)pa[i] * dpv[i];
+        ds[8 + i] = (float)pb[i] * dpv[8 + i];
       }
       const bf16x8 op0 = pack8(&ds[0]), op1 = pack8(&ds[8]);
       __builtin_amdgcn_sched_barrier(0);
@@ -473,10 +473,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
     };
     // sum over kk of a[kk] x b[kk] as one dependent chain, with the prefetch
     // of visit v after the first half of the products
-    auto chain_with_prefetch = [&](const bf16x8* a, int v) {
+    // init: the accumulator's starting value (0 for S; -D of the block's rows
+    // for dP, so the chain ends at dP - D)
+    auto chain_with_prefetch = [&](const bf16x8* a, int v, const float* init) {
       f32x16 c;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = 0.f;
+      for (int i = 0; i < 16; ++i) c[i] = init[i];
 #pragma unroll
       for (int kk = 0; kk < kKK / 2; ++kk) c = mfma32(a[kk], bop[kk], c);
       prefetch(v);
@@ -529,7 +531,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         bf16x8 aa[kKK];
         load_ka<D>(aa, qs, off, 0);
         __builtin_amdgcn_sched_barrier(0);
-        const f32x16 sc_ = chain_with_prefetch(aa, v);
+        const float zero16[16] = {};
+        const f32x16 sc_ = chain_with_prefetch(aa, v, zero16);
         __builtin_amdgcn_sched_barrier(0);
         float nl[16], pv[16];
         rows16(&rowv[s][wave][0], nl);
@@ -605,8 +608,10 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         bf16x8 aa[kKK];
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) aa[kk] = row_chunk<D>(dos, prow, 16 * kk + 8 * g);
+        float nd[16];  // -D of the block's rows (visit v has landed)
+        rows16(&rowv[v % kKvStages][wave][kKvQB], nd);
         __builtin_amdgcn_sched_barrier(0);
-        dp_new = chain_with_prefetch(aa, v);
+        dp_new = chain_with_prefetch(aa, v, nd);
         if constexpr (decltype(has_prev)::value) ds_dk(v - 1, dp_old);
       };
       f32x16 dpa, dpb;
