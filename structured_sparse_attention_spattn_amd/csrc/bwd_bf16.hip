@@ -179,7 +179,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   }
   const float sl2 = p.scale_log2;
   const float scl = p.scale;
-  const float ndsc = -dval * scl;
+  // -D in every register of a 32 x 32 accumulator: the dP^T chain starts
+  // from it (as its first product's C operand), so it ends at dP - D
+  f32x16 nd16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) nd16[i] = -dval;
 #pragma unroll
   for (int kk = 0; kk < kKK; ++kk) {
     settle(qreg[kk]);
@@ -230,9 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) opa[kk] = *(const bf16x8*)((const char*)vs + off.k[kk]);
         __builtin_amdgcn_sched_barrier(0);
-        f32x16 pacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pacc[i] = 0.f;
+        f32x16 pacc = nd16;
         float pe[16];
         // fixed order: one dP^T product, then its share of the exponentials
 #pragma unroll
@@ -246,11 +248,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
         // K^T operands of dQ^T += K^T dS^T, in flight during the dS math
         bf16x8 kt[2 * kDT];
         load_va<D>(kt, ks, off, 0);
-        // dS = P (dP - D) scale, with (dP - D) scale as one FMA; on a partial
-        // tile the band is applied by selection (P may overflow out of band)
+        // dS = P (dP - D), the scale applied to dQ once at the store; on a
+        // partial tile the band is applied by selection (P may overflow out
+        // of band)
         float ds[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ds[i] = pe[i] * __builtin_fmaf(pacc[i], scl, ndsc);
+        for (int i = 0; i < 16; ++i) ds[i] = pe[i] * pacc[i];
         if (!full) {
           const int mb = iq - jb - 8 * g - lo;  // (iq - key - lo) + c for register i
           const uint32_t width = (uint32_t)(hi - lo);
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
   if (wave_live) {
     float* stg = (float*)smem + wave * 32 * D;
-    stage_transposed<D>(stg, acc, 1.f, lane);
+    stage_transposed<D>(stg, acc, scl, lane);  // dQ = scale sum dS K
     store_staged<D>(stg, p.dq, sh.row0 + iw0, min(32, N - iw0), p.grad_f32 != 0, lane);
   }
 }
