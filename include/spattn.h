@@ -17,8 +17,10 @@
  * - Every function returns an int status (enum spattn_status); nothing throws
  *   across this boundary.
  * - Tensors are caller-owned DEVICE pointers to contiguous row-major
- *   [B, H, N, d] arrays (batch, head, position, feature).  LSE and the
- *   backward D vector are [B, H, N] float32.  Band arrays are HOST pointers.
+ *   [B, H, N, d] arrays (batch, head, position, feature), 16-byte aligned
+ *   (rows are moved in 16-byte pieces).  LSE is [B, H, N] float32; LSE,
+ *   decode lengths and cu_seqlens are 4-byte aligned.  A null or misaligned
+ *   pointer is SPATTN_E_ARG.  Band arrays are HOST pointers.
  * - dtype codes: SPATTN_F32 = 0 (float32 everywhere), SPATTN_BF16 = 1
  *   (bfloat16 storage, float32 accumulation).  Head size d must be 64 or 128.
  * - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls
@@ -42,7 +44,7 @@ extern "C" {
 
 enum spattn_status {
   SPATTN_OK = 0,
-  SPATTN_E_ARG = 1,          /* null pointer, size out of range, bad band */
+  SPATTN_E_ARG = 1,          /* null or misaligned pointer, size out of range, bad band */
   SPATTN_E_UNSUPPORTED = 2,  /* head size / dtype combination not built */
   SPATTN_E_HIP = 3,          /* the HIP runtime refused the launch */
   SPATTN_E_WORKSPACE = 4     /* backward workspace too small */

@@ -67,6 +67,11 @@ int check_sizes(int B, int H, int N, int d, int dtype) {
 
 float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
 
+// The kernels move tensor rows in 16-byte pieces and row vectors / index
+// arrays in 4-byte ones: a null or misaligned pointer is an argument error.
+bool tensor_ptr(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+bool vec_ptr(const void* p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
+
 // Query-major tile list of one band, computed with the forward kernel's
 // scheduler (band_key_span + tile_full) by a single workgroup.
 __global__ __launch_bounds__(256) void tile_list_kernel(int N, int lo, int hi, int BQ, int BK, int32_t* row_ptr,
@@ -122,7 +127,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, void* o, float*
                     int32_t local_window, float scale, void* stream) {
   int st = check_sizes(B, H, N, d, dtype);
   if (st != SPATTN_OK) return st;
-  if (!q || !k || !v || !o || !lse || local_window < 0) return SPATTN_E_ARG;
+  if (!tensor_ptr(q) || !tensor_ptr(k) || !tensor_ptr(v) || !tensor_ptr(o) || !vec_ptr(lse) || local_window < 0)
+    return SPATTN_E_ARG;
   Bands bands;
   st = make_bands(N, H, band_lo, band_hi, &bands);
   if (st != SPATTN_OK) return st;
@@ -171,7 +177,9 @@ int spattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, co
   Bands bands;
   int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
   if (st != SPATTN_OK) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dq) return SPATTN_E_ARG;
+  if (!tensor_ptr(q) || !tensor_ptr(k) || !tensor_ptr(v) || !tensor_ptr(o) || !vec_ptr(lse) || !tensor_ptr(dout) ||
+      !tensor_ptr(dq))
+    return SPATTN_E_ARG;
   return launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, 0,
                        resolve_scale(scale, d), kFixed, workspace, (hipStream_t)stream);
 }
@@ -183,7 +191,9 @@ int spattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* ls
   Bands bands;
   int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
   if (st != SPATTN_OK) return st;
-  if (!q || !k || !v || !lse || !dout || !dk || !dv) return SPATTN_E_ARG;
+  if (!tensor_ptr(q) || !tensor_ptr(k) || !tensor_ptr(v) || !vec_ptr(lse) || !tensor_ptr(dout) || !tensor_ptr(dk) ||
+      !tensor_ptr(dv))
+    return SPATTN_E_ARG;
   return launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, B, H, N, d, dtype, grad_dtype, bands, 0,
                          resolve_scale(scale, d), kFixed, workspace, (hipStream_t)stream);
 }
@@ -195,7 +205,9 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   Bands bands;
   int st = bwd_check(B, H, N, d, dtype, grad_dtype, band_lo, band_hi, workspace, workspace_bytes, &bands);
   if (st != SPATTN_OK) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || local_window < 0) return SPATTN_E_ARG;
+  if (!tensor_ptr(q) || !tensor_ptr(k) || !tensor_ptr(v) || !tensor_ptr(o) || !vec_ptr(lse) || !tensor_ptr(dout) ||
+      !tensor_ptr(dq) || !tensor_ptr(dk) || !tensor_ptr(dv) || local_window < 0)
+    return SPATTN_E_ARG;
   const float sc = resolve_scale(scale, d);
   const int w = local_window < N ? local_window : N;
   st = launch_bwd_dq(q, k, v, o, lse, dout, dq, B, H, N, d, dtype, grad_dtype, bands, w, sc, kFixed, workspace,
@@ -246,7 +258,8 @@ int spattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, floa
   int st = varlen_check(cu_seqlens, n_seqs, max_seqlen, total, H, d, dtype, band_lo, band_hi, local_window, &bands,
                         &pk);
   if (st != SPATTN_OK) return st;
-  if (!q || !k || !v || !o || !lse) return SPATTN_E_ARG;
+  if (!tensor_ptr(q) || !tensor_ptr(k) || !tensor_ptr(v) || !tensor_ptr(o) || !vec_ptr(lse) || !vec_ptr(cu_seqlens))
+    return SPATTN_E_ARG;
   const float sc = resolve_scale(scale, d);
   const int w = local_window < max_seqlen ? local_window : max_seqlen;
   if (dtype == SPATTN_BF16)
@@ -268,7 +281,9 @@ int spattn_bwd_varlen(const void* q, const void* k, const void* v, const void* o
   const size_t need = bwd_workspace_bytes(1, H, total, d, dtype, grad_dtype);
   if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
     return SPATTN_E_WORKSPACE;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPATTN_E_ARG;
+  if (!tensor_ptr(q) || !tensor_ptr(k) || !tensor_ptr(v) || !tensor_ptr(o) || !vec_ptr(lse) || !tensor_ptr(dout) ||
+      !tensor_ptr(dq) || !tensor_ptr(dk) || !tensor_ptr(dv) || !vec_ptr(cu_seqlens))
+    return SPATTN_E_ARG;
   const float sc = resolve_scale(scale, d);
   const int w = local_window < max_seqlen ? local_window : max_seqlen;
   st = launch_bwd_dq(q, k, v, o, lse, dout, dq, n_seqs, H, max_seqlen, d, dtype, grad_dtype, bands, w, sc, pk,
@@ -283,7 +298,9 @@ int spattn_decode(const void* q, const void* k_cache, const void* v_cache, void*
                   const int32_t* band_lo, const int32_t* band_hi, int32_t local_window, float scale, void* stream) {
   int st = check_sizes(B, H, Nmax, d, dtype);
   if (st != SPATTN_OK) return st;
-  if (!q || !k_cache || !v_cache || !o || !lse || local_window < 0) return SPATTN_E_ARG;
+  if (!tensor_ptr(q) || !tensor_ptr(k_cache) || !tensor_ptr(v_cache) || !tensor_ptr(o) || !vec_ptr(lse) ||
+      (lengths != nullptr && !vec_ptr(lengths)) || local_window < 0)
+    return SPATTN_E_ARG;
   Bands bands;
   st = make_bands(Nmax, H, band_lo, band_hi, &bands);
   if (st != SPATTN_OK) return st;

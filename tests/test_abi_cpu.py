@@ -210,3 +210,27 @@ def test_varlen_validation_before_launch():
     assert bwd(nbytes=16) == _lib.E_WORKSPACE
     assert bwd(gdt=7) == _lib.E_UNSUPPORTED
     assert bwd(ptr=ctypes.c_void_p(0)) == _lib.E_ARG
+
+
+def test_misaligned_pointers_rejected_before_launch():
+    """Tensor pointers must be 16-byte aligned, LSE / lengths / cu_seqlens
+    4-byte aligned: one misaligned pointer (all others aligned) is E_ARG,
+    checked before anything is launched."""
+    lib = _lib.load()
+    A = 1 << 20  # aligned stand-in addresses, never dereferenced: each call below fails validation
+    P = lambda off=0: ctypes.c_void_p(A + off)
+    for i in range(5):
+        args = [P(), P(), P(), P(), P()]
+        args[i] = P(8 if i < 4 else 2)
+        assert lib.spattn_fwd(*args, 1, 2, 64, 64, _lib.BF16, None, None, 0.0, None) == _lib.E_ARG, i
+    need = lib.spattn_bwd_workspace_bytes(1, 2, 64, 64, _lib.BF16, _lib.BF16)
+    ws = ctypes.c_void_p(A)
+    for i in range(9):
+        args = [P() for _ in range(9)]
+        args[i] = P(2 if i == 4 else 8)  # index 4 is LSE
+        assert lib.spattn_bwd(*args, 1, 2, 64, 64, _lib.BF16, _lib.BF16, None, None, 0.0, ws, need,
+                              None) == _lib.E_ARG, i
+    assert lib.spattn_decode(P(), P(), P(), P(), P(), P(2), 1, 2, 64, 64, _lib.BF16, None, None, 0, 0.0,
+                             None) == _lib.E_ARG
+    assert lib.spattn_fwd_varlen(P(), P(), P(), P(), P(), P(2), 2, 8, 12, 2, 64, _lib.BF16, None, None, 0, 0.0,
+                                 None) == _lib.E_ARG
