@@ -333,12 +333,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   using Tile = AsyncTile<kKvQB, D, kWaves>;
   constexpr int kL = 2 * Tile::kPer + 1;  // loads per wave per stage (Q, dO, LSE|D)
   __shared__ __attribute__((aligned(16))) bf16 smem[kKvStages * 2 * kTile];  // [stage][Q, dO]
-  // [stage][wave][LSE of the 32 rows | D of the 32 rows]: every wave loads its own copy
+  // [stage][wave][-LSE log2(e) of the 32 rows | -D of the 32 rows]: every
+  // wave loads its own copy
   __shared__ __attribute__((aligned(16))) float rowv[kKvStages][kWaves][2 * kKvQB];
-  // P from P wave w to dS wave w + kKvPairs: [block parity][w][lane][16 values]
-  // [block parity][pair][half][lane]: each half of a lane's 16 values is one
-  // 1 KB contiguous row of 16-byte pieces, so writes and reads are single
-  // conflict-free sweeps.
+  // P from P wave w to dS wave w + kKvPairs, [block parity][pair][half][lane]:
+  // each half of a lane's 16 values is one 1 KB contiguous row of 16-byte
+  // pieces, so writes and reads are single conflict-free sweeps.
   __shared__ __attribute__((aligned(16))) f16 pbuf[2][kKvPairs][2][64][8];
 
   const int tid = threadIdx.x;
@@ -388,6 +388,21 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   // query blocks to visit, in order; visit v sits in ring stage v % kKvStages
   const TileWalk walk = tile_walk(band_query_span(j0, j1, lo, hi, N), qspan2, kKvQB);
   const int n_visit = walk.n;
+  // Stepped schedule.  The second key pair (keys 32 .. 63 of the tile) never
+  // needs the walk's first query block when the first pair never needs its
+  // last: the second pair then runs one block ahead of the first and the
+  // workgroup takes n_visit - 1 steps instead of n_visit, with no step spent
+  // on a block that misses a pair's keys.  Step t: this wave's visit is
+  // t + voff; waits, barriers and ring loads follow the step.
+  bool shifted = false;
+  if (n_visit >= 2 && j0 + 32 <= N - 1 && !(TWO && has_second(dset))) {
+    const int a1 = j0 + 31, b0 = j0 + 32, b1 = min(N - 1, j0 + 63);
+    const int f0 = walk.at(0) * kKvQB, f1 = min(N - 1, f0 + kKvQB - 1);
+    const int l0 = walk.at(n_visit - 1) * kKvQB, l1 = min(N - 1, l0 + kKvQB - 1);
+    shifted = !tile_meets(f0, f1, b0, b1, lo, hi) && !tile_meets(l0, l1, j0, a1, lo, hi);
+  }
+  const int n_step = shifted ? n_visit - 1 : n_visit;
+  const int voff = shifted && kw == 1 ? 1 : 0;
   if (n_visit > 0) {
     const float sl2 = p.scale_log2;
     const float scl = p.scale;
@@ -457,34 +472,35 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(bb[2 * dt + 1], op1, acc[dt]);
     };
 
-    // Top of every iteration, for both roles (same barrier sequence): wait for
-    // this wave's loads of visit v (those of v + 1 may stay in flight), then
-    // the barrier -- visit v complete for everyone, iteration v - 1 finished
-    // everywhere, so the stage of visit v - 2 is free and the P of visit
-    // v - 1 is visible -- then prefetch visit v + kKvAhead.
-    auto block_start = [&](int v) {
-      if (v + 1 < n_visit)
+    // Top of every step t, for both roles (same barrier sequence): wait for
+    // this wave's loads of the visits step t uses -- visit t (those of t + 1
+    // may stay in flight), or t + 1 on the stepped schedule (nothing in
+    // flight) -- then the barrier: those visits complete for everyone, step
+    // t - 1 finished everywhere, so the stage of visit t - 2 is free and the
+    // P of the previous visit is visible; then visit t + kKvAhead is loaded.
+    auto block_start = [&](int t) {
+      if (!shifted && t + 1 < n_step)
         wait_vmcnt<kL>();
       else
         wait_vmcnt<0>();
       __syncthreads();
     };
-    // The ring loads of visit v + kKvAhead are issued in the middle of a
+    // The ring loads of visit t + kKvAhead are issued in the middle of a
     // dependent MFMA chain (score or dP), whose stalls absorb their issue cost.
-    auto prefetch = [&](int v) {
-      if (v + kKvAhead < n_visit) issue(v + kKvAhead);
+    auto prefetch = [&](int t) {
+      if (t + kKvAhead < n_visit) issue(t + kKvAhead);
     };
     // sum over kk of a[kk] x b[kk] as one dependent chain, with the prefetch
-    // of visit v after the first half of the products
+    // of step t after the first half of the products
     // init: the accumulator's starting value (0 for S; -D of the block's rows
     // for dP, so the chain ends at dP - D)
-    auto chain_with_prefetch = [&](const bf16x8* a, int v, const float* init) {
+    auto chain_with_prefetch = [&](const bf16x8* a, int t, const float* init) {
       f32x16 c;
 #pragma unroll
       for (int i = 0; i < 16; ++i) c[i] = init[i];
 #pragma unroll
       for (int kk = 0; kk < kKK / 2; ++kk) c = mfma32(a[kk], bop[kk], c);
-      prefetch(v);
+      prefetch(t);
 #pragma unroll
       for (int kk = kKK / 2; kk < kKK; ++kk) c = mfma32(a[kk], bop[kk], c);
       return c;
@@ -515,8 +531,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       };
       // within-tile row offset of accumulator register i, less 8 g
       auto creg = [](int i) { return ((i >> 3) << 4) + (i & 7); };
-      auto p_block = [&](int v, auto has_prev) {
-        block_start(v);
+      auto p_block = [&](int t, auto has_prev) {
+        block_start(t);
+        const int v = t + voff;
         off.refresh();
         const int s = v % kKvStages;
         const bf16* qs = smem + s * 2 * kTile;
@@ -535,7 +552,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         load_ka<D>(aa, qs, off, 0);
         __builtin_amdgcn_sched_barrier(0);
         const float zero16[16] = {};
-        const f32x16 sc_ = chain_with_prefetch(aa, v, zero16);
+        const f32x16 sc_ = chain_with_prefetch(aa, t, zero16);
         __builtin_amdgcn_sched_barrier(0);
         float nl[16], pv[16];
         rows16(&rowv[s][wave][0], nl);
@@ -590,11 +607,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         pp1 = pack8(&pv[8]);
       };
       p_block(0, std::false_type{});
-      for (int v = 1; v < n_visit; ++v) p_block(v, std::true_type{});
+      for (int t = 1; t < n_step; ++t) p_block(t, std::true_type{});
       __syncthreads();  // matches the dS waves' final barrier
       {
         bf16x8 bb[2 * kDT];
-        dv_operands(n_visit - 1, bb);
+        dv_operands(n_step - 1 + voff, bb);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32(bb[2 * dt], pp0, acc[dt]);
@@ -605,8 +622,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
       // dP of block v into dp_new, then dS and dK of block v - 1 from dp_old;
       // the two dP registers alternate (loop unrolled by two), so nothing is
       // copied between blocks.
-      auto d_block = [&](int v, f32x16& dp_new, const f32x16& dp_old, auto has_prev) {
-        block_start(v);
+      auto d_block = [&](int t, f32x16& dp_new, const f32x16& dp_old, auto has_prev) {
+        block_start(t);
+        const int v = t + voff;
         const bf16* dos = smem + (v % kKvStages) * 2 * kTile + kTile;
         bf16x8 aa[kKK];
 #pragma unroll
@@ -614,23 +632,23 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         float nd[16];  // -D of the block's rows (visit v has landed)
         rows16(&rowv[v % kKvStages][wave][kKvQB], nd);
         __builtin_amdgcn_sched_barrier(0);
-        dp_new = chain_with_prefetch(aa, v, nd);
+        dp_new = chain_with_prefetch(aa, t, nd);
         if constexpr (decltype(has_prev)::value) ds_dk(v - 1, dp_old);
       };
       f32x16 dpa, dpb;
       d_block(0, dpa, dpb, std::false_type{});
-      int v = 1;
-      for (; v + 1 < n_visit; v += 2) {
-        d_block(v, dpb, dpa, std::true_type{});
-        d_block(v + 1, dpa, dpb, std::true_type{});
+      int t = 1;
+      for (; t + 1 < n_step; t += 2) {
+        d_block(t, dpb, dpa, std::true_type{});
+        d_block(t + 1, dpa, dpb, std::true_type{});
       }
-      if (v < n_visit) {
-        d_block(v, dpb, dpa, std::true_type{});
+      if (t < n_step) {
+        d_block(t, dpb, dpa, std::true_type{});
         __syncthreads();  // P of the last block visible
-        ds_dk(v, dpb);
+        ds_dk(t + voff, dpb);
       } else {
         __syncthreads();  // P of the last block visible
-        ds_dk(v - 1, dpa);
+        ds_dk(t - 1 + voff, dpa);
       }
     }
   }
