@@ -8,8 +8,9 @@
 //
 // Two deterministic kernels, no atomics:
 //   bwd_dq    query-major, one workgroup per (b, h, 128 query rows), 4 waves
-//             of 32 rows.  Computes D for its rows (written for the second
-//             kernel), then walks the 32-key tiles of its band strip:
+//             of 32 rows.  Computes D for its rows (-D and -LSE log2(e) are
+//             written for the second kernel), then walks the 32-key tiles of
+//             its band strip:
 //             S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T (K^T is
 //             read from the row-major K tile with the LDS transpose read).
 //   bwd_dkdv  key-major, one workgroup per (b, h, 64 key rows), 4 waves in
@@ -17,7 +18,8 @@
 //             keys: S = Q K^T and dV += P^T dO in one wave of a pair, dP = dO V^T,
 //             dS and dK += dS^T Q in the other, dK / dV held in registers for
 //             the whole walk (dO and Q enter the last two products through the
-//             LDS transpose read).
+//             LDS transpose read).  When the two pairs' query blocks are offset
+//             by one, the second pair runs a block ahead (stepped schedule).
 // Both recompute P from the saved LSE with the same band-tile enumeration as
 // the forward pass and mask element-wise only on tiles that are not FULL.
 #include "common.h"
@@ -85,7 +87,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const int lo = dset.lo;
   const int hi = dset.hi;
   // Query tiles without keys (a prefix of the tiles) only get zero rows of dQ
-  // and D (D = 0 keeps a later dK/dV block that overlaps these rows finite):
+  // and of the two row vectors (finite values keep a later dK/dV block that
+  // overlaps these rows finite):
   // the first of every kZeroGroup of them writes the group, the others exit.
   {
     const int md = min_dist(dset, N);
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   constexpr int kKK = D / 16;
   constexpr int kDT = D / 32;
   using Tile = AsyncTile<kKvQB, D, kWaves>;
-  constexpr int kL = 2 * Tile::kPer + 1;  // loads per wave per stage (Q, dO, LSE|D)
+  constexpr int kL = 2 * Tile::kPer + 1;  // loads per wave per stage (Q, dO, row values)
   __shared__ __attribute__((aligned(16))) bf16 smem[kKvStages * 2 * kTile];  // [stage][Q, dO]
   // [stage][wave][-LSE log2(e) of the 32 rows | -D of the 32 rows]: every
   // wave loads its own copy
