@@ -421,6 +421,15 @@ def cpu_baseline(inp, lo, hi, flops_all):
     t0 = time.perf_counter()
     oracle.band_attention_bwd(q, k, v, do, lo, hi)  # includes the forward recompute
     dt = time.perf_counter() - t0
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(flops_all / dt / 1e12, 5),
         "unit": "TFLOP/s",
@@ -428,7 +437,9 @@ def cpu_baseline(inp, lo, hi, flops_all):
         "kind": "oracle",
         "sample": "whole workload (B=8 H=16 N=4096 d=128), float64 numpy, fwd+bwd",
         "seconds": round(dt, 2),
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": model,
+        "cpu_count": os.cpu_count(),
+        "affinity": len(os.sched_getaffinity(0)),
     }
 
 
