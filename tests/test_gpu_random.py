@@ -70,3 +70,25 @@ def test_random_shape_fwd_bwd(seed):
         assert err <= tol, f"{nm}: max-abs {err:.3e}"
         if dtype == "bf16" and np.linalg.norm(ref) > 0:  # and 1e-2 relative L2
             assert np.linalg.norm(g - ref) / np.linalg.norm(ref) <= 1e-2, f"{nm}: relative L2"
+
+
+@pytest.mark.parametrize("B,H,N,d,w", [(1, 256, 300, 64, 0), (1, 200, 1000, 128, 8)])
+def test_many_heads(B, H, N, d, w):
+    """Up to the ABI's 256 heads: the per-head band table travels in the kernel
+    arguments; width-1 and width-2 bands (N / H < 4)."""
+    _say(f"many heads B={B} H={H} N={N} d={d} w={w}")
+    inp = make_inputs(B, H, N, d, dtype="bf16", seed=H + N, with_dout=True)
+    dv_ = {k: v.to(DEV) for k, v in inp.items()}
+    o, lse = ops.fwd(dv_["q"], dv_["k"], dv_["v"], local_window=w)
+    dq, dk, dv = ops.bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dv_["dout"], local_window=w, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    lo, hi = oracle.band_table(N, H)
+    rq, rk, rv, ro, rl = oracle.band_attention_bwd(*(as_f64(inp[n]) for n in ("q", "k", "v", "dout")), lo, hi,
+                                                   local_window=w)
+    lse_h = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(lse_h), np.isneginf(rl))
+    fin = ~np.isneginf(rl)
+    assert np.max(np.abs(lse_h[fin] - rl[fin])) <= 2e-2
+    for got, ref, nm in ((o, ro, "O"), (dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        err = float(np.max(np.abs(got.float().cpu().numpy() - ref)))
+        assert err <= 2e-2, f"{nm}: max-abs {err:.3e}"
