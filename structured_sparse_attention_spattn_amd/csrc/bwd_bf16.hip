@@ -408,7 +408,6 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   const int voff = shifted && kw == 1 ? 1 : 0;
   if (n_visit > 0) {
     const float sl2 = p.scale_log2;
-    const float scl = p.scale;
     auto issue = [&](int v) {
       const int st = v % kKvStages;
       const int tq = walk.at(v);
@@ -638,7 +637,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
         dp_new = chain_with_prefetch(aa, t, nd);
         if constexpr (decltype(has_prev)::value) ds_dk(v - 1, dp_old);
       };
-      f32x16 dpa, dpb;
+      f32x16 dpa, dpb{};  // dpb: unused by the first block (no previous one)
       d_block(0, dpa, dpb, std::false_type{});
       int t = 1;
       for (; t + 1 < n_step; t += 2) {
