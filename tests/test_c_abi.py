@@ -1,0 +1,40 @@
+"""The C ABI from plain C: tests/c/abi_host.c is compiled with gcc against
+include/spattn.h, linked with libspattn.so and run (host-side calls only, no
+GPU needed).  The band table must match the Balanced Distance Partitioning
+instance of "Making Every Head Count" (Figure 1 caption: N = 1024, H = 8,
+bands of 128 distances, head 0 nearest)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from structured_sparse_attention_spattn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="no C compiler")
+def test_c_program_uses_the_abi(tmp_path):
+    lib = _lib.load()  # builds are in-tree; fails loudly if the library is missing
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    exe = tmp_path / "abi_host"
+    hip_lib = "/opt/rocm/lib"
+    cmd = ["gcc", "-std=c11", "-O1", "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c", "abi_host.c"),
+           "-o", str(exe), "-L", libdir, "-l:libspattn.so", f"-Wl,-rpath,{libdir}"]
+    if os.path.isdir(hip_lib):
+        cmd += [f"-Wl,-rpath,{hip_lib}", f"-Wl,-rpath-link,{hip_lib}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    lines = dict(l.split(" ", 1) for l in out.stdout.strip().splitlines())
+    want = "0 " + " ".join(f"[{128 * h},{128 * h + 127}]" for h in range(8))
+    assert lines["band_table"] == want
+    assert lines["band_table_uneven"] == "0 [0,3] [4,6] [7,9]"
+    assert lines["band_table_bad"] == str(_lib.E_ARG)
+    assert int(lines["workspace"]) == lib.spattn_bwd_workspace_bytes(2, 3, 100, 128, _lib.BF16, _lib.BF16) > 0
+    assert lines["workspace_bad"] == "0"
+    assert lines["tiles"].split()[0] == "0"
+    assert lines["fwd_misaligned"].split()[0] == str(_lib.E_ARG)
+    assert lines["fwd_d96"].split()[0] == str(_lib.E_UNSUPPORTED)
