@@ -74,12 +74,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const int total = p.B * p.H * p.n_tiles;
-  const int item = xcd_remap(blockIdx.x, total);
-  const int t = item % p.n_tiles;
-  const int bh = item / p.n_tiles;
-  const int h = bh % p.H;
-  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, bh / p.H, h);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  if (!wi.valid) return;  // padding pair
+  const int t = wi.t;
+  const int h = wi.h;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, wi.b, h);
   const int N = sh.n;
   if (t * kDqBQ >= N) return;  // past the end of a packed sequence
   // the head's distance set: its band, joined with the local window if any
@@ -352,12 +351,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const int total = p.B * p.H * p.n_tiles;
-  const int item = xcd_remap(blockIdx.x, total);
-  const int ut = item % p.n_tiles;
-  const int bh = item / p.n_tiles;
-  const int h = bh % p.H;
-  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, bh / p.H, h);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  if (!wi.valid) return;  // padding pair
+  const int ut = wi.t;
+  const int h = wi.h;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, wi.b, h);
   const int N = sh.n;
   if (ut * kKvBK >= N) return;  // past the end of a packed sequence
   // the head's distance set: its band, joined with the local window if any
@@ -710,7 +708,7 @@ int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* 
   BwdArgs a = make_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, grad_f32, bands, scale, dvec, nl2, pk);
   a.n_tiles = (N + kDqBQ - 1) / kDqBQ;
   a.local_window = local_window;
-  const long long total = (long long)B * H * a.n_tiles;
+  const long long total = work_grid(B, H, a.n_tiles);
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   const dim3 grid((unsigned)total), block(kThreads);
   const bool two = local_window > 0;
@@ -731,7 +729,7 @@ int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const floa
   BwdArgs a = make_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, grad_f32, bands, scale, dvec, nl2, pk);
   a.n_tiles = (N + kKvBK - 1) / kKvBK;
   a.local_window = local_window;
-  const long long total = (long long)B * H * a.n_tiles;
+  const long long total = work_grid(B, H, a.n_tiles);
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   const dim3 grid((unsigned)total), block(kKvThreads);
   const bool two = local_window > 0;

@@ -617,4 +617,35 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// Work item of a launch over (sequence b, head h, row tile t).  With distance
+// bands ordered nearest first, a head's rows before its band start have no
+// keys, so the work of a (b, h) pair falls with h.  The pairs are ranked
+// heaviest first (h ascending, then b) and dealt to the 8 XCDs in
+// boustrophedon rounds: XCD x takes ranks x, 15 - x, 16 + x, 31 - x, ...,
+// each pair with all its tiles, as one contiguous run of that XCD's
+// workgroups (xcd_remap).  Every XCD then holds the same number of pairs, a
+// mix of heavy and light heads, in heavy-first order.  The pair count is
+// rounded up to a multiple of 8 (work_grid); items of the padding pairs have
+// valid == false.
+struct WorkItem {
+  int b, h, t;
+  bool valid;
+};
+__host__ __device__ __forceinline__ long long work_grid(int B, int H, int n_tiles) {
+  return 8LL * ((B * H + 7) / 8) * n_tiles;
+}
+__device__ __forceinline__ WorkItem work_item(int pid, int B, int H, int n_tiles) {
+  const int c = (B * H + 7) / 8;  // pairs per XCD
+  const int item = xcd_remap(pid, 8 * c * n_tiles);
+  const int m = item / n_tiles;
+  const int x = m / c, li = m % c;
+  const int k = 8 * li + ((li & 1) ? 7 - x : x);
+  WorkItem w;
+  w.b = k % B;
+  w.h = k / B;
+  w.t = item % n_tiles;
+  w.valid = k < B * H;
+  return w;
+}
+
 }  // namespace spattn

@@ -237,12 +237,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const int total = p.B * p.H * p.n_qt;
-  const int item = xcd_remap(blockIdx.x, total);
-  const int t = item % p.n_qt;
-  const int bh = item / p.n_qt;
-  const int h = bh % p.H;
-  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, bh / p.H, h);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_qt);
+  if (!wi.valid) return;  // padding pair
+  const int t = wi.t;
+  const int h = wi.h;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, wi.b, h);
   const int N = sh.n;
   if (t * kBQ >= N) return;  // past the end of a packed sequence
   // the head's distance set: its band, joined with the local window if any
@@ -376,7 +375,7 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   a.local_window = local_window;
   a.scale_log2 = scale * kLog2e;
   a.bands = bands;
-  const long long total = (long long)B * H * a.n_qt;
+  const long long total = work_grid(B, H, a.n_qt);
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   dim3 grid((unsigned)total), block(kThreads);
   const bool two = local_window > 0;
