@@ -324,7 +324,16 @@ def main():
                 "pct_peak": round(100 * tf / peak, 2), "peak_tflops": peak,
                 "hbm_frac_minimal_io": round(min_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             }
+            if w["dtype"] == "f32":
+                per_cfg[w["name"]].update(f32_backward(cq, ck, cv, co, cl, seed_for(idx) + 7, dev))
             del cq, ck, cv, co, cl, cinp
+        # the float32 backward where it is throughput-bound (no workload of its own)
+        fB, fH, fN, fd = 2, 16, 4096, 128
+        finp = make_inputs(fB, fH, fN, fd, dtype="f32", seed=4242)
+        fq, fk, fv = (finp[n].to(dev) for n in ("q", "k", "v"))
+        fo, fl = ops.fwd(fq, fk, fv)
+        per_cfg[f"bwd_f32_B{fB}_H{fH}_N{fN}_d{fd}"] = f32_backward(fq, fk, fv, fo, fl, 4243, dev)
+        del fq, fk, fv, fo, fl, finp
         out["configs"] = per_cfg
 
     if not args.no_variants:
@@ -404,6 +413,39 @@ def main():
         out["cpu_baseline"] = cpu_baseline(inp, lo, hi, fl_all)
 
     print(json.dumps(out), flush=True)
+
+
+def f32_backward(q, k, v, o, lse, seed, dev, reps=20):
+    """HIP-event times of the float32 backward stages on resident inputs
+    (dO seeded N(0, 1)); TFLOP/s counts 10 d per in-band pair."""
+    import torch
+    from structured_sparse_attention_spattn_amd import ops
+    B, H, N, d = q.shape
+    g = torch.Generator().manual_seed(seed)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float32).to(dev)
+    ws = torch.empty(ops.bwd_workspace_bytes(B, H, N, d, torch.float32, torch.float32), dtype=torch.uint8,
+                     device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    for _ in range(3):
+        ops.bwd_dq(q, k, v, o, lse, do, ws, out=dq)
+        ops.bwd_dkdv(q, k, v, lse, do, ws, out=(dk, dv))
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(reps):
+        ops.bwd_dq(q, k, v, o, lse, do, ws, out=dq)
+    ev[1].record()
+    for _ in range(reps):
+        ops.bwd_dkdv(q, k, v, lse, do, ws, out=(dk, dv))
+    ev[2].record()
+    torch.cuda.synchronize()
+    dq_ms, kv_ms = ev[0].elapsed_time(ev[1]) / reps, ev[1].elapsed_time(ev[2]) / reps
+    lo, hi = ops.band_table(N, H)
+    pairs = pairs_total(lo, hi, seq_len=N, batch=B)
+    tf = 10 * d * pairs / ((dq_ms + kv_ms) * 1e-3) / 1e12
+    return {"bwd_us": round((dq_ms + kv_ms) * 1e3, 2), "bwd_dq_us": round(dq_ms * 1e3, 2),
+            "bwd_dkdv_us": round(kv_ms * 1e3, 2), "bwd_tflops": round(tf, 2),
+            "bwd_pct_peak": round(100 * tf / FP32_PEAK_TFLOPS, 2)}
 
 
 def cpu_baseline(inp, lo, hi, flops_all):
