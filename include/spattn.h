@@ -96,7 +96,8 @@ int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * Bytes of device workspace spattn_bwd needs for these sizes: two float32
  * row vectors [B,H,N], each rounded up to 256 bytes: -D_i = -dO_i . O_i,
- * then -LSE_i log2(e), the exponent offset the dK/dV kernel recomputes P with.
+ * then -LSE_i log2(e), the exponent offset the bfloat16 dK/dV kernel
+ * recomputes P with (the float32 kernels leave the second vector unused).
  * Returns 0 for invalid sizes.
  */
 size_t spattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d,
@@ -209,8 +210,8 @@ int spattn_decode(const void* q, const void* k_cache, const void* v_cache, void*
  * The two stages spattn_bwd runs, exported for callers that schedule them
  * separately (and for per-kernel timing).  Same arguments and checks as
  * spattn_bwd; together they compute exactly what spattn_bwd computes.
- *   spattn_bwd_dq    writes -D_i = -dO_i . O_i (and -LSE_i log2(e)) into the
- *                    workspace, and dq.
+ *   spattn_bwd_dq    writes -D_i = -dO_i . O_i (and, for bfloat16 inputs,
+ *                    -LSE_i log2(e)) into the workspace, and dq.
  *   spattn_bwd_dkdv  reads them from the workspace and writes dk, dv; it must run
  *                    after spattn_bwd_dq with the same workspace, bands and
  *                    inputs, on the same stream (or after a synchronisation).

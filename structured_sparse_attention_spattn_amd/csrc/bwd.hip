@@ -5,38 +5,12 @@
 //     D_i = dO_i . O_i,  dP = dO V^T,  dS = P * (dP - D),
 //     dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
 //
-// This file holds the preprocess of the float32 path and the dispatcher; the
-// MFMA kernels are in bwd_bf16.hip and bwd_f32.hip.
-//   bwd_pre      D_i = dO_i . O_i for every row (float32 path only; the
-//                bfloat16 dQ kernel computes D from its own rows).
+// This file holds the workspace layout and the dispatch by dtype; the MFMA
+// kernels are in bwd_bf16.hip and bwd_f32.hip.  In both paths the dQ kernel
+// forms D_i for its own rows and stores -D_i for the dK/dV kernel.
 #include "common.h"
 
 namespace spattn {
-namespace {
-
-constexpr int kThreads = 256;
-
-// ------------------------------------------------------------ preprocess
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                           float* __restrict__ dvec, long long rows) {
-  constexpr int kLanes = D / 8;  // threads per row, 8 elements each
-  const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
-  const long long row = gid / kLanes;
-  const int part = (int)(gid % kLanes);
-  float s = 0.f;
-  if (row < rows) {
-    const T* po = o + row * D + part * 8;
-    const T* pd = dout + row * D + part * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s += (float)po[e] * (float)pd[e];
-  }
-#pragma unroll
-  for (int off = kLanes / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && part == 0) dvec[row] = -s;  // the workspace holds -D
-}
-
-}  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype) {
   (void)d;
@@ -49,12 +23,12 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype
 int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                        void* dq, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
                        float scale, float* dvec, float* nl2, const Packed& pk, hipStream_t stream);
-int launch_bwd_dq_f32(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
-                      int B, int H, int N, int d, const Bands& bands, int local_window, float scale,
-                      const float* dvec, const Packed& pk, hipStream_t stream);
+int launch_bwd_dq_f32(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                      void* dq, int B, int H, int N, int d, const Bands& bands, int local_window, float scale,
+                      float* dvec, const Packed& pk, hipStream_t stream);
 int launch_bwd_dkdv_f32(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                         void* dv, int B, int H, int N, int d, const Bands& bands, int local_window, float scale,
-                        const float* dvec, const Packed& pk, hipStream_t stream);
+                        float* dvec, const Packed& pk, hipStream_t stream);
 int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                          void* dv, int B, int H, int N, int d, bool grad_f32, const Bands& bands, int local_window,
                          float scale, float* dvec, float* nl2, const Packed& pk, hipStream_t stream);
@@ -76,19 +50,7 @@ int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, co
   if (dtype == SPATTN_BF16)
     return launch_bwd_dq_bf16(q, k, v, o, lse, dout, dq, B, H, N, d, grad_dtype == SPATTN_F32, bands, local_window,
                               scale, dvec, row_vector(workspace, 1, B, H, N, pk), pk, stream);
-  {
-    const long long data_rows = pk.cu != nullptr ? (long long)H * pk.T : (long long)B * H * N;  // rows held in the tensors
-    const long long threads = data_rows * (d / 8);
-    dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
-    if (d == 128)
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, block, 0, stream, (const float*)o, (const float*)dout,
-                         dvec, data_rows);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, block, 0, stream, (const float*)o, (const float*)dout,
-                         dvec, data_rows);
-    if (hipGetLastError() != hipSuccess) return SPATTN_E_HIP;
-  }
-  return launch_bwd_dq_f32(q, k, v, lse, dout, dq, B, H, N, d, bands, local_window, scale, dvec, pk, stream);
+  return launch_bwd_dq_f32(q, k, v, o, lse, dout, dq, B, H, N, d, bands, local_window, scale, dvec, pk, stream);
 }
 
 // Stage 2: dK and dV, reading D from the workspace written by stage 1.

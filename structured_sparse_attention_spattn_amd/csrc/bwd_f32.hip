@@ -5,8 +5,9 @@
 // distance bands of "Making Every Head Count" Figure 1):
 //     dP = dO V^T,  dS = P * (dP - D),
 //     dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
-// with P recomputed from the saved natural-log LSE and -D_i read from the
-// workspace (written by the preprocess kernel).
+// with P recomputed from the saved natural-log LSE.  The dQ kernels form
+// D_i = dO_i . O_i for their own rows and store -D_i in the workspace for the
+// dK/dV kernels.
 //
 // With a k-depth of 2 per product every operand is a single float, so both
 // orientations of a staged tile come straight from LDS: a lane reads along a
@@ -48,8 +49,9 @@ struct F32BwdArgs {
   const float* k;
   const float* v;
   const float* dout;
+  const float* o;  // dQ kernels only
   const float* lse;
-  const float* dvec;  // -D_i
+  float* dvec;  // -D_i: written by the dQ kernels, read by the dK/dV kernels
   float* dq;
   float* dk;
   float* dv;
@@ -79,6 +81,21 @@ __device__ __forceinline__ f32x16 zero16() {
 
 // Row of the 32x32 accumulator held in register r of a lane in half g.
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// -D_i = -(dO_i . O_i) for the row a lane pair holds: each half-wave has
+// features g * D/2 .. g * D/2 + D/2 - 1 of dO in registers and reads the same
+// features of O; the two halves are added across lanes l and l ^ 32.
+template <int D>
+__device__ __forceinline__ float neg_d(const float* __restrict__ orow, const f32x4* dreg, bool ok) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const f32x4 o4 = ok ? *(const f32x4*)(orow + 4 * c) : f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += o4[e] * dreg[c][e];
+  }
+  return -(s + __shfl_xor(s, 32));
+}
 
 // Nothing is scheduled across this point.
 __device__ __forceinline__ void fence_sched() { __builtin_amdgcn_sched_barrier(0); }
@@ -229,18 +246,22 @@ __global__ __launch_bounds__(64 * W) void bwd_f32_dq_kernel(F32BwdArgs p) {
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) acc[dt] = zero16();
 
-  if (walk.n > 0) {
-    f32x4 qreg[kKK / 4], dreg[kKK / 4];  // features g * D/2 .. g * D/2 + D/2 - 1 of row iq
+  f32x4 qreg[kKK / 4], dreg[kKK / 4];  // features g * D/2 .. g * D/2 + D/2 - 1 of row iq
 #pragma unroll
-    for (int c = 0; c < kKK / 4; ++c) {
-      const size_t at = base + (size_t)iq * D + g * kKK + 4 * c;
-      qreg[c] = row_ok ? *(const f32x4*)(p.q + at) : f32x4{0, 0, 0, 0};
-      dreg[c] = row_ok ? *(const f32x4*)(p.dout + at) : f32x4{0, 0, 0, 0};
-    }
+  for (int c = 0; c < kKK / 4; ++c)
+    dreg[c] = row_ok ? *(const f32x4*)(p.dout + base + (size_t)iq * D + g * kKK + 4 * c) : f32x4{0, 0, 0, 0};
+  // -D of every row, keys or not: the dK/dV kernel reads it for all rows of
+  // its query tiles
+  const float nd = neg_d<D>(p.o + base + (size_t)iq * D + g * kKK, dreg, row_ok);
+  if (row_ok && g == 0) p.dvec[sh.row0 + iq] = nd;
+
+  if (walk.n > 0) {
+#pragma unroll
+    for (int c = 0; c < kKK / 4; ++c)
+      qreg[c] = row_ok ? *(const f32x4*)(p.q + base + (size_t)iq * D + g * kKK + 4 * c) : f32x4{0, 0, 0, 0};
     // P = exp2(s * scale * log2(e) - LSE * log2(e)); rows past N use 0 (their
     // results are never stored).
     const float nl2 = row_ok ? -p.lse[sh.row0 + iq] * kLog2e : 0.f;
-    const float nd = row_ok ? p.dvec[sh.row0 + iq] : 0.f;
     const float sl2 = p.scale_log2;
 
     PairTile<D, kThr> st;
@@ -452,13 +473,250 @@ __global__ __launch_bounds__(64 * W) void bwd_f32_dkdv_kernel(F32BwdArgs p) {
   store_rows<D>(p.dv + base, dv, 1.f, jk, row_ok, g);
 }
 
-F32BwdArgs make_f32_args(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
-                         void* dk, void* dv, int B, int H, int N, const Bands& bands, int local_window, float scale,
-                         const float* dvec, const Packed& pk, int rows_per_tile) {
+// ------------------------------------------------------------ small launches
+// Too few 64-row tiles to occupy the chip: one workgroup per 32-row tile, and
+// its four waves split the tile's walk (wave w takes visits w, w + 4, ...),
+// each staging its own tiles in its own LDS area.  The partial gradients are
+// plain sums over the visited tiles, so the four are added through LDS in
+// wave order (deterministic) and the workgroup writes the rows once.
+constexpr int kSplitWaves = 4;
+constexpr int kSplitMaxTiles = 512;  // 64-row tiles below which the walk is split
+
+// Orders this wave's LDS accesses around a rewrite of its own area: LDS
+// instructions of one wave complete in order, so only the compiler's
+// ordering has to be pinned.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Rows [r0, r0 + 32) of a [rows, D] float tensor into an LDS tile of stride
+// kRow<D>, by the 64 lanes of one wave; rows past n are zero.
+template <int D>
+__device__ __forceinline__ void wave_stage(const float* __restrict__ src, float* dst, int r0, int n, int lane) {
+#pragma unroll
+  for (int r = 0; r < kT * D / 4 / 64; ++r) {
+    const int c = lane + 64 * r;
+    const int row = c / (D / 4), col = c % (D / 4);
+    const f32x4 x = r0 + row < n ? *(const f32x4*)(src + (size_t)(r0 + row) * D + col * 4) : f32x4{0, 0, 0, 0};
+    *(f32x4*)(dst + row * kRow<D> + col * 4) = x;
+  }
+}
+
+// Sum of the four waves' 32 x D accumulators (transposed as in store_rows)
+// times mul, written to rows row0 .. row0 + 31 (< n) of dst.  red holds
+// 4 * 32 * kRow<D> floats; the caller has synchronised the workgroup.
+template <int D>
+__device__ __forceinline__ void merge_rows(float* red, const f32x16* acc, float mul, float* __restrict__ dst,
+                                           int row0, int n, int tid) {
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+  float* mine = red + wave * kT * kRow<D>;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      f32x4 w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = acc[dt][4 * a + c];
+      *(f32x4*)(mine + c32 * kRow<D> + 32 * dt + 8 * a + 4 * g) = w;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kT * D / 4 / (64 * kSplitWaves); ++r) {
+    const int c = tid + 64 * kSplitWaves * r;
+    const int row = c / (D / 4), col = c % (D / 4);
+    f32x4 sum = *(const f32x4*)(red + row * kRow<D> + col * 4);
+#pragma unroll
+    for (int w = 1; w < kSplitWaves; ++w) sum += *(const f32x4*)(red + w * kT * kRow<D> + row * kRow<D> + col * 4);
+    if (row0 + row < n) *(f32x4*)(dst + (size_t)(row0 + row) * D + col * 4) = sum * mul;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kSplitWaves) void bwd_f32_dq_split_kernel(F32BwdArgs p) {
+  constexpr int kKK = D / 2;
+  constexpr int kDT = D / 32;
+  constexpr int kTensor = kT * kRow<D>;
+  constexpr int kArea = 2 * kTensor;  // one wave's K tile, then V tile
+  static_assert(kSplitWaves * kT * kRow<D> <= kSplitWaves * kArea, "merge area");
+  __shared__ __align__(16) float smem[kSplitWaves * kArea];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  if (!wi.valid) return;  // padding pair
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, wi.b, wi.h);
+  const int N = sh.n;
+  const int i0 = wi.t * kT;
+  if (i0 >= N) return;  // past the end of a packed sequence
+  const int i1 = min(N - 1, i0 + kT - 1);
+  const DistSet dset = dist_set(sh.lo, sh.hi, p.local_window);
+  const size_t base = sh.row0 * D;
+
+  KeySpan span2{0, -1};
+  if (has_second(dset)) span2 = band_key_span(i0, i1, dset.nlo, dset.nhi);
+  const TileWalk walk = tile_walk(band_key_span(i0, i1, dset.lo, dset.hi), span2, kT);
+
+  const int iq = i0 + c32;
+  const bool row_ok = iq < N;
+  f32x16 acc[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) acc[dt] = zero16();
+
+  f32x4 qreg[kKK / 4], dreg[kKK / 4];
+#pragma unroll
+  for (int c = 0; c < kKK / 4; ++c)
+    dreg[c] = row_ok ? *(const f32x4*)(p.dout + base + (size_t)iq * D + g * kKK + 4 * c) : f32x4{0, 0, 0, 0};
+  // -D of every row, keys or not (wave 0 stores it for the dK/dV kernel)
+  const float nd = neg_d<D>(p.o + base + (size_t)iq * D + g * kKK, dreg, row_ok);
+  if (wave == 0 && row_ok && g == 0) p.dvec[sh.row0 + iq] = nd;
+
+  if (walk.n > wave) {
+#pragma unroll
+    for (int c = 0; c < kKK / 4; ++c)
+      qreg[c] = row_ok ? *(const f32x4*)(p.q + base + (size_t)iq * D + g * kKK + 4 * c) : f32x4{0, 0, 0, 0};
+    const float nl2 = row_ok ? -p.lse[sh.row0 + iq] * kLog2e : 0.f;
+    const float sl2 = p.scale_log2;
+    float* ks = smem + wave * kArea;
+    float* vs = ks + kTensor;
+    for (int v = wave; v < walk.n; v += kSplitWaves) {
+      const int jb = walk.at(v) * kT;
+      wave_sync();
+      wave_stage<D>(p.k + base, ks, jb, N, lane);
+      wave_stage<D>(p.v + base, vs, jb, N, lane);
+      wave_sync();
+      if (!set_meets(i0, i1, jb, jb + kT - 1, dset)) continue;
+      f32x16 sacc = zero16(), pacc = zero16();
+      row_products<D>(ks + c32 * kRow<D> + g * kKK, vs + c32 * kRow<D> + g * kKK, qreg, dreg, sacc, pacc);
+      const bool full = set_full(i0, i1, jb, jb + kT - 1, dset);
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dist = iq - (jb + acc_row(r, g));
+        const bool in = full || (dist >= dset.lo && dist <= dset.hi) || (dist >= dset.nlo && dist <= dset.nhi);
+        const float pr = in ? fast_exp2(__builtin_fmaf(sacc[r], sl2, nl2)) : 0.f;
+        ds[r] = pr * (pacc[r] + nd);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt)
+          acc[dt] = mfma32_f32(ks[acc_row(r, g) * kRow<D> + 32 * dt + c32], ds[r], acc[dt]);
+    }
+  }
+  __syncthreads();  // every wave is done with its tile area
+  merge_rows<D>(smem, acc, p.scale, p.dq + base, i0, N, tid);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kSplitWaves) void bwd_f32_dkdv_split_kernel(F32BwdArgs p) {
+  constexpr int kKK = D / 2;
+  constexpr int kDT = D / 32;
+  constexpr int kTensor = kT * kRow<D>;
+  constexpr int kArea = 2 * kTensor + 2 * kT;  // one wave's Q tile, dO tile, -LSE*log2(e), -D
+  static_assert(kSplitWaves * kT * kRow<D> <= kSplitWaves * kArea, "merge area");
+  __shared__ __align__(16) float smem[kSplitWaves * kArea];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  if (!wi.valid) return;  // padding pair
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, wi.b, wi.h);
+  const int N = sh.n;
+  const int j0 = wi.t * kT;
+  if (j0 >= N) return;  // past the end of a packed sequence
+  const int j1 = min(N - 1, j0 + kT - 1);
+  const DistSet dset = dist_set(sh.lo, sh.hi, p.local_window);
+  const size_t base = sh.row0 * D;
+  const float* __restrict__ lb = p.lse + sh.row0;
+  const float* __restrict__ nb = p.dvec + sh.row0;
+
+  KeySpan span2{0, -1};
+  if (has_second(dset)) span2 = band_query_span(j0, j1, dset.nlo, dset.nhi, N);
+  const TileWalk walk = tile_walk(band_query_span(j0, j1, dset.lo, dset.hi, N), span2, kT);
+
+  const int jk = j0 + c32;
+  const bool row_ok = jk < N;
+  f32x16 dk[kDT], dv[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) {
+    dk[dt] = zero16();
+    dv[dt] = zero16();
+  }
+
+  if (walk.n > wave) {
+    f32x4 kreg[kKK / 4], vreg[kKK / 4];
+#pragma unroll
+    for (int c = 0; c < kKK / 4; ++c) {
+      const size_t at = base + (size_t)jk * D + g * kKK + 4 * c;
+      kreg[c] = row_ok ? *(const f32x4*)(p.k + at) : f32x4{0, 0, 0, 0};
+      vreg[c] = row_ok ? *(const f32x4*)(p.v + at) : f32x4{0, 0, 0, 0};
+    }
+    const float sl2 = p.scale_log2;
+    float* qs = smem + wave * kArea;
+    float* dos = qs + kTensor;
+    float* nls = qs + 2 * kTensor;
+    float* nds = nls + kT;
+    for (int v = wave; v < walk.n; v += kSplitWaves) {
+      const int ib = walk.at(v) * kT;
+      const int ie = min(N - 1, ib + kT - 1);
+      wave_sync();
+      wave_stage<D>(p.q + base, qs, ib, N, lane);
+      wave_stage<D>(p.dout + base, dos, ib, N, lane);
+      if (lane < kT) {
+        const int i = ib + lane;
+        nls[lane] = i < N ? -lb[i] * kLog2e : -__builtin_inff();
+        nds[lane] = i < N ? nb[i] : 0.f;
+      }
+      wave_sync();
+      if (!set_meets(ib, ie, j0, j1, dset)) continue;
+      f32x16 sacc = zero16(), pacc = zero16();
+      row_products<D>(qs + c32 * kRow<D> + g * kKK, dos + c32 * kRow<D> + g * kKK, kreg, vreg, sacc, pacc);
+      const bool full = set_full(ib, ie, j0, j1, dset);
+      float pr[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int il = acc_row(r, g);
+        const int dist = ib + il - jk;
+        const bool in = full || (ib + il < N && ((dist >= dset.lo && dist <= dset.hi) ||
+                                                 (dist >= dset.nlo && dist <= dset.nhi)));
+        pr[r] = in ? fast_exp2(__builtin_fmaf(sacc[r], sl2, nls[il])) : 0.f;
+        ds[r] = pr[r] * (pacc[r] + nds[il]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int il = acc_row(r, g);
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) {
+          dv[dt] = mfma32_f32(dos[il * kRow<D> + 32 * dt + c32], pr[r], dv[dt]);
+          dk[dt] = mfma32_f32(qs[il * kRow<D> + 32 * dt + c32], ds[r], dk[dt]);
+        }
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with its tile area
+  merge_rows<D>(smem, dk, p.scale, p.dk + base, j0, N, tid);
+  __syncthreads();  // the merge area is rewritten
+  merge_rows<D>(smem, dv, 1.f, p.dv + base, j0, N, tid);
+}
+
+F32BwdArgs make_f32_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, const Bands& bands,
+                         int local_window, float scale, float* dvec, const Packed& pk, int rows_per_tile) {
   F32BwdArgs a;
   a.q = (const float*)q;
   a.k = (const float*)k;
   a.v = (const float*)v;
+  a.o = (const float*)o;
   a.dout = (const float*)dout;
   a.lse = lse;
   a.dvec = dvec;
@@ -480,17 +738,28 @@ F32BwdArgs make_f32_args(const void* q, const void* k, const void* v, const floa
 }
 
 
+// the walk-splitting kernels when the 64-row tiles would not occupy the chip
+bool split_launch(int B, int H, int N) {
+  return (long long)B * H * ((N + kW * kT - 1) / (kW * kT)) < kSplitMaxTiles;
+}
+
 }  // namespace
 
-int launch_bwd_dq_f32(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
-                      int B, int H, int N, int d, const Bands& bands, int local_window, float scale,
-                      const float* dvec, const Packed& pk, hipStream_t stream) {
-  const F32BwdArgs a = make_f32_args(q, k, v, lse, dout, dq, nullptr, nullptr, B, H, N, bands, local_window, scale,
-                                     dvec, pk, kW * kT);
+int launch_bwd_dq_f32(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                      void* dq, int B, int H, int N, int d, const Bands& bands, int local_window, float scale,
+                      float* dvec, const Packed& pk, hipStream_t stream) {
+  const bool split = split_launch(B, H, N);
+  const F32BwdArgs a = make_f32_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, bands, local_window, scale,
+                                     dvec, pk, split ? kT : kW * kT);
   const long long total = work_grid(B, H, a.n_tiles);
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   const dim3 grid((unsigned)total), block(64 * kW);
-  if (d == 128)
+  if (split) {
+    if (d == 128)
+      hipLaunchKernelGGL(bwd_f32_dq_split_kernel<128>, grid, dim3(64 * kSplitWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL(bwd_f32_dq_split_kernel<64>, grid, dim3(64 * kSplitWaves), 0, stream, a);
+  } else if (d == 128)
     hipLaunchKernelGGL((bwd_f32_dq_kernel<128, kW>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((bwd_f32_dq_kernel<64, kW>), grid, block, 0, stream, a);
@@ -499,13 +768,19 @@ int launch_bwd_dq_f32(const void* q, const void* k, const void* v, const float* 
 
 int launch_bwd_dkdv_f32(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
                         void* dv, int B, int H, int N, int d, const Bands& bands, int local_window, float scale,
-                        const float* dvec, const Packed& pk, hipStream_t stream) {
-  const F32BwdArgs a = make_f32_args(q, k, v, lse, dout, nullptr, dk, dv, B, H, N, bands, local_window, scale, dvec,
-                                     pk, kW * kT);
+                        float* dvec, const Packed& pk, hipStream_t stream) {
+  const bool split = split_launch(B, H, N);
+  const F32BwdArgs a = make_f32_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, bands, local_window,
+                                     scale, dvec, pk, split ? kT : kW * kT);
   const long long total = work_grid(B, H, a.n_tiles);
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   const dim3 grid((unsigned)total), block(64 * kW);
-  if (d == 128)
+  if (split) {
+    if (d == 128)
+      hipLaunchKernelGGL(bwd_f32_dkdv_split_kernel<128>, grid, dim3(64 * kSplitWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL(bwd_f32_dkdv_split_kernel<64>, grid, dim3(64 * kSplitWaves), 0, stream, a);
+  } else if (d == 128)
     hipLaunchKernelGGL((bwd_f32_dkdv_kernel<128, kW>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((bwd_f32_dkdv_kernel<64, kW>), grid, block, 0, stream, a);
