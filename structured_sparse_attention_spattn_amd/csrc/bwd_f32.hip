@@ -30,12 +30,14 @@
 // and each wave idles (at the tile barrier) on the tiles outside its own
 // strip, so wider workgroups waste more; two waves per workgroup measured
 // faster than four at every size.  Every gradient row is written once, by the
-// wave that owns it: no atomics, deterministic results.
+// wave that owns it: no atomics, deterministic results.  At d = 128 the operand
+// rows and accumulators take about 390-430 registers, one wave per SIMD; at
+// d = 64 both kernels are held to 256 for two waves per SIMD.
 //
-// One wave per SIMD (the operand rows and accumulators take about 400
-// registers), so nothing hides a product's wait for its LDS operand: the
-// loops below read the operands of the next two groups of products ahead and
-// fence the order with scheduling barriers.
+//   bwd_f32_*_split_kernel  small launches (too few 64-row tiles to occupy
+//                        the chip): one workgroup per 32-row tile, its four
+//                        waves splitting the tile walk, partial gradients
+//                        added through LDS.
 #include "common.h"
 
 namespace spattn {
@@ -103,7 +105,8 @@ __device__ __forceinline__ void fence_sched() { __builtin_amdgcn_sched_barrier(0
 // Row-wise products: acc1 += A1 B1^T, acc2 += A2 B2^T over D features, with
 // A1, A2 the rows c32 of two staged tiles (this half-wave's D/2 features) and
 // B1, B2 the lane's own operand rows in registers.  The 16-byte operand reads
-// run two groups of four products ahead.
+// run two groups of four products ahead (fenced: the compiler otherwise
+// issues each read just before its products).
 template <int D>
 __device__ __forceinline__ void row_products(const float* a1, const float* a2, const f32x4* b1, const f32x4* b2,
                                              f32x16& acc1, f32x16& acc2) {
@@ -204,7 +207,7 @@ __device__ __forceinline__ void store_rows(float* __restrict__ dst, const f32x16
 
 // ------------------------------------------------------------ dQ (query-major)
 template <int D, int W>
-__global__ __launch_bounds__(64 * W) void bwd_f32_dq_kernel(F32BwdArgs p) {
+__global__ __launch_bounds__(64 * W, D == 64 ? 2 : 1) void bwd_f32_dq_kernel(F32BwdArgs p) {
   constexpr int kThr = 64 * W;
   constexpr int kKK = D / 2;
   constexpr int kDT = D / 32;
@@ -280,12 +283,6 @@ __global__ __launch_bounds__(64 * W) void bwd_f32_dq_kernel(F32BwdArgs p) {
         // S^T and dP^T: rows = the tile's keys, columns = this wave's queries
         f32x16 sacc = zero16(), pacc = zero16();
         row_products<D>(ks + c32 * kRow<D> + g * kKK, vs + c32 * kRow<D> + g * kKK, qreg, dreg, sacc, pacc);
-        // the K columns of the first two dQ products, read while dS is formed
-        float kc[16][kDT];
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-          for (int dt = 0; dt < kDT; ++dt) kc[r][dt] = ks[acc_row(r, g) * kRow<D> + 32 * dt + c32];
         const bool full = set_full(iw0, iw1, jb, jb + kT - 1, dset);
         float ds[16];
 #pragma unroll
@@ -295,18 +292,12 @@ __global__ __launch_bounds__(64 * W) void bwd_f32_dq_kernel(F32BwdArgs p) {
           const float pr = in ? fast_exp2(__builtin_fmaf(sacc[r], sl2, nl2)) : 0.f;
           ds[r] = pr * (pacc[r] + nd);
         }
-        // dQ^T += K^T dS^T: k-slot g of product r is key acc_row(r, g); the
-        // K columns run two products ahead
+        // dQ^T += K^T dS^T: k-slot g of product r is key acc_row(r, g)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (r + 2 < 16)
+        for (int r = 0; r < 16; ++r)
 #pragma unroll
-            for (int dt = 0; dt < kDT; ++dt) kc[r + 2][dt] = ks[acc_row(r + 2, g) * kRow<D> + 32 * dt + c32];
-          fence_sched();
-#pragma unroll
-          for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32_f32(kc[r][dt], ds[r], acc[dt]);
-          fence_sched();
-        }
+          for (int dt = 0; dt < kDT; ++dt)
+            acc[dt] = mfma32_f32(ks[acc_row(r, g) * kRow<D> + 32 * dt + c32], ds[r], acc[dt]);
       }
       if (has_next) st.store(smem + (s ^ 1) * kStage, smem + (s ^ 1) * kStage + kTensor, tid);
       __syncthreads();
@@ -317,7 +308,7 @@ __global__ __launch_bounds__(64 * W) void bwd_f32_dq_kernel(F32BwdArgs p) {
 
 // ------------------------------------------------------------ dK, dV (key-major)
 template <int D, int W>
-__global__ __launch_bounds__(64 * W) void bwd_f32_dkdv_kernel(F32BwdArgs p) {
+__global__ __launch_bounds__(64 * W, D == 64 ? 2 : 1) void bwd_f32_dkdv_kernel(F32BwdArgs p) {
   constexpr int kThr = 64 * W;
   constexpr int kKK = D / 2;
   constexpr int kDT = D / 32;
@@ -417,15 +408,6 @@ __global__ __launch_bounds__(64 * W) void bwd_f32_dkdv_kernel(F32BwdArgs p) {
         // S and dP: rows = the tile's queries, columns = this wave's keys
         f32x16 sacc = zero16(), pacc = zero16();
         row_products<D>(qs + c32 * kRow<D> + g * kKK, dos + c32 * kRow<D> + g * kKK, kreg, vreg, sacc, pacc);
-        // the dO and Q columns of the first two dV/dK products, read while P and dS are formed
-        float oc[16][kDT], qc[16][kDT];
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-          for (int dt = 0; dt < kDT; ++dt) {
-            oc[r][dt] = dos[acc_row(r, g) * kRow<D> + 32 * dt + c32];
-            qc[r][dt] = qs[acc_row(r, g) * kRow<D> + 32 * dt + c32];
-          }
         if (has_next) {
           store_q(s ^ 1);
           st.load(db, inext, N, tid);
@@ -441,25 +423,15 @@ __global__ __launch_bounds__(64 * W) void bwd_f32_dkdv_kernel(F32BwdArgs p) {
           pr[r] = in ? fast_exp2(__builtin_fmaf(sacc[r], sl2, nls[il])) : 0.f;
           ds[r] = pr[r] * (pacc[r] + nds[il]);
         }
-        // dV^T += dO^T P and dK^T += Q^T dS: k-slot g of product r is query
-        // acc_row(r, g); the dO and Q columns run two products ahead
+        // dV^T += dO^T P and dK^T += Q^T dS: k-slot g of product r is query acc_row(r, g)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (r + 2 < 16) {
-            const int il = acc_row(r + 2, g);
-#pragma unroll
-            for (int dt = 0; dt < kDT; ++dt) {
-              oc[r + 2][dt] = dos[il * kRow<D> + 32 * dt + c32];
-              qc[r + 2][dt] = qs[il * kRow<D> + 32 * dt + c32];
-            }
-          }
-          fence_sched();
+          const int il = acc_row(r, g);
 #pragma unroll
           for (int dt = 0; dt < kDT; ++dt) {
-            dv[dt] = mfma32_f32(oc[r][dt], pr[r], dv[dt]);
-            dk[dt] = mfma32_f32(qc[r][dt], ds[r], dk[dt]);
+            dv[dt] = mfma32_f32(dos[il * kRow<D> + 32 * dt + c32], pr[r], dv[dt]);
+            dk[dt] = mfma32_f32(qs[il * kRow<D> + 32 * dt + c32], ds[r], dk[dt]);
           }
-          fence_sched();
         }
       } else if (has_next) {
         store_q(s ^ 1);
