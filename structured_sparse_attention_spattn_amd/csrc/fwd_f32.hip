@@ -8,7 +8,9 @@
 // 32 rows staged in LDS (double buffered), visited only inside the band
 // strip.  S^T = K Q^T and O^T += V^T P^T as in the bfloat16 kernel; with a
 // k-depth of 2 per product the operands are single floats, so V is read
-// row-major from LDS without a transpose.
+// row-major from LDS without a transpose.  In S^T, product kk takes feature
+// kk in lanes 0-31 and feature D/2 + kk in lanes 32-63, so a lane's K
+// operands for four consecutive products are one 16-byte LDS read.
 #include "common.h"
 
 namespace spattn {
@@ -36,7 +38,7 @@ struct FwdF32Args {
 
 template <int D>
 struct F32Smem {
-  static constexpr int kKRow = D + 2;  // odd-pair stride: 64 distinct banks per K read
+  static constexpr int kKRow = D + 4;  // 16-byte rows; 16 lanes' row reads on distinct banks
   static constexpr int kVRow = D + 8;  // rows 4 apart land 32 banks apart
   static constexpr int kKStage = kBK * kKRow;
   static constexpr int kStage = kKStage + kBK * kVRow;
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
   constexpr int kDT = D / 32;
   constexpr int kKK = D / 2;
   constexpr int kLoads = kBK * D / 4 / kThreads;  // float4 loads per thread per tensor
-  __shared__ float smem[2 * SM::kStage];
+  __shared__ __align__(16) float smem[2 * SM::kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,9 +96,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
   const bool wave_live = iw0 <= N - 1;
   const int iq = iw0 + c32;
 
-  float qreg[kKK];
+  f32x4 qreg[kKK / 4];  // features g * D/2 .. g * D/2 + D/2 - 1 of row iq
 #pragma unroll
-  for (int kk = 0; kk < kKK; ++kk) qreg[kk] = iq < N ? qb[(size_t)iq * D + 2 * kk + g] : 0.f;
+  for (int c = 0; c < kKK / 4; ++c)
+    qreg[c] = iq < N ? *(const f32x4*)(qb + (size_t)iq * D + g * kKK + 4 * c) : f32x4{0, 0, 0, 0};
 
   f32x4 kreg[kLoads], vreg[kLoads];
   auto load_tile = [&](int u) {
@@ -150,7 +153,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < kKK; ++kk) sacc = mfma32_f32(ks[c32 * SM::kKRow + 2 * kk + g], qreg[kk], sacc);
+      for (int c = 0; c < kKK / 4; ++c) {
+        const f32x4 ka = *(const f32x4*)(ks + c32 * SM::kKRow + g * kKK + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc = mfma32_f32(ka[e], qreg[c][e], sacc);
+      }
       float x[16];
       const bool full = set_full(iw0, iw1, jb, jb + 31, dset);
 #pragma unroll
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_split_kernel(FwdF32Args p) {
   constexpr int kWaveLoads = kBK * D / 4 / 64;  // float4 loads per lane per tensor (a wave loads a tile)
   constexpr int kRedRow = D + 4;                // merge rows: 16-byte aligned, spread over banks
   static_assert(kWaves * 32 * kRedRow + 2 * kWaves * 32 <= kWaves * SM::kStage, "merge area");
-  __shared__ float smem[kWaves * SM::kStage];
+  __shared__ __align__(16) float smem[kWaves * SM::kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -266,9 +273,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_split_kernel(FwdF32Args p) {
   }
   const int iq = i0 + c32;
 
-  float qreg[kKK];
+  f32x4 qreg[kKK / 4];  // features g * D/2 .. g * D/2 + D/2 - 1 of row iq
 #pragma unroll
-  for (int kk = 0; kk < kKK; ++kk) qreg[kk] = iq < N ? qb[(size_t)iq * D + 2 * kk + g] : 0.f;
+  for (int c = 0; c < kKK / 4; ++c)
+    qreg[c] = iq < N ? *(const f32x4*)(qb + (size_t)iq * D + g * kKK + 4 * c) : f32x4{0, 0, 0, 0};
 
   float* ks = smem + wave * SM::kStage;
   float* vs = ks + SM::kKStage;
@@ -316,7 +324,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_split_kernel(FwdF32Args p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) sacc = mfma32_f32(ks[c32 * SM::kKRow + 2 * kk + g], qreg[kk], sacc);
+    for (int c = 0; c < kKK / 4; ++c) {
+      const f32x4 ka = *(const f32x4*)(ks + c32 * SM::kKRow + g * kKK + 4 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc = mfma32_f32(ka[e], qreg[c][e], sacc);
+    }
     float x[16];
     const bool full = set_full(i0, i1, jb, jb + kBK - 1, dset);
 #pragma unroll
