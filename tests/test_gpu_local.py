@@ -200,7 +200,7 @@ LOCAL_F32 = [
     (2, 3, 257, 128, 120, "bdp", 122),
     (1, 9, 7, 64, 2, "bdp", 123),
     (1, 5, 200, 64, 7, "odd", 124),
-    (4, 16, 1024, 64, 40, "bdp", 125),  # 512 tiles of 128 rows: the 4-wave float32 kernels
+    (4, 16, 1024, 64, 40, "bdp", 125),  # 1024 tiles of 64 rows: the two-wave float32 kernels, not the split ones
 ]
 
 

@@ -240,8 +240,10 @@ BWD_SMALL = [
     (2, 6, 451, 64, "bf16", "bf16", "odd", 46),
     (1, 3, 200, 64, "f32", "f32", "bdp", 47),
     (1, 2, 130, 128, "f32", "f32", "dense", 48),
-    (4, 16, 1024, 64, "f32", "f32", "bdp", 49),     # 512 tiles of 128 rows: the 4-wave float32 kernels
+    (4, 16, 1024, 64, "f32", "f32", "bdp", 49),     # 1024 tiles of 64 rows: the two-wave float32 kernels, not the split ones
     (2, 32, 1024, 128, "f32", "f32", "odd", 50),
+    (1, 9, 7, 64, "f32", "f32", "bdp", 51),        # H > N: empty bands, float32
+    (4, 16, 1000, 64, "f32", "f32", "bdp", 52),    # two-wave float32 kernels with a ragged last tile
 ]
 
 
