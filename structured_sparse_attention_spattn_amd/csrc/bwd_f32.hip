@@ -58,7 +58,7 @@ struct F32BwdArgs {
   float* dk;
   float* dv;
   int B, H, N;       // sequences (B), heads, tokens per sequence (the longest, when packed)
-  int n_tiles;       // row tiles of 32*W per (sequence, head)
+  int n_tiles;       // row tiles per (sequence, head): 32 * kW rows, or 32 for the split kernels
   int local_window;  // shared local window width (0: exclusive bands)
   float scale;
   float scale_log2;
@@ -105,8 +105,9 @@ __device__ __forceinline__ void fence_sched() { __builtin_amdgcn_sched_barrier(0
 // Row-wise products: acc1 += A1 B1^T, acc2 += A2 B2^T over D features, with
 // A1, A2 the rows c32 of two staged tiles (this half-wave's D/2 features) and
 // B1, B2 the lane's own operand rows in registers.  The 16-byte operand reads
-// run two groups of four products ahead (fenced: the compiler otherwise
-// issues each read just before its products).
+// run two groups of four products ahead, fenced so that the compiler keeps
+// the distance (measured neutral against its own order, which issues each
+// read just before its products).
 template <int D>
 __device__ __forceinline__ void row_products(const float* a1, const float* a2, const f32x4* b1, const f32x4* b2,
                                              f32x16& acc1, f32x16& acc2) {
