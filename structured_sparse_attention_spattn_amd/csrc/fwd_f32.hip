@@ -4,9 +4,11 @@
 // "Sparse Attention, Then and Now" section 1 over each head's distance band
 // ("Making Every Head Count", Figure 1 caption).
 //
-// One workgroup = (b, h, 128 query rows), 4 waves of 32 rows; key tiles of
+// One workgroup = (b, h, 64 query rows), 2 waves of 32 rows; key tiles of
 // 32 rows staged in LDS (double buffered), visited only inside the band
-// strip.  S^T = K Q^T and O^T += V^T P^T as in the bfloat16 kernel; with a
+// strip.  A workgroup's walk covers the strips of all its waves, and a wave
+// idles at the tile barrier on tiles outside its own, so two waves per
+// workgroup waste less than four.  S^T = K Q^T and O^T += V^T P^T as in the bfloat16 kernel; with a
 // k-depth of 2 per product the operands are single floats, so V is read
 // row-major from LDS without a transpose.  In S^T, product kk takes feature
 // kk in lanes 0-31 and feature D/2 + kk in lanes 32-63, so a lane's K
@@ -16,9 +18,10 @@
 namespace spattn {
 namespace {
 
-constexpr int kBQ = 128;
+constexpr int kBQ = 64;        // query rows per workgroup of fwd_f32_kernel (2 waves)
+constexpr int kFwdThreads = 128;
 constexpr int kBK = 32;
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // the split kernel's workgroup (4 waves)
 
 struct FwdF32Args {
   const float* q;
@@ -45,11 +48,11 @@ struct F32Smem {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
+__global__ __launch_bounds__(kFwdThreads) void fwd_f32_kernel(FwdF32Args p) {
   using SM = F32Smem<D>;
   constexpr int kDT = D / 32;
   constexpr int kKK = D / 2;
-  constexpr int kLoads = kBK * D / 4 / kThreads;  // float4 loads per thread per tensor
+  constexpr int kLoads = kBK * D / 4 / kFwdThreads;  // float4 loads per thread per tensor
   __shared__ __align__(16) float smem[2 * SM::kStage];
 
   const int tid = threadIdx.x;
@@ -83,11 +86,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
   if (has_second(dset)) span2 = band_key_span(i_tile0, i_tile1, dset.nlo, dset.nhi);
   const TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kBK);
   if (walk.n == 0) {
-    for (int c = tid; c < kBQ * (D / 4); c += kThreads) {
+    for (int c = tid; c < kBQ * (D / 4); c += kFwdThreads) {
       const int r = c / (D / 4), cc = c % (D / 4);
       if (i_tile0 + r < N) *(f32x4*)(ob + (size_t)(i_tile0 + r) * D + cc * 4) = f32x4{0, 0, 0, 0};
     }
-    for (int r = tid; r < kBQ; r += kThreads)
+    for (int r = tid; r < kBQ; r += kFwdThreads)
       if (i_tile0 + r < N) lb[i_tile0 + r] = ninf;
     return;
   }
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
     const int j0 = u * kBK;
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
-      const int c = tid + kThreads * r;
+      const int c = tid + kFwdThreads * r;
       const int row = c / (D / 4), col = c % (D / 4);
       const int j = j0 + row;
       kreg[r] = j < N ? *(const f32x4*)(kb + (size_t)j * D + col * 4) : f32x4{0, 0, 0, 0};
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdF32Args p) {
     float* vs = ks + SM::kKStage;
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
-      const int c = tid + kThreads * r;
+      const int c = tid + kFwdThreads * r;
       const int row = c / (D / 4), col = c % (D / 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -423,9 +426,8 @@ int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
   a.B = B;
   a.H = H;
   a.N = N;
-  a.n_qt = (N + kBQ - 1) / kBQ;
-  const bool split = (long long)B * H * a.n_qt < kSplitMaxTiles;
-  if (split) a.n_qt = (N + kSplitBQ - 1) / kSplitBQ;
+  const bool split = (long long)B * H * ((N + 127) / 128) < kSplitMaxTiles;
+  a.n_qt = split ? (N + kSplitBQ - 1) / kSplitBQ : (N + kBQ - 1) / kBQ;
   a.cu = pk.cu;
   a.T = pk.T;
   a.own_bdp = pk.own_bdp;
@@ -434,7 +436,7 @@ int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
   a.bands = bands;
   const long long total = work_grid(B, H, a.n_qt);
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
-  dim3 grid((unsigned)total), block(kThreads);
+  dim3 grid((unsigned)total), block(split ? kThreads : kFwdThreads);
   if (d == 128 && split)
     hipLaunchKernelGGL(fwd_f32_split_kernel<128>, grid, block, 0, stream, a);
   else if (d == 64 && split)
