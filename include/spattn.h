@@ -231,9 +231,9 @@ int spattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* ls
 /*
  * Tile sizes the forward kernel schedules with for (d, dtype): BQ query rows
  * per workgroup and BK key rows per LDS stage.  Host only.  Float32 launches
- * with fewer than 512 query tiles of BQ rows (B * H * ceil(N / BQ)) instead
- * take 32-row tiles whose key tiles are split over the workgroup's waves;
- * the values returned here are those of the larger launches.
+ * with fewer than 512 tiles of 128 query rows (B * H * ceil(N / 128))
+ * instead take 32-row tiles whose key tiles are split over the workgroup's
+ * waves; the values returned here are those of the larger launches.
  * Errors: SPATTN_E_ARG for NULL outputs, SPATTN_E_UNSUPPORTED otherwise.
  */
 int spattn_kernel_tiles(int32_t d, int32_t dtype, int32_t* BQ, int32_t* BK);
