@@ -339,7 +339,8 @@ def main():
     if not args.no_variants:
         def timed_total(bands, lw, steps, warmup):
             """fwd and bwd (both stages) of the whole batch with these bands /
-            local window; HIP events on the launch stream."""
+            local window; HIP events on the launch stream, median per step
+            (and the mean wall time per step)."""
             for _ in range(warmup):
                 ops.fwd(q, k, v, bands=bands, out=o, lse=lse, local_window=lw)
                 ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads, local_window=lw)
@@ -354,8 +355,9 @@ def main():
                 e2.record()
             torch.cuda.synchronize()
             wall = (time.perf_counter() - t0) * 1e3 / steps
-            f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-            b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+            # medians: one stalled step must not stand for the variant
+            f = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+            b = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
             return wall, f, b
 
         variants = {}
