@@ -16,6 +16,7 @@ band tables of the page's ablation patterns (sliding window, gapped half
 bands) and with a shared local window joined to every band.
 """
 import argparse
+import gc
 import json
 import math
 import os
@@ -111,6 +112,11 @@ def main():
 
     import numpy as np
     import torch
+
+    # no collector pauses inside the timed regions: collect once now and leave
+    # the rest of this short run to reference counting
+    gc.collect()
+    gc.disable()
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
