@@ -398,3 +398,40 @@ def test_calls_run_on_the_callers_stream():
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
     for a, b_ in zip(g0, g1):
         assert torch.equal(a, b_)
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,bk", [
+    (1, 8, 1024, 64, "f32", "bdp"),     # float32 split kernels
+    (4, 16, 1024, 64, "f32", "bdp"),    # float32 two-wave kernels
+    (1, 4, 515, 128, "f32", "odd"),
+    (2, 32, 1024, 128, "f32", "bdp"),
+    (1, 4, 515, 128, "bf16", "bdp"),
+    (2, 6, 451, 64, "bf16", "odd"),
+])
+def test_bwd_repeatable_with_poisoned_workspace(B, H, N, d, dtype, bk):
+    """Both backward stages, repeated with the workspace filled with NaN bit
+    patterns before every repeat: the dQ stage must write -D (and, for
+    bfloat16, -LSE log2 e) for every row that the dK/dV stage reads, or NaN
+    reaches the gradients; and the gradients agree bit for bit across repeats
+    (every row written once, fixed summation order)."""
+    _say(f"poisoned-workspace repeat B={B} H={H} N={N} d={d} {dtype} {bk}")
+    inp = _to_dev(make_inputs(B, H, N, d, dtype=dtype, seed=600 + N + d, with_dout=True))
+    band_arg, _ = _bands(bk, N, H)
+    o, lse = ops.fwd(inp["q"], inp["k"], inp["v"], bands=band_arg)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    ws = torch.empty(ops.bwd_workspace_bytes(B, H, N, d, tdt, tdt), dtype=torch.uint8, device=DEV)
+    first = None
+    for rep in range(3):
+        ws.fill_(255)  # every float of the workspace reads as NaN
+        dq = ops.bwd_dq(inp["q"], inp["k"], inp["v"], o, lse, inp["dout"], ws, bands=band_arg)
+        dk, dv = ops.bwd_dkdv(inp["q"], inp["k"], inp["v"], lse, inp["dout"], ws, bands=band_arg)
+        torch.cuda.synchronize()
+        outs = (dq, dk, dv)
+        for a, nm in zip(outs, ("dQ", "dK", "dV")):
+            assert bool(torch.isfinite(a).all()), f"{nm} not finite on repeat {rep}"
+        if first is None:
+            first = outs
+            continue
+        for a, b_, nm in zip(first, outs, ("dQ", "dK", "dV")):
+            it = torch.int16 if a.element_size() == 2 else torch.int32
+            assert torch.equal(a.view(it), b_.view(it)), f"{nm} differs on repeat {rep}"
