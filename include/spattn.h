@@ -56,6 +56,21 @@ enum spattn_dtype { SPATTN_F32 = 0, SPATTN_BF16 = 1 };
  * argument block). */
 #define SPATTN_MAX_HEADS 256
 
+/* Attention patterns of spattn_band_table_pattern. */
+enum spattn_pattern {
+  SPATTN_PATTERN_BDP = 0,             /* Balanced Distance Partitioning (the method) */
+  SPATTN_PATTERN_SLIDING_WINDOW = 1,  /* every head: distances [0, width - 1] */
+  SPATTN_PATTERN_GAPPED_HALF = 2,     /* first half of each partition band */
+  SPATTN_PATTERN_DENSE = 3            /* every head: [0, N - 1], dense causal */
+};
+
+/* Kernels whose tile walk spattn_tile_walk reports. */
+enum spattn_kernel {
+  SPATTN_KERNEL_FWD = 0,      /* forward: query-major */
+  SPATTN_KERNEL_BWD_DQ = 1,   /* first backward stage (D and dQ): query-major */
+  SPATTN_KERNEL_BWD_DKDV = 2  /* second backward stage (dK, dV): key-major */
+};
+
 /*
  * Band table of Balanced Distance Partitioning ("Making Every Head Count",
  * Figure 1 caption).  Host only, no GPU needed.
@@ -69,6 +84,28 @@ enum spattn_dtype { SPATTN_F32 = 0, SPATTN_BF16 = 1 };
  * NULL (outputs untouched).
  */
 int spattn_band_table(int32_t N, int32_t H, int32_t* lo, int32_t* hi);
+
+/*
+ * Band tables of the attention patterns that "Making Every Head Count"
+ * compares in its Figure 2 caption, for use as band_lo / band_hi of the
+ * other calls.  Host only.
+ *   kind  SPATTN_PATTERN_BDP: the partition itself (as spattn_band_table).
+ *         SPATTN_PATTERN_SLIDING_WINDOW: every head restricted to the same
+ *           local window, distances [0, w - 1] with w = min(width, N); the
+ *           page gives no width.  width = 0 gives every head an empty band.
+ *         SPATTN_PATTERN_GAPPED_HALF: each head keeps only the first half of
+ *           its partition band, floor(W_h / 2) distances from lo_h (the
+ *           rounding is not on the page); a width-1 band becomes empty.
+ *         SPATTN_PATTERN_DENSE: every head [0, N - 1], dense causal attention
+ *           (the baseline the method is compared against).
+ *   width used by SPATTN_PATTERN_SLIDING_WINDOW only (>= 0).
+ *   lo, hi  caller-owned host arrays of H int32; an empty band is written
+ *           lo = N, hi = N - 1.
+ * Errors: SPATTN_E_ARG for N < 1, H outside 1 .. SPATTN_MAX_HEADS, a NULL
+ * pointer, an unknown kind or a negative sliding-window width.
+ */
+int spattn_band_table_pattern(int32_t N, int32_t H, int32_t kind, int32_t width,
+                              int32_t* lo, int32_t* hi);
 
 /*
  * Forward pass: for every (b, h, i), with S = { j : lo_h <= i - j <= hi_h,
@@ -98,7 +135,10 @@ int spattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * row vectors [B,H,N], each rounded up to 256 bytes: -D_i = -dO_i . O_i,
  * then -LSE_i log2(e), the exponent offset the bfloat16 dK/dV kernel
  * recomputes P with (the float32 kernels leave the second vector unused).
- * Returns 0 for invalid sizes.
+ * grad_dtype (SPATTN_F32 or dtype, as in spattn_bwd) is part of the query so
+ * that a gradient type needing more workspace can be added without a new
+ * call; every current combination needs the same two vectors.
+ * Returns 0 for invalid sizes or an unsupported grad_dtype.
  */
 size_t spattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d,
                                   int32_t dtype, int32_t grad_dtype);
@@ -157,7 +197,11 @@ int spattn_bwd_local(const void* q, const void* k, const void* v, const void* o,
  * sequence boundary: token i of sequence s attends the keys j of s with
  * i - j in its head's set, as in spattn_fwd_local.
  *   cu_seqlens  device int32 [n_seqs + 1], non-decreasing, cu_seqlens[0] = 0,
- *               cu_seqlens[n_seqs] = total; read by the kernels (not checked).
+ *               cu_seqlens[n_seqs] = total.  Read by the kernels, not by the
+ *               host, so a malformed array is not reported; the kernels clamp
+ *               every sequence to tokens [0, total) and to max_seqlen, so they
+ *               never index outside the tensors, but the rows of tokens that
+ *               no valid sequence covers are then left unwritten.
  *   max_seqlen  an upper bound on every sequence's length.  It sizes the
  *               grid, and tokens past it in a longer sequence are not computed.
  *   band_lo, band_hi  host, H int32 each, validated against max_seqlen as in
@@ -256,6 +300,36 @@ int spattn_kernel_tiles(int32_t d, int32_t dtype, int32_t* BQ, int32_t* BK);
 int spattn_tile_list(int32_t N, int32_t lo, int32_t hi, int32_t BQ, int32_t BK,
                      int32_t* row_ptr, int32_t* tiles, uint8_t* kind, int32_t cap,
                      int32_t* n_out, void* stream);
+
+/*
+ * Test export of a kernel's actual tile walk: for one band [lo, hi] (with
+ * the shared local window as in spattn_fwd_local) of a length-N sequence,
+ * runs on the device the walk builder and tile test the chosen kernel runs,
+ * for the launch that B sequences of H heads would make (the float32 kernels
+ * pick their tile shape by launch size).  Output in CSR form over the tiles
+ * the kernel owns (query tiles for SPATTN_KERNEL_FWD and _BWD_DQ, key tiles
+ * for SPATTN_KERNEL_BWD_DKDV):
+ *   ptr    device int32 [ceil(N / own_rows) + 1]
+ *   tiles  device int32 [cap]  indices of the visited tiles of the other
+ *          operand, in the kernel's visit order (at most two ascending runs,
+ *          a single run possibly rotated so that neighbouring workgroups read
+ *          a shared tile at the same step)
+ *   kind   device uint8 [cap]  0 = FULL (every pair of the two tiles is in
+ *          the head's set), 1 = PARTIAL
+ *   n_out  device int32 [1]    total number of visits
+ *   own_rows, tile_rows  host int32, optional (NULL): rows of an owned tile
+ *          and of a visited tile.
+ * The visited tiles of an owned tile are exactly those in which some pair
+ * (i, j), j <= i < N, has i - j in the head's set.  If the list is longer
+ * than cap, n_out holds the full count and the first cap entries are written.
+ * Errors: SPATTN_E_ARG (unknown kernel, null pointers, B, H or N < 1, band
+ * outside [0, N-1], local_window < 0), SPATTN_E_UNSUPPORTED (dtype),
+ * SPATTN_E_HIP.
+ */
+int spattn_tile_walk(int32_t kernel, int32_t dtype, int32_t B, int32_t H, int32_t N,
+                     int32_t lo, int32_t hi, int32_t local_window, int32_t* ptr,
+                     int32_t* tiles, uint8_t* kind, int32_t cap, int32_t* n_out,
+                     int32_t* own_rows, int32_t* tile_rows, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* spattn_status_string(int status);

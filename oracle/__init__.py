@@ -45,7 +45,7 @@ from .attention import (
     band_attention_fwd_rows,
     band_attention_bwd_rows,
 )
-from .tiles import query_tile_list, key_tile_list
+from .tiles import query_tile_list, key_tile_list, distance_ranges
 from .decode import decode_key_set, decode_attention
 from .varlen import seq_bands, varlen_fwd, varlen_bwd
 
@@ -53,6 +53,6 @@ __all__ = [
     "band_table", "band_pairs", "band_table_sliding_window", "band_table_gapped_half",
     "masked_attention_literal", "masked_attention_dense", "masked_attention_dense_bwd",
     "band_mask", "band_attention_fwd", "band_attention_bwd", "band_attention_fwd_rows", "band_attention_bwd_rows",
-    "query_tile_list", "key_tile_list", "decode_key_set", "decode_attention",
+    "query_tile_list", "key_tile_list", "distance_ranges", "decode_key_set", "decode_attention",
     "seq_bands", "varlen_fwd", "varlen_bwd",
 ]

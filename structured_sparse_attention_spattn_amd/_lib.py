@@ -12,12 +12,15 @@ LIB_PATH = os.path.join(HERE, "libspattn.so")
 OK, E_ARG, E_UNSUPPORTED, E_HIP, E_WORKSPACE = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 MAX_HEADS = 256
+PATTERN_BDP, PATTERN_SLIDING_WINDOW, PATTERN_GAPPED_HALF, PATTERN_DENSE = 0, 1, 2, 3
+KERNEL_FWD, KERNEL_BWD_DQ, KERNEL_BWD_DKDV = 0, 1, 2
 
 EXPORTS = (
     "spattn_band_table", "spattn_fwd", "spattn_bwd_workspace_bytes", "spattn_bwd",
     "spattn_bwd_dq", "spattn_bwd_dkdv", "spattn_fwd_local", "spattn_bwd_local", "spattn_decode",
     "spattn_fwd_varlen", "spattn_bwd_varlen",
     "spattn_kernel_tiles", "spattn_tile_list", "spattn_status_string",
+    "spattn_band_table_pattern", "spattn_tile_walk",
 )
 
 _lib = None
@@ -45,6 +48,11 @@ def load():
     lib = ctypes.CDLL(LIB_PATH)
     lib.spattn_band_table.argtypes = [_i32, _i32, _pi32, _pi32]
     lib.spattn_band_table.restype = ctypes.c_int
+    lib.spattn_band_table_pattern.argtypes = [_i32, _i32, _i32, _i32, _pi32, _pi32]
+    lib.spattn_band_table_pattern.restype = ctypes.c_int
+    lib.spattn_tile_walk.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _pi32,
+                                     _pi32, _p]
+    lib.spattn_tile_walk.restype = ctypes.c_int
     lib.spattn_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32,
                                ctypes.c_float, _p]
     lib.spattn_fwd.restype = ctypes.c_int

@@ -58,6 +58,8 @@ struct BwdArgs {
 constexpr int kDqBQ = 128;    // query rows per workgroup
 constexpr int kDqBK = 32;     // key rows per stage
 constexpr int kDqStages = 4;  // LDS ring depth: tiles u+1 .. u+3 load while u is used
+// query-major: 128 rows own 32-key tiles, a single run rotated (align_walk)
+constexpr WalkShape kDqWalk{kDqBQ, kDqBK, false, true};
 
 template <int D, bool TWO>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
@@ -116,13 +118,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const int iq = iw0 + c32;
   const bool row_ok = iq < N;
 
-  const int i_tile1 = min(N - 1, i_tile0 + kDqBQ - 1);
-  KeySpan span2{0, -1};
-  if constexpr (TWO)
-    if (has_second(dset)) span2 = band_key_span(i_tile0, i_tile1, dset.nlo, dset.nhi);
   // key tiles to visit, in order; the ring holds visit v in stage v % kDqStages
-  TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kDqBK);
-  align_walk(walk, i_tile0 - hi, i_tile0 + kDqBQ - 1 - lo, kDqBK);
+  const TileWalk walk = kernel_walk(kDqWalk, i_tile0, N, dset);
   const int n_visit = walk.n;
   auto issue = [&](int v) {
     bf16* st = smem + (v % kDqStages) * 2 * kTile;
@@ -305,6 +302,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
 // wave keeps a single 32 x d accumulator.
 constexpr int kKvBK = 64;     // key rows per workgroup
 constexpr int kKvQB = 32;     // query rows per stage
+// key-major: 64 key rows own 32-row query blocks, ascending
+constexpr WalkShape kKvWalk{kKvBK, kKvQB, true, false};
 constexpr int kKvStages = 4;  // LDS ring depth
 constexpr int kKvAhead = 2;   // blocks tq + 1 .. tq + kKvAhead in flight while tq is used
 constexpr int kKvThreads = 256;
@@ -383,11 +382,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  KeySpan qspan2{0, -1};
-  if constexpr (TWO)
-    if (has_second(dset)) qspan2 = band_query_span(j0, j1, dset.nlo, dset.nhi, N);
   // query blocks to visit, in order; visit v sits in ring stage v % kKvStages
-  const TileWalk walk = tile_walk(band_query_span(j0, j1, lo, hi, N), qspan2, kKvQB);
+  const TileWalk walk = kernel_walk(kKvWalk, j0, N, dset);
   const int n_visit = walk.n;
   // Stepped schedule.  The second key pair (keys 32 .. 63 of the tile) never
   // needs the walk's first query block when the first pair never needs its
@@ -743,5 +739,9 @@ int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const floa
     hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), grid, block, 0, stream, a);
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
 }
+
+// The walks of the two bfloat16 backward kernels.
+WalkShape bwd_bf16_dq_walk() { return kDqWalk; }
+WalkShape bwd_bf16_dkdv_walk() { return kKvWalk; }
 
 }  // namespace spattn

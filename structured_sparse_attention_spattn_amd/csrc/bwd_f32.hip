@@ -45,6 +45,10 @@ namespace {
 
 constexpr int kT = 32;  // a wave's own rows, and the rows of a staged tile
 constexpr int kW = 2;   // waves per workgroup
+// Walks: a workgroup of w waves owns w * 32 rows and visits 32-row tiles of the
+// other operand, ascending (the split kernels: w = 1, visits dealt over waves).
+__host__ __device__ constexpr WalkShape dq_walk(int w) { return WalkShape{kT * w, kT, false, false}; }
+__host__ __device__ constexpr WalkShape dkdv_walk(int w) { return WalkShape{kT * w, kT, true, false}; }
 
 struct F32BwdArgs {
   const float* q;
@@ -236,9 +240,7 @@ __global__ __launch_bounds__(64 * W, D == 64 ? 2 : 1) void bwd_f32_dq_kernel(F32
   const float* __restrict__ kb = p.k + base;
   const float* __restrict__ vb = p.v + base;
 
-  KeySpan span2{0, -1};
-  if (has_second(dset)) span2 = band_key_span(i0, i1, dset.nlo, dset.nhi);
-  const TileWalk walk = tile_walk(band_key_span(i0, i1, dset.lo, dset.hi), span2, kT);
+  const TileWalk walk = kernel_walk(dq_walk(W), i0, N, dset);
 
   const int iw0 = i0 + kT * wave;
   const int iw1 = min(N - 1, iw0 + kT - 1);
@@ -339,9 +341,7 @@ __global__ __launch_bounds__(64 * W, D == 64 ? 2 : 1) void bwd_f32_dkdv_kernel(F
   const float* __restrict__ lb = p.lse + sh.row0;
   const float* __restrict__ nb = p.dvec + sh.row0;
 
-  KeySpan span2{0, -1};
-  if (has_second(dset)) span2 = band_query_span(j0, j1, dset.nlo, dset.nhi, N);
-  const TileWalk walk = tile_walk(band_query_span(j0, j1, dset.lo, dset.hi, N), span2, kT);
+  const TileWalk walk = kernel_walk(dkdv_walk(W), j0, N, dset);
 
   const int jw0 = j0 + kT * wave;
   const int jw1 = min(N - 1, jw0 + kT - 1);
@@ -531,9 +531,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void bwd_f32_dq_split_kernel(F32B
   const DistSet dset = dist_set(sh.lo, sh.hi, p.local_window);
   const size_t base = sh.row0 * D;
 
-  KeySpan span2{0, -1};
-  if (has_second(dset)) span2 = band_key_span(i0, i1, dset.nlo, dset.nhi);
-  const TileWalk walk = tile_walk(band_key_span(i0, i1, dset.lo, dset.hi), span2, kT);
+  const TileWalk walk = kernel_walk(dq_walk(1), i0, N, dset);
 
   const int iq = i0 + c32;
   const bool row_ok = iq < N;
@@ -613,9 +611,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void bwd_f32_dkdv_split_kernel(F3
   const float* __restrict__ lb = p.lse + sh.row0;
   const float* __restrict__ nb = p.dvec + sh.row0;
 
-  KeySpan span2{0, -1};
-  if (has_second(dset)) span2 = band_query_span(j0, j1, dset.nlo, dset.nhi, N);
-  const TileWalk walk = tile_walk(band_query_span(j0, j1, dset.lo, dset.hi, N), span2, kT);
+  const TileWalk walk = kernel_walk(dkdv_walk(1), j0, N, dset);
 
   const int jk = j0 + c32;
   const bool row_ok = jk < N;
@@ -717,6 +713,10 @@ bool split_launch(int B, int H, int N) {
 }
 
 }  // namespace
+
+// The walks the float32 backward launches for B * H sequences of N rows use.
+WalkShape bwd_f32_dq_walk(int B, int H, int N) { return dq_walk(split_launch(B, H, N) ? 1 : kW); }
+WalkShape bwd_f32_dkdv_walk(int B, int H, int N) { return dkdv_walk(split_launch(B, H, N) ? 1 : kW); }
 
 int launch_bwd_dq_f32(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                       void* dq, int B, int H, int N, int d, const Bands& bands, int local_window, float scale,

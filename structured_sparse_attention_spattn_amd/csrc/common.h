@@ -55,8 +55,13 @@ struct SeqHead {
   int n;        // tokens in the sequence
   int lo, hi;   // the head's band
 };
-__device__ __forceinline__ SeqHead seq_head(const int32_t* cu, int T, int own_bdp, int H, int N, const Bands& b,
-                                            int s, int h) {
+// A packed sequence's view is clamped so that no kernel indexes outside the
+// [H, T, d] tensors whatever cu holds: its first token o lies in [0, T], its
+// length n in [0, min(N, T - o)] (N = the longest sequence, which sizes the
+// grid; tokens of a longer sequence past N are not computed).  Offsets that
+// decrease give an empty sequence.
+__host__ __device__ __forceinline__ SeqHead seq_head(const int32_t* cu, int T, int own_bdp, int H, int N,
+                                                     const Bands& b, int s, int h) {
   SeqHead r;
   if (cu == nullptr) {
     r.row0 = ((size_t)s * H + h) * N;
@@ -65,8 +70,10 @@ __device__ __forceinline__ SeqHead seq_head(const int32_t* cu, int T, int own_bd
     r.hi = b.hi[h];
     return r;
   }
-  const int o = cu[s];
-  r.n = cu[s + 1] - o;
+  const int c0 = cu[s], c1 = cu[s + 1];
+  const int o = c0 < 0 ? 0 : (c0 > T ? T : c0);
+  const int e = c1 < o ? o : (c1 > T ? T : c1);
+  r.n = e - o < N ? e - o : N;
   r.row0 = (size_t)h * T + o;
   if (own_bdp) {
     const int base = r.n / H, extra = r.n % H;
@@ -586,6 +593,35 @@ __host__ __device__ __forceinline__ void align_walk(TileWalk& w, int r0, int r1,
   if (m < 2) return;
   const int k = (m - w.a0 % m) % m;
   w.rot = k < w.n ? k : 0;
+}
+
+// The tiles one workgroup visits.  A query-major kernel (forward, dQ) owns
+// query rows [r0, r0 + own - 1] of a sequence of n rows and visits key tiles of
+// `tile` rows; a key-major kernel (dK / dV) owns key rows and visits query
+// tiles.  The visited tiles are those meeting the head's distance set, as at
+// most two ascending runs; `aligned` rotates a single run (align_walk).
+struct WalkShape {
+  int own, tile;
+  bool key_major, aligned;
+};
+__host__ __device__ __forceinline__ TileWalk kernel_walk(const WalkShape& ws, int r0, int n, const DistSet& s) {
+  const int r1 = (r0 + ws.own - 1 < n - 1) ? r0 + ws.own - 1 : n - 1;
+  KeySpan s1, s2{0, -1};
+  if (ws.key_major) {
+    s1 = band_query_span(r0, r1, s.lo, s.hi, n);
+    if (has_second(s)) s2 = band_query_span(r0, r1, s.nlo, s.nhi, n);
+  } else {
+    s1 = band_key_span(r0, r1, s.lo, s.hi);
+    if (has_second(s)) s2 = band_key_span(r0, r1, s.nlo, s.nhi);
+  }
+  TileWalk w = tile_walk(s1, s2, ws.tile);
+  if (ws.aligned) {
+    if (ws.key_major)
+      align_walk(w, r0 + s.lo, r0 + ws.own - 1 + s.hi, ws.tile);
+    else
+      align_walk(w, r0 - s.hi, r0 + ws.own - 1 - s.lo, ws.tile);
+  }
+  return w;
 }
 
 // Smallest distance of the set, or n (no distance in [0, n - 1]) when the set

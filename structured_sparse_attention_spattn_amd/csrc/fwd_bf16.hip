@@ -35,6 +35,8 @@ namespace {
 constexpr int kBQ = 128;
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
+// query-major: 128 rows own 64-key tiles, a single run rotated (align_walk)
+constexpr WalkShape kWalk{kBQ, kBK, false, true};
 
 struct FwdArgs {
   const bf16* q;
@@ -257,12 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   const float ninf = -__builtin_inff();
 
   const int i_tile0 = t * kBQ;
-  const int i_tile1 = min(N - 1, i_tile0 + kBQ - 1);
-  KeySpan span2{0, -1};
-  if constexpr (TWO)
-    if (has_second(dset)) span2 = band_key_span(i_tile0, i_tile1, dset.nlo, dset.nhi);
-  TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kBK);
-  align_walk(walk, i_tile0 - hi, i_tile0 + kBQ - 1 - lo, kBK);
+  const TileWalk walk = kernel_walk(kWalk, i_tile0, N, dset);
   if (walk.n == 0) {
     // No row of this tile has a key: output 0, LSE -inf.
     constexpr int kCpr = D / 8;
@@ -396,5 +393,7 @@ void fwd_bf16_tiles(int* BQ, int* BK) {
   *BQ = kBQ;
   *BK = kBK;
 }
+
+WalkShape fwd_bf16_walk() { return kWalk; }
 
 }  // namespace spattn

@@ -22,6 +22,8 @@ constexpr int kBQ = 64;        // query rows per workgroup of fwd_f32_kernel (2 
 constexpr int kFwdThreads = 128;
 constexpr int kBK = 32;
 constexpr int kThreads = 256;  // the split kernel's workgroup (4 waves)
+// query-major: 64 rows own 32-key tiles, ascending
+constexpr WalkShape kWalk{kBQ, kBK, false, false};
 
 struct FwdF32Args {
   const float* q;
@@ -81,10 +83,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_f32_kernel(FwdF32Args p) {
   const float ninf = -__builtin_inff();
 
   const int i_tile0 = t * kBQ;
-  const int i_tile1 = min(N - 1, i_tile0 + kBQ - 1);
-  KeySpan span2{0, -1};
-  if (has_second(dset)) span2 = band_key_span(i_tile0, i_tile1, dset.nlo, dset.nhi);
-  const TileWalk walk = tile_walk(band_key_span(i_tile0, i_tile1, lo, hi), span2, kBK);
+  const TileWalk walk = kernel_walk(kWalk, i_tile0, N, dset);
   if (walk.n == 0) {
     for (int c = tid; c < kBQ * (D / 4); c += kFwdThreads) {
       const int r = c / (D / 4), cc = c % (D / 4);
@@ -224,6 +223,8 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_f32_kernel(FwdF32Args p) {
 // softmax state; at the end the four (maximum, sum, output) triples are merged
 // through LDS, the same merge as across the chunks of a single wave.
 constexpr int kSplitBQ = 32;
+// query-major: 32 rows own 32-key tiles, ascending (wave w takes visits w, w + 4, ...)
+constexpr WalkShape kSplitWalk{kSplitBQ, kBK, false, false};
 constexpr int kSplitMaxTiles = 512;  // 128-row tiles below which the key split is used (2 per CU)
 
 template <int D>
@@ -263,9 +264,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_split_kernel(FwdF32Args p) {
 
   const int i0 = t * kSplitBQ;
   const int i1 = min(N - 1, i0 + kSplitBQ - 1);
-  KeySpan span2{0, -1};
-  if (has_second(dset)) span2 = band_key_span(i0, i1, dset.nlo, dset.nhi);
-  const TileWalk walk = tile_walk(band_key_span(i0, i1, lo, hi), span2, kBK);
+  const TileWalk walk = kernel_walk(kSplitWalk, i0, N, dset);
   if (walk.n == 0) {
     for (int c = tid; c < kSplitBQ * (D / 4); c += kThreads) {
       const int r = c / (D / 4), cc = c % (D / 4);
@@ -453,6 +452,13 @@ int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
 void fwd_f32_tiles(int* BQ, int* BK) {
   *BQ = kBQ;
   *BK = kBK;
+}
+
+// The walk of the float32 forward launch for B * H sequences of N rows (the
+// key-split kernel below 512 tiles of 128 rows, as launch_fwd_f32 decides).
+WalkShape fwd_f32_walk(int B, int H, int N) {
+  const bool split = (long long)B * H * ((N + 127) / 128) < kSplitMaxTiles;
+  return split ? kSplitWalk : kWalk;
 }
 
 }  // namespace spattn

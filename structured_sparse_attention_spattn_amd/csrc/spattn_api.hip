@@ -16,6 +16,12 @@ int launch_decode(const void* q, const void* k, const void* v, void* o, float* l
                   hipStream_t stream);
 void fwd_bf16_tiles(int* BQ, int* BK);
 void fwd_f32_tiles(int* BQ, int* BK);
+WalkShape fwd_bf16_walk();
+WalkShape bwd_bf16_dq_walk();
+WalkShape bwd_bf16_dkdv_walk();
+WalkShape fwd_f32_walk(int B, int H, int N);
+WalkShape bwd_f32_dq_walk(int B, int H, int N);
+WalkShape bwd_f32_dkdv_walk(int B, int H, int N);
 size_t bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int grad_dtype);
 int launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                   void* dq, int B, int H, int N, int d, int dtype, int grad_dtype, const Bands& bands,
@@ -109,6 +115,81 @@ __global__ __launch_bounds__(256) void tile_list_kernel(int N, int lo, int hi, i
   }
 }
 
+// Visit order of one band's walk in the CSR form of spattn_tile_walk, with
+// the kernels' own walk builder (kernel_walk) and tile tests (set_full), by a
+// single workgroup: owned tile t lists the tiles it visits, in visit order.
+__global__ __launch_bounds__(256) void walk_list_kernel(WalkShape ws, int N, DistSet ds, int32_t* ptr,
+                                                         int32_t* tiles, uint8_t* kind, int cap, int32_t* n_out) {
+  const int n_own = (N + ws.own - 1) / ws.own;
+  for (int t = threadIdx.x; t < n_own; t += blockDim.x) ptr[t + 1] = kernel_walk(ws, t * ws.own, N, ds).n;
+  __syncthreads();
+  __threadfence_block();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    ptr[0] = 0;
+    for (int t = 0; t < n_own; ++t) {
+      run += ptr[t + 1];
+      ptr[t + 1] = run;
+    }
+    *n_out = run;
+  }
+  __syncthreads();
+  __threadfence_block();
+  for (int t = threadIdx.x; t < n_own; t += blockDim.x) {
+    const int r0 = t * ws.own, r1 = min(N - 1, r0 + ws.own - 1);
+    const TileWalk w = kernel_walk(ws, r0, N, ds);
+    int pos = ptr[t];
+    for (int v = 0; v < w.n && pos < cap; ++v, ++pos) {
+      const int u = w.at(v);
+      const int a0 = u * ws.tile, a1 = min(N - 1, a0 + ws.tile - 1);
+      const bool full = ws.key_major ? set_full(a0, a1, r0, r1, ds) : set_full(r0, r1, a0, a1, ds);
+      tiles[pos] = u;
+      kind[pos] = full ? 0 : 1;
+    }
+  }
+}
+
+// Table of one of the "Making Every Head Count" Figure 2 attention patterns.
+int pattern_table(int N, int H, int kind, int width, int32_t* lo, int32_t* hi) {
+  switch (kind) {
+    case SPATTN_PATTERN_BDP:
+      bdp_table(N, H, lo, hi);
+      return SPATTN_OK;
+    case SPATTN_PATTERN_SLIDING_WINDOW: {
+      // every head sees the same distances [0, w - 1]; w = 0 leaves them empty
+      if (width < 0) return SPATTN_E_ARG;
+      const int w = width < N ? width : N;
+      for (int h = 0; h < H; ++h) {
+        lo[h] = w == 0 ? N : 0;
+        hi[h] = w == 0 ? N - 1 : w - 1;
+      }
+      return SPATTN_OK;
+    }
+    case SPATTN_PATTERN_GAPPED_HALF: {
+      // the first floor(W_h / 2) distances of each head's partition band
+      bdp_table(N, H, lo, hi);
+      for (int h = 0; h < H; ++h) {
+        const int half = (hi[h] - lo[h] + 1) / 2;
+        if (half == 0) {
+          lo[h] = N;
+          hi[h] = N - 1;
+        } else {
+          hi[h] = lo[h] + half - 1;
+        }
+      }
+      return SPATTN_OK;
+    }
+    case SPATTN_PATTERN_DENSE:
+      for (int h = 0; h < H; ++h) {
+        lo[h] = 0;
+        hi[h] = N - 1;
+      }
+      return SPATTN_OK;
+    default:
+      return SPATTN_E_ARG;
+  }
+}
+
 }  // namespace
 }  // namespace spattn
 
@@ -120,6 +201,11 @@ int spattn_band_table(int32_t N, int32_t H, int32_t* lo, int32_t* hi) {
   if (N < 1 || H < 1 || H > SPATTN_MAX_HEADS || lo == nullptr || hi == nullptr) return SPATTN_E_ARG;
   bdp_table(N, H, lo, hi);
   return SPATTN_OK;
+}
+
+int spattn_band_table_pattern(int32_t N, int32_t H, int32_t kind, int32_t width, int32_t* lo, int32_t* hi) {
+  if (N < 1 || H < 1 || H > SPATTN_MAX_HEADS || lo == nullptr || hi == nullptr) return SPATTN_E_ARG;
+  return pattern_table(N, H, kind, width, lo, hi);
 }
 
 static int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
@@ -334,6 +420,43 @@ int spattn_tile_list(int32_t N, int32_t lo, int32_t hi, int32_t BQ, int32_t BK, 
     fwd_bf16_tiles(&BQ, &BK);
   }
   hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, N, lo, hi, BQ, BK, row_ptr,
+                     tiles, kind, cap, n_out);
+  return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
+}
+
+int spattn_tile_walk(int32_t kernel, int32_t dtype, int32_t B, int32_t H, int32_t N, int32_t lo, int32_t hi,
+                     int32_t local_window, int32_t* ptr, int32_t* tiles, uint8_t* kind, int32_t cap,
+                     int32_t* n_out, int32_t* own_rows, int32_t* tile_rows, void* stream) {
+  if (B < 1 || H < 1 || N < 1 || cap < 0 || local_window < 0 || !ptr || !n_out ||
+      (cap > 0 && (!tiles || !kind)))
+    return SPATTN_E_ARG;
+  if (lo < 0 || hi > N - 1 || lo > hi + 1) return SPATTN_E_ARG;
+  WalkShape ws;
+  if (dtype == SPATTN_BF16) {
+    if (kernel == SPATTN_KERNEL_FWD)
+      ws = fwd_bf16_walk();
+    else if (kernel == SPATTN_KERNEL_BWD_DQ)
+      ws = bwd_bf16_dq_walk();
+    else if (kernel == SPATTN_KERNEL_BWD_DKDV)
+      ws = bwd_bf16_dkdv_walk();
+    else
+      return SPATTN_E_ARG;
+  } else if (dtype == SPATTN_F32) {
+    if (kernel == SPATTN_KERNEL_FWD)
+      ws = fwd_f32_walk(B, H, N);
+    else if (kernel == SPATTN_KERNEL_BWD_DQ)
+      ws = bwd_f32_dq_walk(B, H, N);
+    else if (kernel == SPATTN_KERNEL_BWD_DKDV)
+      ws = bwd_f32_dkdv_walk(B, H, N);
+    else
+      return SPATTN_E_ARG;
+  } else {
+    return SPATTN_E_UNSUPPORTED;
+  }
+  if (own_rows) *own_rows = ws.own;
+  if (tile_rows) *tile_rows = ws.tile;
+  const int w = local_window < N ? local_window : N;
+  hipLaunchKernelGGL(walk_list_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, ws, N, dist_set(lo, hi, w), ptr,
                      tiles, kind, cap, n_out);
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
 }

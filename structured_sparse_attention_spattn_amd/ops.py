@@ -56,29 +56,33 @@ def band_table(N, H):
     return lo, hi
 
 
+def pattern_bands(N, H, kind, width=0):
+    """Band table of an attention pattern from the library
+    (spattn_band_table_pattern): ``kind`` one of _lib.PATTERN_*."""
+    lo = np.zeros(max(H, 0), dtype=np.int32)
+    hi = np.zeros(max(H, 0), dtype=np.int32)
+    st = _lib.load().spattn_band_table_pattern(
+        N, H, int(kind), int(width), lo.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        hi.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    _lib.check(st, "spattn_band_table_pattern")
+    return lo, hi
+
+
 def dense_bands(N, H):
     """Every head sees the whole causal range [0, N-1] (dense causal MHA)."""
-    return np.zeros(H, dtype=np.int32), np.full(H, N - 1, dtype=np.int32)
+    return pattern_bands(N, H, _lib.PATTERN_DENSE)
 
 
 def window_bands(N, H, window):
-    """Sliding-window pattern ("Making Every Head Count", Figure 2(a)): every
+    """Sliding-window pattern ("Making Every Head Count", Figure 2): every
     head covers distances [0, window - 1] (window 0: empty bands)."""
-    w = max(0, min(int(window), N))
-    if w == 0:
-        return np.full(H, N, dtype=np.int32), np.full(H, N - 1, dtype=np.int32)
-    return np.zeros(H, dtype=np.int32), np.full(H, w - 1, dtype=np.int32)
+    return pattern_bands(N, H, _lib.PATTERN_SLIDING_WINDOW, max(0, int(window)))
 
 
 def gapped_half_bands(N, H):
-    """Gapped-bands pattern (same figure, (c)): each head keeps the first half
-    of its Balanced Distance Partitioning band, the half-width rounded down (a
-    width-1 band becomes empty)."""
-    lo, hi = band_table(N, H)
-    half = (hi - lo + 1) // 2
-    lo2 = np.where(half == 0, N, lo).astype(np.int32)
-    hi2 = np.where(half == 0, N - 1, lo + half - 1).astype(np.int32)
-    return lo2, hi2
+    """Gapped-bands pattern (same figure): each head keeps the first half of
+    its Balanced Distance Partitioning band (half-width rounded down)."""
+    return pattern_bands(N, H, _lib.PATTERN_GAPPED_HALF)
 
 
 def fwd(q, k, v, bands=None, scale=None, out=None, lse=None, local_window=0):
@@ -116,6 +120,14 @@ def _varlen_prep(q, cu_seqlens, max_seqlen):
     if not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be contiguous with at least two entries")
     H, T, d = q.shape
+    # The kernels clamp every sequence to the tensors, but a malformed offsets
+    # array would leave rows unwritten: check it once on the host.
+    cu = cu_seqlens.cpu().numpy().astype(np.int64)
+    lens = np.diff(cu)
+    if cu[0] != 0 or cu[-1] != T or np.any(lens < 0):
+        raise ValueError(f"cu_seqlens must rise from 0 to the packed length {T} without decreasing")
+    if int(lens.max()) > int(max_seqlen):
+        raise ValueError(f"a sequence of {int(lens.max())} tokens exceeds max_seqlen = {int(max_seqlen)}")
     return H, T, d, cu_seqlens.numel() - 1, int(max_seqlen)
 
 
@@ -184,8 +196,9 @@ def decode(q, k_cache, v_cache, lengths=None, bands=None, local_window=0, scale=
     for t in (q, k_cache, v_cache):
         if not t.is_contiguous() or not t.is_cuda:
             raise ValueError("tensors must be contiguous and on the GPU")
-    if lengths is not None and (lengths.dtype != torch.int32 or lengths.shape != (B,) or not lengths.is_cuda):
-        raise ValueError("lengths must be an int32 GPU tensor of shape [B]")
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.shape != (B,) or not lengths.is_cuda
+                                or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous int32 GPU tensor of shape [B]")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -292,6 +305,31 @@ def tile_list(N, lo, hi, BQ=0, BK=0, device="cuda"):
     torch.cuda.current_stream(row_ptr.device).synchronize()
     n = int(n_out.item())
     return row_ptr.cpu().numpy(), tiles[:n].cpu().numpy(), kind[:n].cpu().numpy()
+
+
+def tile_walk(kernel, N, lo, hi, dtype=torch.bfloat16, B=1, H=1, local_window=0, device="cuda"):
+    """A kernel's actual tile walk for one band (spattn_tile_walk), as numpy
+    (ptr, tiles, kind, own_rows, tile_rows): owned tile t visits
+    tiles[ptr[t]:ptr[t + 1]] in that order."""
+    own, tile = ctypes.c_int32(), ctypes.c_int32()
+    lib = _lib.load()
+    n_out = torch.zeros(1, dtype=torch.int32, device=device)
+    # sizes first (cap 0 writes only ptr and the count)
+    probe = torch.zeros(N + 1, dtype=torch.int32, device=device)
+    st = lib.spattn_tile_walk(int(kernel), _DT[dtype], B, H, N, lo, hi, int(local_window), _ptr(probe), None, None,
+                              0, _ptr(n_out), ctypes.byref(own), ctypes.byref(tile), _stream_handle(probe.device))
+    _lib.check(st, "spattn_tile_walk")
+    torch.cuda.current_stream(probe.device).synchronize()
+    n = int(n_out.item())
+    n_own = (N + own.value - 1) // own.value
+    ptr = torch.zeros(n_own + 1, dtype=torch.int32, device=device)
+    tiles = torch.zeros(max(n, 1), dtype=torch.int32, device=device)
+    kind = torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+    st = lib.spattn_tile_walk(int(kernel), _DT[dtype], B, H, N, lo, hi, int(local_window), _ptr(ptr), _ptr(tiles),
+                              _ptr(kind), n, _ptr(n_out), None, None, _stream_handle(ptr.device))
+    _lib.check(st, "spattn_tile_walk")
+    torch.cuda.current_stream(ptr.device).synchronize()
+    return (ptr.cpu().numpy(), tiles[:n].cpu().numpy(), kind[:n].cpu().numpy(), own.value, tile.value)
 
 
 class _BandAttention(torch.autograd.Function):

@@ -17,6 +17,12 @@ int main(void) {
   st = spattn_band_table(10, 3, lo3, hi3);  /* widths 4, 3, 3: wider bands first */
   printf("band_table_uneven %d [%d,%d] [%d,%d] [%d,%d]\n", st, lo3[0], hi3[0], lo3[1], hi3[1], lo3[2], hi3[2]);
   printf("band_table_bad %d\n", spattn_band_table(0, 8, lo, hi));
+  int32_t plo[3], phi[3];
+  st = spattn_band_table_pattern(10, 3, SPATTN_PATTERN_GAPPED_HALF, 0, plo, phi);  /* halves of 4, 3, 3 */
+  printf("gapped_half %d [%d,%d] [%d,%d] [%d,%d]\n", st, plo[0], phi[0], plo[1], phi[1], plo[2], phi[2]);
+  st = spattn_band_table_pattern(10, 3, SPATTN_PATTERN_SLIDING_WINDOW, 4, plo, phi);
+  printf("sliding_window %d [%d,%d] [%d,%d] [%d,%d]\n", st, plo[0], phi[0], plo[1], phi[1], plo[2], phi[2]);
+  printf("pattern_bad %d\n", spattn_band_table_pattern(10, 3, 17, 0, plo, phi));
   printf("workspace %zu\n", spattn_bwd_workspace_bytes(2, 3, 100, 128, SPATTN_BF16, SPATTN_BF16));
   printf("workspace_bad %zu\n", spattn_bwd_workspace_bytes(2, 3, 100, 96, SPATTN_BF16, SPATTN_BF16));
   int32_t bq = 0, bk = 0;

@@ -158,8 +158,10 @@ def test_local_window_validation_before_launch():
     assert lib.spattn_fwd_local(ptr0, p, p, p, p, 1, 2, 8, 64, _lib.BF16, None, None, 3, 0.0, None) == _lib.E_ARG
 
 
-@pytest.mark.parametrize("N,H", [(1024, 8), (4096, 16), (7, 3), (5, 9), (10000, 12)])
+@pytest.mark.parametrize("N,H", [(1024, 8), (4096, 16), (7, 3), (5, 9), (10000, 12), (1, 1), (3, 256)])
 def test_pattern_tables_match_oracle(N, H):
+    """The Figure 2 pattern tables come from the library
+    (spattn_band_table_pattern) and equal the oracle's, bit for bit."""
     for w in (0, 1, N // H, N, N + 5):
         lo, hi = ops.window_bands(N, H, w)
         olo, ohi = oracle.band_table_sliding_window(N, H, w)
@@ -167,6 +169,39 @@ def test_pattern_tables_match_oracle(N, H):
     lo, hi = ops.gapped_half_bands(N, H)
     olo, ohi = oracle.band_table_gapped_half(N, H)
     assert np.array_equal(lo, olo) and np.array_equal(hi, ohi)
+    lo, hi = ops.pattern_bands(N, H, _lib.PATTERN_BDP)
+    olo, ohi = oracle.band_table(N, H)
+    assert np.array_equal(lo, olo) and np.array_equal(hi, ohi)
+    lo, hi = ops.dense_bands(N, H)
+    assert np.all(lo == 0) and np.all(hi == N - 1)
+
+
+def test_pattern_table_rejects_bad_args():
+    lib = _lib.load()
+    buf = (ctypes.c_int32 * 4)()
+    assert lib.spattn_band_table_pattern(8, 4, 9, 0, buf, buf) == _lib.E_ARG             # unknown kind
+    assert lib.spattn_band_table_pattern(8, 4, _lib.PATTERN_SLIDING_WINDOW, -1, buf, buf) == _lib.E_ARG
+    assert lib.spattn_band_table_pattern(0, 4, _lib.PATTERN_BDP, 0, buf, buf) == _lib.E_ARG
+    assert lib.spattn_band_table_pattern(8, 257, _lib.PATTERN_BDP, 0, buf, buf) == _lib.E_ARG
+    assert lib.spattn_band_table_pattern(8, 4, _lib.PATTERN_DENSE, 0, None, buf) == _lib.E_ARG
+
+
+def test_tile_walk_validation():
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+
+    def walk(kernel=0, dtype=_lib.BF16, B=1, H=1, N=10, lo=0, hi=5, w=0, ptr=p, cap=4):
+        return lib.spattn_tile_walk(kernel, dtype, B, H, N, lo, hi, w, ptr, p, p, cap, p, None, None, None)
+    assert walk(kernel=3) == _lib.E_ARG
+    assert walk(kernel=-1) == _lib.E_ARG
+    assert walk(dtype=4) == _lib.E_UNSUPPORTED
+    assert walk(N=0) == _lib.E_ARG
+    assert walk(B=0) == _lib.E_ARG
+    assert walk(hi=10) == _lib.E_ARG
+    assert walk(lo=7, hi=5) == _lib.E_ARG
+    assert walk(w=-1) == _lib.E_ARG
+    assert walk(ptr=None) == _lib.E_ARG
+    assert walk(cap=-1) == _lib.E_ARG
 
 
 def test_decode_validation_before_launch():

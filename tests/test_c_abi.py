@@ -33,6 +33,9 @@ def test_c_program_uses_the_abi(tmp_path):
     assert lines["band_table"] == want
     assert lines["band_table_uneven"] == "0 [0,3] [4,6] [7,9]"
     assert lines["band_table_bad"] == str(_lib.E_ARG)
+    assert lines["gapped_half"] == "0 [0,1] [4,4] [7,7]"
+    assert lines["sliding_window"] == "0 [0,3] [0,3] [0,3]"
+    assert lines["pattern_bad"] == str(_lib.E_ARG)
     assert int(lines["workspace"]) == lib.spattn_bwd_workspace_bytes(2, 3, 100, 128, _lib.BF16, _lib.BF16) > 0
     assert lines["workspace_bad"] == "0"
     assert lines["tiles"].split()[0] == "0"

@@ -5,7 +5,7 @@ Source of the variant: "Making Every Head Count", Figure 2 caption (the
 exclusive-band ablation is the method with local sharing removed); the window
 width is a parameter (not given on the page).  Bars as elsewhere: bfloat16
 outputs and gradients within 2e-2 max-abs and 1e-2 relative L2, -inf LSE
-positions identical; gradients of the full workload on sampled rows.
+positions identical.  The full workload is compared on whole tensors.
 """
 import math
 import sys
@@ -36,6 +36,7 @@ def _check(got, ref, what):
     err = float(np.max(np.abs(got - ref))) if got.size else 0.0
     den = np.linalg.norm(ref)
     rel = np.linalg.norm(got - ref) / den if den > 0 else np.linalg.norm(got)
+    _say(f"  {what}: max-abs {err:.3e}  rel-L2 {rel:.3e}")
     assert err <= TOL and rel <= REL, f"{what}: max-abs {err:.3e}, rel-L2 {rel:.3e}"
 
 
@@ -118,15 +119,9 @@ def test_zero_window_is_the_plain_entry_point():
 FULL = dict(B=8, H=16, N=4096, d=128, w=64, seed=1005)
 
 
-def _sample_rows(N, lo, hi, w, rng):
-    rows = {0, 1, w - 1, w, w + 1, lo - 1, lo, lo + 1, min(N - 1, hi), min(N - 1, hi + 1), 127, 128, N // 2, N - 1}
-    rows |= set(rng.integers(0, N, 3).tolist())
-    return sorted(r for r in rows if 0 <= r < N)
-
-
-def test_local_full_workload_sampled_and_invariants():
+def test_local_full_workload_whole_and_invariants():
     B, H, N, d, w = FULL["B"], FULL["H"], FULL["N"], FULL["d"], FULL["w"]
-    _say(f"local window full workload B={B} H={H} N={N} d={d} w={w}")
+    _say(f"local window full workload B={B} H={H} N={N} d={d} w={w} (whole tensors)")
     inp = make_inputs(B, H, N, d, dtype="bf16", seed=FULL["seed"], with_dout=True)
     x = {n: t.to(DEV) for n, t in inp.items()}
     o, lse = ops.fwd(x["q"], x["k"], x["v"], local_window=w)
@@ -134,29 +129,23 @@ def test_local_full_workload_sampled_and_invariants():
     torch.cuda.synchronize()
     lo, hi = oracle.band_table(N, H)
     o_h, lse_h = o.float().cpu().numpy(), lse.cpu().numpy()
-    dq_h, dk_h, dv_h = (t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
+    dq_h, dk_h, dv_h = (t.cpu().numpy() for t in (dq, dk, dv))
+    del x, o, lse, dq, dk, dv
     assert not np.any(np.isneginf(lse_h))  # the window gives every row at least its diagonal
-    do = inp["dout"].double().numpy()
+    do = as_f64(inp["dout"])
     for h in range(H):
-        sk = dk_h[:, h].sum(axis=1)  # sum_j dK_j = 0 per (b, feature)
+        sk = dk_h[:, h].astype(np.float64).sum(axis=1)  # sum_j dK_j = 0 per (b, feature)
         assert np.max(np.abs(sk)) <= 2e-2 * max(1.0, np.max(np.abs(dk_h[:, h])) * math.sqrt(N)), h
-        sv = dv_h[:, h].sum(axis=1)  # every row is non-empty: sum_j dV_j = sum_i dO_i
+        sv = dv_h[:, h].astype(np.float64).sum(axis=1)  # every row is non-empty: sum_j dV_j = sum_i dO_i
         ref_sv = do[:, h].sum(axis=1)
         assert np.max(np.abs(sv - ref_sv)) <= 2e-2 * max(1.0, np.max(np.abs(ref_sv))), h
-    rng = np.random.default_rng(7)
-    q64, k64, v64, d64 = (inp[n].float().numpy() for n in ("q", "k", "v", "dout"))
-    for b in (0, B - 1):
-        for h in (0, 1, H // 2, H - 1):
-            rows = _sample_rows(N, int(lo[h]), int(hi[h]), w, rng)
-            ro, rl = oracle.band_attention_fwd_rows(q64, k64, v64, lo, hi, b, h, rows, local_window=w)
-            _check(o_h[b, h, rows], ro, f"O b={b} h={h}")
-            _check_lse(lse_h[b, h, rows], rl, f"LSE b={b} h={h}")
-            qr = rows[:8]
-            kr = sorted({0, w - 1, 127, 128, N - 1 - int(lo[h]), N - 1, int(rng.integers(0, N))})
-            rq, rk, rv = oracle.band_attention_bwd_rows(q64, k64, v64, d64, lo, hi, b, h, qr, kr, local_window=w)
-            for got, ref, nm in ((dq_h[b, h, qr], rq, "dQ"), (dk_h[b, h, kr], rk, "dK"), (dv_h[b, h, kr], rv, "dV")):
-                err = np.max(np.abs(got - ref))
-                assert err <= TOL, f"{nm} b={b} h={h}: max-abs {err:.3e}"
+    rq, rk, rv, ro, rl = oracle.band_attention_bwd(*(as_f64(inp[n]) for n in ("q", "k", "v", "dout")), lo, hi,
+                                                   local_window=w)
+    _check(o_h, ro, "O")
+    _check_lse(lse_h, rl, "LSE")
+    _check(dq_h, rq, "dQ")
+    _check(dk_h, rk, "dK")
+    _check(dv_h, rv, "dV")
 
 
 def test_local_full_closed_form_zero_queries():

@@ -4,9 +4,13 @@ oracle on the same seeded inputs.
 Bars (stated per test): band tables and tile lists bit-exact; float32
 outputs within 1e-4 max-abs; bfloat16 outputs and gradients within 2e-2
 max-abs and 1e-2 relative L2; the positions of LSE = -inf identical.
-Small shapes are compared element by element; the full workload sizes are
-compared on sampled rows the oracle computes one by one, plus properties that
-hold at any size (empty-row positions, a closed form, gradient sums).
+Small shapes and every full workload size (the N = 1024 float32 forward,
+the N = 4096, 8192 and 10000 bfloat16 forwards, and the N = 4096 forward +
+backward) are compared element by element on whole tensors, three seeds
+each; a longer sequence (N = 32768) is compared on rows the oracle computes
+one by one, drawn inside every head's band, plus properties that hold at any
+size (empty-row positions, a closed form, gradient sums).  Every check prints
+its max-abs and relative-L2 error, so the margin to the bar is visible.
 """
 import math
 import sys
@@ -42,16 +46,19 @@ def _rel_l2(got, ref):
 
 
 def _check(got, ref, dtype, what):
+    """Both bars on one array; prints and returns (max-abs, relative L2)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    rel = float(_rel_l2(got, ref)) if got.size else 0.0
+    _say(f"  {what}: max-abs {err:.3e}  rel-L2 {rel:.3e}")
     if dtype == "f32":
         assert err <= F32_TOL, f"{what}: max-abs {err:.3e} > {F32_TOL}"
     else:
-        rel = _rel_l2(got, ref)
         assert err <= BF16_TOL and rel <= BF16_REL, f"{what}: max-abs {err:.3e}, rel-L2 {rel:.3e}"
-    return err
+    return err, rel
 
 
 def _check_lse(got, ref, dtype, what):
@@ -62,6 +69,7 @@ def _check_lse(got, ref, dtype, what):
     fin = ~ri
     if fin.any():
         err = float(np.max(np.abs(got[fin] - ref[fin])))
+        _say(f"  {what}: max-abs {err:.3e} over {int(fin.sum())} finite rows, {int(ri.sum())} -inf rows")
         tol = F32_TOL if dtype == "f32" else BF16_TOL
         assert err <= tol, f"{what}: LSE max-abs {err:.3e}"
 
@@ -115,6 +123,53 @@ def test_tile_lists_bit_exact():
         assert np.array_equal(kd, okd), (N, lo_, hi_, BQ, BK)
 
 
+def _walk_cases():
+    cases = []
+    for idx, w in WORKLOADS.items():
+        lo, hi = oracle.band_table(w["N"], w["H"])
+        for h in range(w["H"]):
+            cases.append((w["B"], w["H"], w["N"], int(lo[h]), int(hi[h]), 0))
+        cases.append((w["B"], w["H"], w["N"], int(lo[-1]), int(hi[-1]), 64))
+        cases.append((w["B"], w["H"], w["N"], int(lo[1]), int(hi[1]), int(lo[1])))  # window touching the band
+    for N in (1, 5, 64, 129, 300, 1000):
+        for (lo_, hi_) in [(0, N - 1), (0, 0), (N - 1, N - 1), (N // 3, N // 2), (N, N - 1)]:
+            for w in (0, 1, 17, N // 2 + 3):
+                cases.append((1, 1, N, lo_, hi_, w))
+                cases.append((8, 16, N, lo_, hi_, w))  # float32: the larger launches' tiles
+    return cases
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("kernel", [0, 1, 2])
+def test_tile_walks_are_the_canonical_lists(kernel, dtype):
+    """Each kernel's actual walk (spattn_tile_walk runs the kernels' walk
+    builder on the device), for every head of every workload and for small
+    bands with and without a shared local window: the tiles an owned tile
+    visits are exactly the oracle's list for it, each once, with the same
+    FULL / PARTIAL kinds, and in an order that is a rotation of the ascending
+    list."""
+    key_major = kernel == 2
+    cases = _walk_cases()
+    _say(f"tile walks kernel={kernel} {dtype}: {len(cases)} cases")
+    for B, H, N, lo_, hi_, w in cases:
+        ptr, tl, kd, own, tile = ops.tile_walk(kernel, N, lo_, hi_, dtype=dtype, B=B, H=H, local_window=w)
+        if key_major:
+            optr, otl, okd = oracle.key_tile_list(N, lo_, hi_, tile, own, local_window=w)
+        else:
+            optr, otl, okd = oracle.query_tile_list(N, lo_, hi_, own, tile, local_window=w)
+        assert np.array_equal(np.diff(ptr), np.diff(optr)), (kernel, B, H, N, lo_, hi_, w)
+        for t in range(len(ptr) - 1):
+            seq = tl[ptr[t]:ptr[t + 1]].tolist()
+            kinds = dict(zip(seq, kd[ptr[t]:ptr[t + 1]].tolist()))
+            ref = otl[optr[t]:optr[t + 1]].tolist()
+            ref_k = dict(zip(ref, okd[optr[t]:optr[t + 1]].tolist()))
+            assert len(set(seq)) == len(seq) and sorted(seq) == ref, (kernel, N, lo_, hi_, w, t, seq, ref)
+            assert kinds == ref_k, (kernel, N, lo_, hi_, w, t)
+            if seq:
+                r = seq.index(ref[0])
+                assert seq[r:] + seq[:r] == ref, (kernel, N, lo_, hi_, w, t, seq)  # a rotation of ascending
+
+
 # ------------------------------------------------------------------ forward, small
 
 
@@ -157,38 +212,34 @@ def test_fwd_small_vs_oracle(B, H, N, d, dtype, bk, seed, qs):
 # ------------------------------------------------------------------ forward, full workloads
 
 
-def _sample_rows(N, lo, hi, rng, bq=128):
-    rows = {0, N - 1, lo, lo - 1, lo + 1, min(N - 1, hi), min(N - 1, hi + 1), bq - 1, bq, N // 2}
-    rows |= set(rng.integers(0, N, 4).tolist())
-    return sorted(r for r in rows if 0 <= r < N)
+SEED_OFFSETS = (0, 100, 200)
 
 
+@pytest.mark.parametrize("off", SEED_OFFSETS)
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
-def test_fwd_full_workload_sampled(idx):
+def test_fwd_full_workload_whole(idx, off):
+    """The forward at every full workload size against the whole-workload
+    float64 oracle, every element of O and LSE, three seeds."""
     w = WORKLOADS[idx]
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
-    _say(f"fwd full workload {w['name']}")
-    inp = make_inputs(B, H, N, d, dtype=w["dtype"], seed=seed_for(idx), scale=w["scale"])
+    seed = seed_for(idx) + off
+    _say(f"fwd full workload {w['name']} seed={seed} (whole tensors)")
+    inp = make_inputs(B, H, N, d, dtype=w["dtype"], seed=seed, scale=w["scale"])
     o, lse = _run_fwd(inp, None)
-    lo, hi = oracle.band_table(N, H)
-    lse_h = lse.cpu().numpy()
-    # empty rows are exactly the rows before each band's start
-    empty = np.arange(N)[None, None, :] < lo[None, :, None]
-    assert np.array_equal(np.isneginf(lse_h), np.broadcast_to(empty, lse_h.shape))
     o_h = o.float().cpu().numpy()
-    assert np.all(o_h[np.broadcast_to(empty, lse_h.shape)] == 0)
-    q64, k64, v64 = (inp[n].float().numpy() for n in ("q", "k", "v"))
-    rng = np.random.default_rng(idx)
-    bq, _ = ops.kernel_tiles(d, torch.bfloat16 if w["dtype"] == "bf16" else torch.float32)
-    for b in sorted({0, B - 1}):
-        for h in range(H):
-            rows = _sample_rows(N, int(lo[h]), int(hi[h]), rng, bq)
-            ro, rl = oracle.band_attention_fwd_rows(q64, k64, v64, lo, hi, b, h, rows)
-            _check(o_h[b, h, rows], ro, w["dtype"], f"O b={b} h={h}")
-            _check_lse(lse_h[b, h, rows], rl, w["dtype"], f"LSE b={b} h={h}")
+    lse_h = lse.cpu().numpy()
+    del o, lse
+    lo, hi = oracle.band_table(N, H)
+    # empty rows are exactly the rows before each band's start, with O = 0
+    empty = np.broadcast_to(np.arange(N)[None, None, :] < lo[None, :, None], lse_h.shape)
+    assert np.array_equal(np.isneginf(lse_h), empty)
+    assert np.all(o_h[empty] == 0)
+    ro, rl = oracle.band_attention_fwd(as_f64(inp["q"]), as_f64(inp["k"]), as_f64(inp["v"]), lo, hi)
+    _check(o_h, ro, w["dtype"], "O")
+    _check_lse(lse_h, rl, w["dtype"], "LSE")
 
 
-@pytest.mark.parametrize("idx", [2, 4])
+@pytest.mark.parametrize("idx", [2, 3, 4])
 def test_fwd_full_closed_form_zero_queries(idx):
     """Q = 0 at full size: O_i is the mean of v_j over the band window and
     LSE_i = ln |S_i| -- checked on every row via prefix sums."""
@@ -264,51 +315,55 @@ def test_bwd_small_vs_oracle(B, H, N, d, dtype, gdt, bk, seed):
     _check(dv.float().cpu().numpy(), rv, tol_kind, "dV")
 
 
-def test_bwd_full_workload_sampled_and_invariants():
+@pytest.mark.parametrize("off", SEED_OFFSETS)
+def test_bwd_full_workload_whole(off):
+    """The forward + backward workload (B = 8, H = 16, N = 4096, d = 128):
+    O, LSE, dQ, dK and dV against the whole-workload float64 oracle, every
+    element, with the gradients written as float32 and as bfloat16; plus the
+    structural invariants (exact zeros outside the band, gradient sums)."""
     w = WORKLOADS[5]
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
-    _say(f"bwd full workload {w['name']}")
-    inp = make_inputs(B, H, N, d, dtype="bf16", seed=seed_for(5), with_dout=True)
+    seed = seed_for(5) + off
+    _say(f"bwd full workload {w['name']} seed={seed} (whole tensors)")
+    inp = make_inputs(B, H, N, d, dtype="bf16", seed=seed, with_dout=True)
     dv_ = _to_dev(inp)
     o, lse = ops.fwd(dv_["q"], dv_["k"], dv_["v"])
-    dq, dk, dv = ops.bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dv_["dout"], grad_dtype=torch.float32)
-    dq16, dk16, dv16 = ops.bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dv_["dout"])
+    g32 = ops.bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dv_["dout"], grad_dtype=torch.float32)
+    g16 = ops.bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dv_["dout"])
     torch.cuda.synchronize()
+    o_h, lse_h = o.float().cpu().numpy(), lse.cpu().numpy()
+    g32_h = [x.cpu().numpy() for x in g32]
+    g16_h = [x.float().cpu().numpy() for x in g16]
+    del dv_, o, lse, g32, g16
     lo, hi = oracle.band_table(N, H)
-    dq_h, dk_h, dv_h = (x.cpu().numpy().astype(np.float64) for x in (dq, dk, dv))
-    dq16_h, dk16_h, dv16_h = (x.float().cpu().numpy().astype(np.float64) for x in (dq16, dk16, dv16))
-    do = inp["dout"].double().numpy()
+    rq, rk, rv, ro, rl = oracle.band_attention_bwd(*(as_f64(inp[n]) for n in ("q", "k", "v", "dout")), lo, hi)
+    _check(o_h, ro, "bf16", "O")
+    _check_lse(lse_h, rl, "bf16", "LSE")
+    for (gq, gk, gv), tag in ((g32_h, "f32 out"), (g16_h, "bf16 out")):
+        _check(gq, rq, "bf16", f"dQ ({tag})")
+        _check(gk, rk, "bf16", f"dK ({tag})")
+        _check(gv, rv, "bf16", f"dV ({tag})")
+    dq_h, dk_h, dv_h = g32_h
+    do = as_f64(inp["dout"])
     empty_rows = np.arange(N)[None, :] < lo[:, None]           # [H, N]
     never_keys = np.arange(N)[None, :] > (N - 1 - lo)[:, None]  # keys no query of the head reaches
     for h in range(H):
         assert np.all(dq_h[:, h][:, empty_rows[h]] == 0)
         assert np.all(dk_h[:, h][:, never_keys[h]] == 0) and np.all(dv_h[:, h][:, never_keys[h]] == 0)
         # sum_j dK_j = 0 and sum_j dV_j = sum of dO over non-empty rows
-        sk = dk_h[:, h].sum(axis=1)
+        sk = dk_h[:, h].astype(np.float64).sum(axis=1)
         assert np.max(np.abs(sk)) <= 2e-2 * max(1.0, np.max(np.abs(dk_h[:, h])) * math.sqrt(N)), h
-        sv = dv_h[:, h].sum(axis=1)
+        sv = dv_h[:, h].astype(np.float64).sum(axis=1)
         ref_sv = do[:, h][:, ~empty_rows[h]].sum(axis=1)
         assert np.max(np.abs(sv - ref_sv)) <= 2e-2 * max(1.0, np.max(np.abs(ref_sv))), h
-    rng = np.random.default_rng(5)
-    q64, k64, v64, d64 = (inp[n].float().numpy() for n in ("q", "k", "v", "dout"))
-    for b in (0, B - 1):
-        for h in (0, 1, H // 2, H - 1):
-            rows = _sample_rows(N, int(lo[h]), int(hi[h]), rng)[:8]
-            krows = sorted({0, 127, 128, N - 1 - int(lo[h]), max(0, N - 2 - int(lo[h])), int(rng.integers(0, N))})
-            rq, rk, rv = oracle.band_attention_bwd_rows(q64, k64, v64, d64, lo, hi, b, h, rows, krows)
-            for got, ref, nm in ((dq_h[b, h, rows], rq, "dQ"), (dk_h[b, h, krows], rk, "dK"),
-                                 (dv_h[b, h, krows], rv, "dV"), (dq16_h[b, h, rows], rq, "dQ bf16"),
-                                 (dk16_h[b, h, krows], rk, "dK bf16"), (dv16_h[b, h, krows], rv, "dV bf16")):
-                err = np.max(np.abs(got - ref))
-                assert err <= BF16_TOL, f"{nm} b={b} h={h}: max-abs {err:.3e}"
 
 
-def test_long_sequence_sampled():
+def test_long_sequence_whole():
     """A long sequence (N = 32768, eight heads: bands 4096 wide, 66 key tiles
-    per query tile): forward and both gradients on sampled rows, each row from
-    the definition, plus the empty-row positions on every row."""
+    per query tile): O, LSE and the three gradients against the float64
+    oracle on whole tensors, plus the empty-row positions."""
     B, H, N, d = 1, 8, 32768, 128
-    _say(f"long sequence B={B} H={H} N={N} d={d}")
+    _say(f"long sequence B={B} H={H} N={N} d={d} (whole tensors)")
     inp = make_inputs(B, H, N, d, dtype="bf16", seed=4242, with_dout=True)
     dv_ = _to_dev(inp)
     o, lse = ops.fwd(dv_["q"], dv_["k"], dv_["v"])
@@ -319,21 +374,14 @@ def test_long_sequence_sampled():
     empty = np.arange(N)[None, None, :] < lo[None, :, None]
     assert np.array_equal(np.isneginf(lse_h), np.broadcast_to(empty, lse_h.shape))
     o_h = o.float().cpu().numpy()
-    dq_h, dk_h, dv_h = (x.cpu().numpy().astype(np.float64) for x in (dq, dk, dv))
-    q64, k64, v64, d64 = (inp[n].float().numpy() for n in ("q", "k", "v", "dout"))
-    rng = np.random.default_rng(4242)
-    for h in range(H):
-        rows = _sample_rows(N, int(lo[h]), int(hi[h]), rng)
-        ro, rl = oracle.band_attention_fwd_rows(q64, k64, v64, lo, hi, 0, h, rows)
-        _check(o_h[0, h, rows], ro, "bf16", f"O h={h}")
-        _check_lse(lse_h[0, h, rows], rl, "bf16", f"LSE h={h}")
-    for h in (0, H - 1):
-        rows = _sample_rows(N, int(lo[h]), int(hi[h]), rng)[:6]
-        krows = sorted({int(rng.integers(0, N - int(lo[h]))), N - 1 - int(lo[h])})
-        rq, rk, rv = oracle.band_attention_bwd_rows(q64, k64, v64, d64, lo, hi, 0, h, rows, krows)
-        for got, ref, nm in ((dq_h[0, h, rows], rq, "dQ"), (dk_h[0, h, krows], rk, "dK"), (dv_h[0, h, krows], rv, "dV")):
-            err = np.max(np.abs(got - ref))
-            assert err <= BF16_TOL, f"{nm} h={h}: max-abs {err:.3e}"
+    dq_h, dk_h, dv_h = (x.cpu().numpy() for x in (dq, dk, dv))
+    del dv_, o, lse, dq, dk, dv
+    rq, rk, rv, ro, rl = oracle.band_attention_bwd(*(as_f64(inp[n]) for n in ("q", "k", "v", "dout")), lo, hi)
+    _check(o_h, ro, "bf16", "O")
+    _check_lse(lse_h, rl, "bf16", "LSE")
+    _check(dq_h, rq, "bf16", "dQ")
+    _check(dk_h, rk, "bf16", "dK")
+    _check(dv_h, rv, "bf16", "dV")
 
 
 def test_full_workload_repeatable_bitwise():
