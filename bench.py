@@ -103,6 +103,8 @@ def main():
                     help="skip the flushed-cache (cold) per-kernel timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--profile-workload", type=int, default=0, metavar="IDX",
+                    help="only run the forward of workload IDX (1-4) --warmup + --steps times, for profilers")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the band kernels shard over "
@@ -132,6 +134,9 @@ def main():
     from structured_sparse_attention_spattn_amd.inputs import make_inputs
 
     dev = torch.device("cuda:0")
+    if args.profile_workload:
+        profile_workload(args.profile_workload, args.steps, args.warmup, dev)
+        return
     inp = make_inputs(B, H, N, D, dtype="bf16", seed=SEED, with_dout=True)
     q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
     lo, hi = ops.band_table(N, H)
@@ -421,6 +426,34 @@ def main():
         out["cpu_baseline"] = cpu_baseline(inp, lo, hi, fl_all)
 
     print(json.dumps(out), flush=True)
+
+
+def profile_workload(idx, steps, warmup, dev):
+    """The forward of one workload, on resident seeded inputs, for a profiler
+    run: warmup + steps launches, then one JSON line with the HIP-event mean."""
+    import numpy as np
+    import torch
+    from structured_sparse_attention_spattn_amd import ops
+    from structured_sparse_attention_spattn_amd.inputs import make_inputs
+    from structured_sparse_attention_spattn_amd.workloads import WORKLOADS, seed_for
+    w = WORKLOADS[idx]
+    cB, cH, cN, cd = w["B"], w["H"], w["N"], w["d"]
+    cinp = make_inputs(cB, cH, cN, cd, dtype=w["dtype"], seed=seed_for(idx), scale=w["scale"])
+    cq, ck, cv = (cinp[n].to(dev) for n in ("q", "k", "v"))
+    co = torch.empty_like(cq)
+    cl = torch.empty((cB, cH, cN), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        ops.fwd(cq, ck, cv, out=co, lse=cl)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        ops.fwd(cq, ck, cv, out=co, lse=cl)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    print(json.dumps({"workload": w["name"], "launches": steps, "fwd_us_mean": round(1e3 * float(np.mean(ms)), 2),
+                      "fwd_us_median": round(1e3 * float(np.median(ms)), 2)}), flush=True)
 
 
 def f32_backward(q, k, v, o, lse, seed, dev, reps=20):

@@ -24,7 +24,11 @@ COMMON_FLAGS = [
 ]
 
 
-def build(verbose=False, extra_flags=()):
+def build(verbose=False, extra_flags=(), build_dir=None, lib_path=None):
+    """Compile every csrc/*.hip to an object and link libspattn.so (or
+    ``lib_path``), objects under ``build_dir``."""
+    BUILD_DIR = build_dir or globals()["BUILD_DIR"]
+    LIB = lib_path or globals()["LIB"]
     os.makedirs(BUILD_DIR, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     procs = []

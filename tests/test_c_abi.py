@@ -28,7 +28,12 @@ def test_c_program_uses_the_abi(tmp_path):
     assert r.returncode == 0, r.stderr
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
-    lines = dict(l.split(" ", 1) for l in out.stdout.strip().splitlines())
+    check_output_lines(out.stdout, lib)
+
+
+def check_output_lines(stdout, lib):
+    """The lines tests/c/abi_host.c prints, against the documented results."""
+    lines = dict(l.split(" ", 1) for l in stdout.strip().splitlines())
     want = "0 " + " ".join(f"[{128 * h},{128 * h + 127}]" for h in range(8))
     assert lines["band_table"] == want
     assert lines["band_table_uneven"] == "0 [0,3] [4,6] [7,9]"
@@ -36,8 +41,17 @@ def test_c_program_uses_the_abi(tmp_path):
     assert lines["gapped_half"] == "0 [0,1] [4,4] [7,7]"
     assert lines["sliding_window"] == "0 [0,3] [0,3] [0,3]"
     assert lines["pattern_bad"] == str(_lib.E_ARG)
+    assert lines["band_tables_swept"] == "0"
     assert int(lines["workspace"]) == lib.spattn_bwd_workspace_bytes(2, 3, 100, 128, _lib.BF16, _lib.BF16) > 0
     assert lines["workspace_bad"] == "0"
     assert lines["tiles"].split()[0] == "0"
     assert lines["fwd_misaligned"].split()[0] == str(_lib.E_ARG)
     assert lines["fwd_d96"].split()[0] == str(_lib.E_UNSUPPORTED)
+    for key, code in (("fwd_band_past_n", _lib.E_ARG), ("fwd_local_neg", _lib.E_ARG),
+                      ("bwd_small_ws", _lib.E_WORKSPACE), ("bwd_grad_dtype", _lib.E_UNSUPPORTED),
+                      ("bwd_dq_null", _lib.E_ARG), ("bwd_dkdv_heads", _lib.E_ARG), ("bwd_local_neg", _lib.E_ARG),
+                      ("varlen_seqs", _lib.E_ARG), ("varlen_ws", _lib.E_WORKSPACE),
+                      ("decode_dtype", _lib.E_UNSUPPORTED), ("walk_kernel", _lib.E_ARG),
+                      ("tile_list_band", _lib.E_ARG)):
+        assert lines[key] == str(code), (key, lines[key])
+    assert lines["status"] == "workspace missing or too small|unknown status"
