@@ -61,6 +61,37 @@ def _check(got, ref, dtype, what):
     return err, rel
 
 
+def _check_stored_bf16(got16, got32, ref, what):
+    """A gradient written as bfloat16 (grad_dtype = the input dtype) against
+    the oracle.  The kernels compute it exactly as the float32-output run
+    (grad_dtype = float32) and only round at the store, so: the bfloat16
+    array must be, bit for bit, the round-to-nearest-even of the float32
+    array (an integer-exact check), and the float32 array must meet both
+    bars.  Both bars are then also applied to the bfloat16 array; an element
+    beyond 2e-2 there can only be the storage rounding of an element within
+    it (half an ulp of bfloat16: 2^-8 relative, 0.0156 on [4, 8)), and such
+    elements are counted and printed rather than failed.  Relative L2 is
+    never exempt."""
+    g16 = torch.as_tensor(np.ascontiguousarray(got16)).to(torch.bfloat16)
+    r32 = torch.as_tensor(np.ascontiguousarray(got32), dtype=torch.float32).to(torch.bfloat16)
+    assert torch.equal(g16.view(torch.int16), r32.view(torch.int16)), f"{what}: not the rounding of the float32 result"
+    _check(got32, ref, "bf16", f"{what} (float32 before the store)")
+    g = g16.float().numpy().astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(g - ref)
+    rel = float(_rel_l2(g, ref))
+    over = err > BF16_TOL
+    half_ulp = np.ldexp(1.0, np.frexp(np.abs(g))[1] - 9)  # half an ulp of bf16 at |g|
+    n_over = int(over.sum())
+    msg = f"  {what}: max-abs {float(err.max()):.3e}  rel-L2 {rel:.3e}"
+    if n_over:
+        msg += (f"  ({n_over} element(s) beyond 2e-2 by storage rounding only: |ref| {np.abs(ref[over]).min():.3f}"
+                f"..{np.abs(ref[over]).max():.3f}, excess <= half-ulp: {bool(np.all(err[over] <= BF16_TOL + half_ulp[over]))})")
+    _say(msg)
+    assert rel <= BF16_REL, f"{what}: rel-L2 {rel:.3e}"
+    assert np.all(err[over] <= BF16_TOL + half_ulp[over]), what
+
+
 def _check_lse(got, ref, dtype, what):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -339,10 +370,9 @@ def test_bwd_full_workload_whole(off):
     rq, rk, rv, ro, rl = oracle.band_attention_bwd(*(as_f64(inp[n]) for n in ("q", "k", "v", "dout")), lo, hi)
     _check(o_h, ro, "bf16", "O")
     _check_lse(lse_h, rl, "bf16", "LSE")
-    for (gq, gk, gv), tag in ((g32_h, "f32 out"), (g16_h, "bf16 out")):
-        _check(gq, rq, "bf16", f"dQ ({tag})")
-        _check(gk, rk, "bf16", f"dK ({tag})")
-        _check(gv, rv, "bf16", f"dV ({tag})")
+    for got32, got16, ref, nm in zip(g32_h, g16_h, (rq, rk, rv), ("dQ", "dK", "dV")):
+        _check(got32, ref, "bf16", f"{nm} (float32 out)")
+        _check_stored_bf16(got16, got32, ref, f"{nm} (bfloat16 out)")
     dq_h, dk_h, dv_h = g32_h
     do = as_f64(inp["dout"])
     empty_rows = np.arange(N)[None, :] < lo[:, None]           # [H, N]
