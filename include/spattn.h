@@ -26,8 +26,9 @@
  * - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *   are asynchronous: the status covers argument checks and the launch only;
  *   faults during execution surface at the caller's next synchronisation.
- * - The library allocates no device memory.  It keeps no mutable global
- *   state, so calls on different streams may run concurrently.
+ * - The library allocates no device memory.  Apart from the workspace array
+ *   of spattn_bwd_noalloc (see there) it keeps no mutable global state, so
+ *   calls on different streams may run concurrently.
  * - Score scale: scale <= 0 selects 1/sqrt(d).
  * - A query row whose key set is empty gets output 0 and LSE = -inf; it and
  *   any key no query reaches get zero gradients.
@@ -330,6 +331,36 @@ int spattn_tile_walk(int32_t kernel, int32_t dtype, int32_t B, int32_t H, int32_
                      int32_t lo, int32_t hi, int32_t local_window, int32_t* ptr,
                      int32_t* tiles, uint8_t* kind, int32_t cap, int32_t* n_out,
                      int32_t* own_rows, int32_t* tile_rows, void* stream);
+
+/*
+ * Size of the device array that spattn_bwd_noalloc uses as its workspace
+ * (16 MiB per GPU): spattn_bwd_workspace_bytes(B, H, N, d, dtype, grad_dtype)
+ * must not exceed it, i.e. B * H * N <= 2,097,152 rows (two float32 row
+ * vectors, each rounded up to 256 bytes).
+ */
+#define SPATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * spattn_bwd for callers that cannot allocate device memory (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, same arguments minus the workspace, which
+ * is a static array of SPATTN_NOALLOC_SCRATCH_BYTES in the library's device
+ * code instead of a caller buffer.  Each GPU the library runs on holds its
+ * own copy of that array until the process ends; its device address is
+ * looked up on the first call on a device (with that device current) and
+ * reused.  The call allocates nothing and needs no cleared memory (the first
+ * stage writes every value the second reads).  All calls on one GPU share
+ * its array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race on it and must be serialised by the caller.
+ * Errors: as spattn_bwd; SPATTN_E_WORKSPACE when the sizes need more than
+ * SPATTN_NOALLOC_SCRATCH_BYTES (checked before any device call);
+ * SPATTN_E_HIP if the array's address cannot be obtained.
+ */
+int spattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype,
+                       int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi,
+                       float scale, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* spattn_status_string(int status);

@@ -14,13 +14,14 @@ F32, BF16 = 0, 1
 MAX_HEADS = 256
 PATTERN_BDP, PATTERN_SLIDING_WINDOW, PATTERN_GAPPED_HALF, PATTERN_DENSE = 0, 1, 2, 3
 KERNEL_FWD, KERNEL_BWD_DQ, KERNEL_BWD_DKDV = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = (
     "spattn_band_table", "spattn_fwd", "spattn_bwd_workspace_bytes", "spattn_bwd",
     "spattn_bwd_dq", "spattn_bwd_dkdv", "spattn_fwd_local", "spattn_bwd_local", "spattn_decode",
     "spattn_fwd_varlen", "spattn_bwd_varlen",
     "spattn_kernel_tiles", "spattn_tile_list", "spattn_status_string",
-    "spattn_band_table_pattern", "spattn_tile_walk",
+    "spattn_band_table_pattern", "spattn_tile_walk", "spattn_bwd_noalloc",
 )
 
 _lib = None
@@ -61,6 +62,9 @@ def load():
     lib.spattn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                _pi32, _pi32, ctypes.c_float, _p, ctypes.c_size_t, _p]
     lib.spattn_bwd.restype = ctypes.c_int
+    lib.spattn_bwd_noalloc.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _pi32, _pi32, ctypes.c_float, _p]
+    lib.spattn_bwd_noalloc.restype = ctypes.c_int
     lib.spattn_fwd_local.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32, _i32,
                                      ctypes.c_float, _p]
     lib.spattn_fwd_local.restype = ctypes.c_int

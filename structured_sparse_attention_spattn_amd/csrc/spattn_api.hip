@@ -4,6 +4,8 @@
 // scheduling code on the device.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace spattn {
@@ -190,6 +192,30 @@ int pattern_table(int N, int H, int kind, int width, int32_t* lo, int32_t* hi) {
   }
 }
 
+// Workspace of the allocation-free backward (spattn_bwd_noalloc): a static
+// device array, one per GPU the library runs on, held until the process
+// ends.  Host code never uses the array's name as an address: its device
+// address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[SPATTN_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPATTN_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SPATTN_E_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return SPATTN_OK;
+}
+
 }  // namespace
 }  // namespace spattn
 
@@ -317,6 +343,29 @@ int spattn_bwd_local(const void* q, const void* k, const void* v, const void* o,
                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, grad_dtype, band_lo, band_hi, local_window,
                   scale, workspace, workspace_bytes, stream);
+}
+
+int spattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, int32_t B, int32_t H, int32_t N, int32_t d,
+                       int32_t dtype, int32_t grad_dtype, const int32_t* band_lo, const int32_t* band_hi, float scale,
+                       void* stream) {
+  // everything that needs no device first, so a bad call fails before any HIP call
+  int st = check_sizes(B, H, N, d, dtype);
+  if (st != SPATTN_OK) return st;
+  if (grad_dtype != SPATTN_F32 && grad_dtype != dtype) return SPATTN_E_UNSUPPORTED;
+  if (bwd_workspace_bytes(B, H, N, d, dtype, grad_dtype) > (size_t)SPATTN_NOALLOC_SCRATCH_BYTES)
+    return SPATTN_E_WORKSPACE;
+  if (!tensor_ptr(q) || !tensor_ptr(k) || !tensor_ptr(v) || !tensor_ptr(o) || !vec_ptr(lse) || !tensor_ptr(dout) ||
+      !tensor_ptr(dq) || !tensor_ptr(dk) || !tensor_ptr(dv))
+    return SPATTN_E_ARG;
+  Bands bands;
+  st = make_bands(N, H, band_lo, band_hi, &bands);
+  if (st != SPATTN_OK) return st;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st != SPATTN_OK) return st;
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, grad_dtype, band_lo, band_hi, 0, scale, ws,
+                  SPATTN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // Packed variable-length batches: n_seqs sequences in [H, total, d] tensors

@@ -281,6 +281,28 @@ def bwd(q, k, v, o, lse, dout, bands=None, scale=None, grad_dtype=None, workspac
     return dq, dk, dv
 
 
+def bwd_noalloc(q, k, v, o, lse, dout, bands=None, scale=None, grad_dtype=None, out=None):
+    """spattn_bwd_noalloc: the backward with the library's static device
+    workspace (no workspace argument).  Calls on one GPU must not overlap."""
+    B, H, N, d = q.shape
+    _check_qkv(q, k, v, o, dout)
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
+    if out is None:
+        out = tuple(torch.empty(q.shape, dtype=grad_dtype, device=q.device) for _ in range(3))
+    for t in out:
+        if t.shape != q.shape or t.dtype != grad_dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("gradient buffers must be contiguous GPU tensors of q's shape and grad_dtype")
+    dq, dk, dv = out
+    p_lo, p_hi, _keep = _bands_arg(bands, H)
+    st = _lib.load().spattn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), B, H, N, d, _DT[q.dtype], _DT[grad_dtype], p_lo, p_hi,
+                                        float(scale or 0.0), _stream_handle(q.device))
+    _lib.check(st, "spattn_bwd_noalloc")
+    return dq, dk, dv
+
+
 def kernel_tiles(d, dtype):
     bq, bk = ctypes.c_int32(), ctypes.c_int32()
     st = _lib.load().spattn_kernel_tiles(d, _DT[dtype], ctypes.byref(bq), ctypes.byref(bk))
