@@ -3,22 +3,23 @@
 One step = the whole hot path over one batch: spattn_fwd (band table, band
 tile schedule, scores, masks, online softmax, P V, epilogue) followed by
 spattn_bwd's two stages (D = rowsum(dO * O) and band-tiled dQ; then band-tiled
-dK / dV), on
-B = 8, H = 16, N = 4096, d = 128, bfloat16 inputs resident in HBM.
+dK / dV), on B = 8, H = 16, N = 4096, d = 128, bfloat16 inputs resident in HBM.
 
 Prints ONE JSON line.  ``value`` is in-band TFLOP/s of fwd+bwd (14 d FLOP per
-attended pair; the heads together attend N(N+1)/2 pairs per sequence).
-Extra keys report the forward alone, per-kernel medians, the same kernels
-with L2 and MALL flushed before each launch ("cold"), the dense-causal kernel
-of the same library at the same shape, the roofline of the dominant kernel, the float64
-CPU oracle timed on this host and, under "variants", the same shape with the
-band tables of the page's ablation patterns (sliding window, gapped half
-bands) and with a shared local window joined to every band.
+attended pair; the heads together attend N(N+1)/2 pairs per sequence) with
+L2 and the MALL flushed before every timed step (a 512 MiB fill outside the
+events), so no input is served from cache; ``warm`` holds the same steps
+back to back.  Extra keys: per-kernel times and HBM fractions, the roofline
+of the dominant kernel, the dense-causal kernel of the same library at the
+same shape, the forward of the other workloads (flushed) each next to the
+float64 CPU oracle timed on this host, the page's ablation patterns and the
+shared local window ("variants"), a decode step, the measured MFMA and HBM
+denominators next to the published ones, and the oracle's fwd+bwd time.
 """
 import argparse
+import ctypes
 import gc
 import json
-import math
 import os
 import sys
 import time
@@ -31,6 +32,7 @@ SEED = 1005
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 FP32_PEAK_TFLOPS = 157.3  # fp32 matrix (and vector) peak
+FLUSH_BYTES = 512 << 20
 
 
 def kernel_source_hash():
@@ -88,19 +90,28 @@ def pairs_total(lo, hi, local_window=0, seq_len=None, batch=None):
     return tot * B
 
 
+def fwd_bytes(B, H, N, d, esz, lo):
+    """Algorithmic HBM bytes of one forward: (minimal I/O, full I/O).
+    Full: read Q, K, V; write O and LSE.  Minimal: read only the rows that
+    take part in some band (head h: query rows i >= lo_h, key rows
+    j <= N - 1 - lo_h, N - lo_h of each); every output row is written."""
+    act = B * sum(max(0, N - int(l)) for l in lo)
+    row, all_rows = d * esz, B * H * N
+    return 3 * row * act + (row + 4) * all_rows, 4 * row * all_rows + 4 * all_rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal comparison")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the ablation-pattern and local-window measurements")
+                    help="skip the ablation-pattern, local-window and decode measurements")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload forward measurements (workloads 1-4)")
-    ap.add_argument("--no-cold", action="store_true",
-                    help="skip the flushed-cache (cold) per-kernel timings")
+    ap.add_argument("--no-probe", action="store_true", help="skip the measured MFMA / HBM denominators")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--profile-workload", type=int, default=0, metavar="IDX",
@@ -145,15 +156,17 @@ def main():
     grads = tuple(torch.empty_like(q) for _ in range(3))
     ws = torch.empty(max(256, ops.bwd_workspace_bytes(B, H, N, D, torch.bfloat16, torch.bfloat16)),
                      dtype=torch.uint8, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
     def step(bands=None):
         ops.fwd(q, k, v, bands=bands, out=o, lse=lse)
         ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads)
 
-    def timed(bands, steps, warmup):
-        """Wall time of `steps` full steps, plus per-kernel HIP-event means and
-        medians (every event is recorded on the stream the kernels are launched
-        on)."""
+    def timed(bands, steps, warmup, flushed):
+        """`steps` full steps with HIP events around each kernel (recorded on
+        the stream the kernels are launched on).  flushed: a 512 MiB fill
+        before every step, outside the events, evicts L2 and the MALL.
+        Returns the wall time and the per-kernel event times (ms)."""
         for _ in range(warmup):
             step(bands)
         torch.cuda.synchronize()
@@ -161,6 +174,8 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for e0, e1, e2, e3 in ev:
+            if flushed:
+                flush.zero_()
             e0.record()
             ops.fwd(q, k, v, bands=bands, out=o, lse=lse)
             e1.record()
@@ -170,14 +185,16 @@ def main():
             e3.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
-               for i, name in enumerate(("fwd", "bwd_dq", "bwd_dkdv"))}
-        med = {name: float(np.median([e[i].elapsed_time(e[i + 1]) for e in ev]))
-               for i, name in enumerate(("fwd", "bwd_dq", "bwd_dkdv"))}
-        return wall, per, med
+        times = {name: [e[i].elapsed_time(e[i + 1]) for e in ev]
+                 for i, name in enumerate(("fwd", "bwd_dq", "bwd_dkdv"))}
+        times["step"] = [e[0].elapsed_time(e[3]) for e in ev]
+        return wall, times
 
-    wall, per, per_median = timed(None, args.steps, args.warmup)
-    ms_per_step = wall * 1e3 / args.steps
+    # ---- headline: flushed steps
+    _, ft = timed(None, args.steps, args.warmup, flushed=True)
+    per = {nm: float(np.mean(t)) for nm, t in ft.items()}
+    per_median = {nm: float(np.median(t)) for nm, t in ft.items()}
+    ms_per_step = per["step"]
     fwd_ms, bwd_ms = per["fwd"], per["bwd_dq"] + per["bwd_dkdv"]
     pairs = pairs_total(lo, hi)
     fl_fwd = 4 * D * pairs
@@ -207,7 +224,8 @@ def main():
     alg_bytes = alg_min
     kern_names = {"fwd": "fwd_bf16_kernel<128, false>", "bwd_dq": "bwd_dq_kernel<128, false>",
                   "bwd_dkdv": "bwd_dkdv_kernel<128, false>"}
-    dom = max(per, key=per.get)
+    kernels = ("fwd", "bwd_dq", "bwd_dkdv")
+    dom = max(kernels, key=per.get)
     gbs = alg_bytes[dom] / (per[dom] * 1e-3) / 1e9
     roofline = {
         "kernel": kern_names[dom],
@@ -219,7 +237,7 @@ def main():
         "traffic": measured_traffic(kern_names[dom]),
         "avg_launch_ms": round(per[dom], 4),
         "algorithmic_bytes_per_launch": alg_bytes[dom],
-        "io": "minimal (rows outside every band are not read)",
+        "io": "minimal (rows outside every band are not read); caches flushed before each step",
         "achieved_full_io": round(alg_full[dom] / (per[dom] * 1e-3) / 1e9, 1),
         "frac_full_io": round(alg_full[dom] / (per[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_full_io": alg_full[dom],
@@ -240,192 +258,256 @@ def main():
         "data": "synthetic (iid N(0,1), seed 1005)",
         "config": {"workload": "band attention fwd+bwd, bf16, B=8 H=16 N=4096 d=128, BDP bands width 256",
                    "B": B, "H": H, "N": N, "d": D},
+        "timing": "HIP events per step, L2 and MALL flushed (512 MiB fill) before each step, outside the events",
         "pct_bf16_mfma_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "inband_pairs": pairs,
         "pairs_per_s": round(pairs / (ms_per_step * 1e-3), 1),
-        "kernel_ms": {kname: round(t, 4) for kname, t in per.items()},
-        "kernel_hbm_frac": {kname: round(alg_bytes[kname] / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-                            for kname, t in per.items()},
-        "kernel_hbm_frac_full_io": {kname: round(alg_full[kname] / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-                                    for kname, t in per.items()},
+        "kernel_ms": {kname: round(per[kname], 4) for kname in kernels},
+        "kernel_ms_median": {kname: round(per_median[kname], 4) for kname in kernels},
+        "kernel_hbm_frac": {kname: round(alg_bytes[kname] / (per[kname] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                            for kname in kernels},
+        "kernel_hbm_frac_full_io": {kname: round(alg_full[kname] / (per[kname] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                                    for kname in kernels},
         "fwd_tflops": round(fl_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_tflops": round(10 * D * pairs / (bwd_ms * 1e-3) / 1e12, 2),
         "roofline": roofline,
     }
 
-    out["kernel_ms_median"] = {kname: round(t, 4) for kname, t in per_median.items()}
-
-    if not args.no_cold:
-        # Cold caches: before every kernel a 512 MiB fill (outside the events)
-        # evicts the inputs from L2 and the MALL; medians over the repeats.
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        n_cold = max(5, args.steps // 2)
-        calls = (("fwd", lambda: ops.fwd(q, k, v, out=o, lse=lse)),
-                 ("bwd_dq", lambda: ops.bwd_dq(q, k, v, o, lse, do, ws, out=grads[0])),
-                 ("bwd_dkdv", lambda: ops.bwd_dkdv(q, k, v, lse, do, ws, out=grads[1:])))
-        evs = []
-        for _ in range(n_cold):
-            for name, call in calls:
-                flush.zero_()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                call()
-                e1.record()
-                evs.append((name, e0, e1))
-        torch.cuda.synchronize()
-        cold = {name: float(np.median([a.elapsed_time(b) for n_, a, b in evs if n_ == name]))
-                for name, _ in calls}
-        cold_step = sum(cold.values())
-        out["cold"] = {
-            "repeats": n_cold,
-            "kernel_ms_median": {kname: round(t, 4) for kname, t in cold.items()},
-            "ms_per_step": round(cold_step, 4),
-            "tflops_fwdbwd": round(fl_all / (cold_step * 1e-3) / 1e12, 2),
-            "kernel_hbm_frac": {kname: round(alg_bytes[kname] / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-                                for kname, t in cold.items()},
-        }
-        del flush
+    # ---- the same steps back to back, caches warm
+    wall, wt = timed(None, args.steps, 2, flushed=False)
+    wper = {nm: float(np.mean(t)) for nm, t in wt.items()}
+    out["warm"] = {
+        "ms_per_step_wall": round(wall * 1e3 / args.steps, 4),
+        "tflops_fwdbwd_wall": round(fl_all / (wall / args.steps) / 1e12, 2),
+        "kernel_ms": {kname: round(wper[kname], 4) for kname in kernels},
+        "ms_per_step_events": round(wper["step"], 4),
+    }
 
     if not args.no_dense:
         dlo, dhi = ops.dense_bands(N, H)
         n_dense = max(5, args.steps // 2)
-        dwall, dper, _ = timed((dlo, dhi), n_dense, 2)
-        dms = dwall * 1e3 / n_dense
-        dfwd, dbwd = dper["fwd"], dper["bwd_dq"] + dper["bwd_dkdv"]
+        _, dt = timed((dlo, dhi), n_dense, 2, flushed=True)
+        dms = float(np.mean(dt["step"]))
+        dfwd, dbwd = float(np.mean(dt["fwd"])), float(np.mean(dt["bwd_dq"])) + float(np.mean(dt["bwd_dkdv"]))
         out["dense_causal"] = {
             "ms_per_step": round(dms, 4), "fwd_ms": round(dfwd, 4), "bwd_ms": round(dbwd, 4),
             "speedup_fwdbwd": round(dms / ms_per_step, 3), "speedup_fwd": round(dfwd / fwd_ms, 3),
             "dense_tflops_fwdbwd": round(14 * D * pairs_total(dlo, dhi) / (dms * 1e-3) / 1e12, 2),
+            "timing": "flushed, as the headline",
         }
 
     if not args.no_configs:
-        # forward throughput of the other workloads (the fp32 N = 1024 one and
-        # the bf16 N = 4096 / 8192 / 10000 ones), seeded inputs of their shapes
-        from structured_sparse_attention_spattn_amd.workloads import WORKLOADS, seed_for
-        per_cfg = {}
-        for idx in (1, 2, 3, 4):
-            w = WORKLOADS[idx]
-            cB, cH, cN, cd = w["B"], w["H"], w["N"], w["d"]
-            cinp = make_inputs(cB, cH, cN, cd, dtype=w["dtype"], seed=seed_for(idx), scale=w["scale"])
-            cq, ck, cv = (cinp[n].to(dev) for n in ("q", "k", "v"))
-            co = torch.empty_like(cq)
-            cl = torch.empty((cB, cH, cN), dtype=torch.float32, device=dev)
-            for _ in range(3):
-                ops.fwd(cq, ck, cv, out=co, lse=cl)
-            torch.cuda.synchronize()
-            reps = 20
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                ops.fwd(cq, ck, cv, out=co, lse=cl)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            clo, chi = ops.band_table(cN, cH)
-            cpairs = pairs_total(clo, chi, seq_len=cN, batch=cB)
-            tf = 4 * cd * cpairs / (ms * 1e-3) / 1e12
-            esz = 4 if w["dtype"] == "f32" else 2
-            act = cB * sum(max(0, cN - int(l)) for l in clo)
-            rowb, allr = cd * esz, cB * cH * cN
-            min_bytes = 3 * rowb * act + (rowb + 4) * allr
-            peak = FP32_PEAK_TFLOPS if w["dtype"] == "f32" else BF16_PEAK_TFLOPS
-            per_cfg[w["name"]] = {
-                "fwd_us": round(ms * 1e3, 2), "inband_pairs": cpairs,
-                "pairs_per_s": round(cpairs / (ms * 1e-3), 1), "tflops": round(tf, 2),
-                "pct_peak": round(100 * tf / peak, 2), "peak_tflops": peak,
-                "hbm_frac_minimal_io": round(min_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            }
-            if w["dtype"] == "f32":
-                per_cfg[w["name"]].update(f32_backward(cq, ck, cv, co, cl, seed_for(idx) + 7, dev))
-            del cq, ck, cv, co, cl, cinp
-        # the float32 backward where it is throughput-bound (no workload of its own)
-        fB, fH, fN, fd = 2, 16, 4096, 128
-        finp = make_inputs(fB, fH, fN, fd, dtype="f32", seed=4242)
-        fq, fk, fv = (finp[n].to(dev) for n in ("q", "k", "v"))
-        fo, fl = ops.fwd(fq, fk, fv)
-        per_cfg[f"bwd_f32_B{fB}_H{fH}_N{fN}_d{fd}"] = f32_backward(fq, fk, fv, fo, fl, 4243, dev)
-        del fq, fk, fv, fo, fl, finp
-        out["configs"] = per_cfg
+        out["configs"] = workload_forwards(dev, flush, with_cpu=not args.no_cpu)
 
     if not args.no_variants:
-        def timed_total(bands, lw, steps, warmup):
-            """fwd and bwd (both stages) of the whole batch with these bands /
-            local window; HIP events on the launch stream, median per step
-            (and the mean wall time per step)."""
-            for _ in range(warmup):
-                ops.fwd(q, k, v, bands=bands, out=o, lse=lse, local_window=lw)
-                ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads, local_window=lw)
-            torch.cuda.synchronize()
-            ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
-            t0 = time.perf_counter()
-            for e0, e1, e2 in ev:
-                e0.record()
-                ops.fwd(q, k, v, bands=bands, out=o, lse=lse, local_window=lw)
-                e1.record()
-                ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads, local_window=lw)
-                e2.record()
-            torch.cuda.synchronize()
-            wall = (time.perf_counter() - t0) * 1e3 / steps
-            # medians: one stalled step must not stand for the variant
-            f = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
-            b = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
-            return wall, f, b
+        out["variants"], out["decode"] = variants_and_decode(q, k, v, do, o, lse, ws, grads, lo, hi, args.steps, dev)
 
-        variants = {}
-        nvs = max(5, args.steps // 2)
-        wlo, whi = ops.window_bands(N, H, N // H)
-        glo, ghi = ops.gapped_half_bands(N, H)
-        for name, bands, lw, (plo, phi) in (
-                (f"sliding_window_{N // H}", (wlo, whi), 0, (wlo, whi)),
-                ("gapped_half_bands", (glo, ghi), 0, (glo, ghi)),
-                ("bands_plus_local_window_64", None, 64, (lo, hi))):
-            wall_v, f_v, b_v = timed_total(bands, lw, nvs, 3)
-            pv = pairs_total(plo, phi, lw)
-            variants[name] = {
-                "ms_per_step": round(f_v + b_v, 4), "fwd_ms": round(f_v, 4), "bwd_ms": round(b_v, 4),
-                "wall_ms_per_step": round(wall_v, 4), "attended_pairs": pv,
-                "tflops_fwdbwd": round(14 * D * pv / ((f_v + b_v) * 1e-3) / 1e12, 2),
-            }
-        out["variants"] = variants
-
-        # decode step (one new query per sequence) over a full key/value cache
-        # of the same head layout; the caches come from a seeded device
-        # generator (synthetic N(0, 1), quantised to bfloat16)
-        dB = 64
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(SEED)
-        qd = torch.randn((dB, H, D), generator=gen, device=dev).to(torch.bfloat16)
-        kc = torch.randn((dB, H, N, D), generator=gen, device=dev).to(torch.bfloat16)
-        vc = torch.randn((dB, H, N, D), generator=gen, device=dev).to(torch.bfloat16)
-        od = torch.empty_like(qd)
-        ld = torch.empty((dB, H), dtype=torch.float32, device=dev)
-        for _ in range(5):
-            ops.decode(qd, kc, vc, out=od, lse=ld)
-        torch.cuda.synchronize()
-        n_dec = 50
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n_dec):
-            ops.decode(qd, kc, vc, out=od, lse=ld)
-        e1.record()
-        torch.cuda.synchronize()
-        dec_ms = e0.elapsed_time(e1) / n_dec
-        keys = sum(min(N - 1, int(u)) - int(l_) + 1 for l_, u in zip(lo, hi) if int(u) >= int(l_))  # at i = N - 1
-        dec_bytes = dB * (keys * 2 * D * 2 + H * (2 * D * 2 + 4))
-        out["decode"] = {
-            "workload": f"decode, bf16, B={dB} H={H} cache={N} d={D}, BDP bands, full caches",
-            "us_per_step": round(dec_ms * 1e3, 2),
-            "tokens_per_s": round(dB / (dec_ms * 1e-3), 1),
-            "gather_bytes": dec_bytes,
-            "gbs": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        }
-        del kc, vc
+    if not args.no_probe:
+        out["measured_peaks"] = measured_peaks(dev)
+        mp = out["measured_peaks"]
+        if mp.get("hbm_read_gbs"):
+            roofline["peak_measured_read"] = mp["hbm_read_gbs"]
+            roofline["frac_of_measured_read"] = round(gbs / mp["hbm_read_gbs"], 4)
+        if mp.get("bf16_mfma_tflops"):
+            out["pct_measured_bf16_mfma_peak"] = round(100 * value / mp["bf16_mfma_tflops"], 2)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, lo, hi, fl_all)
 
     print(json.dumps(out), flush=True)
+
+
+def workload_forwards(dev, flush, with_cpu, reps=20):
+    """Forward of workloads 1-4 on seeded inputs of their shapes: HIP events
+    around each launch with L2 and the MALL flushed before it (median), the
+    warm back-to-back mean, and the whole-workload float64 oracle forward
+    timed on the host cores."""
+    import numpy as np
+    import torch
+    from structured_sparse_attention_spattn_amd import ops
+    from structured_sparse_attention_spattn_amd.inputs import make_inputs
+    from structured_sparse_attention_spattn_amd.workloads import WORKLOADS, seed_for
+    per_cfg = {}
+    for idx in (1, 2, 3, 4):
+        w = WORKLOADS[idx]
+        cB, cH, cN, cd = w["B"], w["H"], w["N"], w["d"]
+        cinp = make_inputs(cB, cH, cN, cd, dtype=w["dtype"], seed=seed_for(idx), scale=w["scale"])
+        cq, ck, cv = (cinp[n].to(dev) for n in ("q", "k", "v"))
+        co = torch.empty_like(cq)
+        cl = torch.empty((cB, cH, cN), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            ops.fwd(cq, ck, cv, out=co, lse=cl)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            flush.zero_()
+            e0.record()
+            ops.fwd(cq, ck, cv, out=co, lse=cl)
+            e1.record()
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record()
+        for _ in range(reps):
+            ops.fwd(cq, ck, cv, out=co, lse=cl)
+        w1.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        warm_ms = w0.elapsed_time(w1) / reps
+        clo, chi = ops.band_table(cN, cH)
+        cpairs = pairs_total(clo, chi, seq_len=cN, batch=cB)
+        tf = 4 * cd * cpairs / (ms * 1e-3) / 1e12
+        esz = 4 if w["dtype"] == "f32" else 2
+        min_bytes, full_bytes = fwd_bytes(cB, cH, cN, cd, esz, clo)
+        peak = FP32_PEAK_TFLOPS if w["dtype"] == "f32" else BF16_PEAK_TFLOPS
+        rec = {
+            "fwd_us": round(ms * 1e3, 2), "inband_pairs": cpairs,
+            "pairs_per_s": round(cpairs / (ms * 1e-3), 1), "tflops": round(tf, 2),
+            "pct_peak": round(100 * tf / peak, 2), "peak_tflops": peak,
+            "hbm_frac_minimal_io": round(min_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "hbm_frac_full_io": round(full_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "timing": "median of flushed launches",
+            "warm_fwd_us": round(warm_ms * 1e3, 2),
+            "warm_tflops": round(4 * cd * cpairs / (warm_ms * 1e-3) / 1e12, 2),
+        }
+        if w["dtype"] == "f32":
+            rec.update(f32_backward(cq, ck, cv, co, cl, seed_for(idx) + 7, dev))
+        del cq, ck, cv, co, cl
+        if with_cpu:
+            rec["cpu_baseline"] = cpu_forward_baseline(cinp, clo, chi, 4 * cd * cpairs, cpairs, w["name"])
+        per_cfg[w["name"]] = rec
+        del cinp
+    # the float32 backward where it is throughput-bound (no workload of its own)
+    fB, fH, fN, fd = 2, 16, 4096, 128
+    finp = make_inputs(fB, fH, fN, fd, dtype="f32", seed=4242)
+    fq, fk, fv = (finp[n].to(dev) for n in ("q", "k", "v"))
+    fo, fl = ops.fwd(fq, fk, fv)
+    per_cfg[f"bwd_f32_B{fB}_H{fH}_N{fN}_d{fd}"] = f32_backward(fq, fk, fv, fo, fl, 4243, dev)
+    return per_cfg
+
+
+def variants_and_decode(q, k, v, do, o, lse, ws, grads, lo, hi, steps, dev):
+    """The page's ablation patterns and the shared local window at the bench
+    shape (medians of device time per step), and a decode step."""
+    import numpy as np
+    import torch
+    from structured_sparse_attention_spattn_amd import ops
+
+    def timed_total(bands, lw, steps, warmup):
+        for _ in range(warmup):
+            ops.fwd(q, k, v, bands=bands, out=o, lse=lse, local_window=lw)
+            ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads, local_window=lw)
+        torch.cuda.synchronize()
+        ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e0, e1, e2 in ev:
+            e0.record()
+            ops.fwd(q, k, v, bands=bands, out=o, lse=lse, local_window=lw)
+            e1.record()
+            ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads, local_window=lw)
+            e2.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        # medians: one stalled step must not stand for the variant
+        f = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+        b = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+        return wall, f, b
+
+    variants = {}
+    nvs = max(5, steps // 2)
+    wlo, whi = ops.window_bands(N, H, N // H)
+    glo, ghi = ops.gapped_half_bands(N, H)
+    for name, bands, lw, (plo, phi) in (
+            (f"sliding_window_{N // H}", (wlo, whi), 0, (wlo, whi)),
+            ("gapped_half_bands", (glo, ghi), 0, (glo, ghi)),
+            ("bands_plus_local_window_64", None, 64, (lo, hi))):
+        wall_v, f_v, b_v = timed_total(bands, lw, nvs, 3)
+        pv = pairs_total(plo, phi, lw)
+        variants[name] = {
+            "ms_per_step": round(f_v + b_v, 4), "fwd_ms": round(f_v, 4), "bwd_ms": round(b_v, 4),
+            "wall_ms_per_step": round(wall_v, 4), "attended_pairs": pv,
+            "tflops_fwdbwd": round(14 * D * pv / ((f_v + b_v) * 1e-3) / 1e12, 2),
+        }
+
+    # decode step (one new query per sequence) over a full key/value cache
+    # of the same head layout; the caches come from a seeded device
+    # generator (synthetic N(0, 1), quantised to bfloat16)
+    dB = 64
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(SEED)
+    qd = torch.randn((dB, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    kc = torch.randn((dB, H, N, D), generator=gen, device=dev).to(torch.bfloat16)
+    vc = torch.randn((dB, H, N, D), generator=gen, device=dev).to(torch.bfloat16)
+    od = torch.empty_like(qd)
+    ld = torch.empty((dB, H), dtype=torch.float32, device=dev)
+    for _ in range(5):
+        ops.decode(qd, kc, vc, out=od, lse=ld)
+    torch.cuda.synchronize()
+    n_dec = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_dec):
+        ops.decode(qd, kc, vc, out=od, lse=ld)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / n_dec
+    keys = sum(min(N - 1, int(u)) - int(l_) + 1 for l_, u in zip(lo, hi) if int(u) >= int(l_))  # at i = N - 1
+    dec_bytes = dB * (keys * 2 * D * 2 + H * (2 * D * 2 + 4))
+    decode = {
+        "workload": f"decode, bf16, B={dB} H={H} cache={N} d={D}, BDP bands, full caches",
+        "us_per_step": round(dec_ms * 1e3, 2),
+        "tokens_per_s": round(dB / (dec_ms * 1e-3), 1),
+        "gather_bytes": dec_bytes,
+        "gbs": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    return variants, decode
+
+
+def measured_peaks(dev):
+    """Measured denominators from libspattn_probe.so (spattn_probe.h): bf16
+    and fp32 MFMA throughput (4 independent chains per wave, 16 waves per
+    CU, registers only) and the read bandwidth of a 4 GiB buffer; the best
+    of 3 launches each.  None where the probe library is not built."""
+    import torch
+    path = os.path.join(ROOT, "structured_sparse_attention_spattn_amd", "libspattn_probe.so")
+    if not os.path.exists(path):
+        return {"note": "libspattn_probe.so not built"}
+    lib = ctypes.CDLL(path)
+    lib.spattn_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.spattn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    blocks = 256 * 4  # 4 workgroups of 4 waves per CU
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def best_ms(call, n=3):
+        call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    res = {"method": "libspattn_probe.so: 4 independent MFMA chains per wave, 4 workgroups x 4 waves per CU; "
+                     "16-byte grid-stride reads of a 4 GiB buffer; best of 3 launches"}
+    for kind, name, flop in ((0, "bf16_mfma_tflops", 32768), (1, "fp32_mfma_tflops", 4096)):
+        iters = 2048 if kind == 0 else 1024
+        ms = best_ms(lambda: lib.spattn_probe_mfma(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()), stream))
+        res[name] = round(blocks * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12, 1)
+    buf = torch.ones(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB
+    nbytes = buf.numel() * 4
+    ms = best_ms(lambda: lib.spattn_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, 256 * 8,
+                                               ctypes.c_void_p(sink.data_ptr()), stream))
+    res["hbm_read_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    res["spec"] = {"bf16_mfma_tflops": BF16_PEAK_TFLOPS, "fp32_mfma_tflops": FP32_PEAK_TFLOPS,
+                   "hbm_gbs": HBM_PEAK_GBS}
+    del buf
+    return res
 
 
 def profile_workload(idx, steps, warmup, dev):
@@ -489,21 +571,13 @@ def f32_backward(q, k, v, o, lse, seed, dev, reps=20):
             "bwd_pct_peak": round(100 * tf / FP32_PEAK_TFLOPS, 2)}
 
 
-def cpu_baseline(inp, lo, hi, flops_all):
-    """The float64 oracle (as is) on this host, fwd+bwd over the whole workload."""
+def _host_info():
     import platform
-
-    import oracle
-    from structured_sparse_attention_spattn_amd.inputs import as_f64
     try:
         from threadpoolctl import threadpool_info
         threads = max(i.get("num_threads", 1) for i in threadpool_info())
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    q, k, v, do = (as_f64(inp[n]) for n in ("q", "k", "v", "dout"))
-    t0 = time.perf_counter()
-    oracle.band_attention_bwd(q, k, v, do, lo, hi)  # includes the forward recompute
-    dt = time.perf_counter() - t0
     model = platform.processor() or platform.machine()
     try:
         with open("/proc/cpuinfo") as f:
@@ -513,10 +587,36 @@ def cpu_baseline(inp, lo, hi, flops_all):
                     break
     except OSError:
         pass
+    return int(threads), model
+
+
+def cpu_forward_baseline(inp, lo, hi, flops, pairs, name):
+    """The float64 oracle forward (as is) over one whole workload on this host."""
+    import oracle
+    from structured_sparse_attention_spattn_amd.inputs import as_f64
+    q, k, v = (as_f64(inp[n]) for n in ("q", "k", "v"))
+    threads, model = _host_info()
+    t0 = time.perf_counter()
+    oracle.band_attention_fwd(q, k, v, lo, hi)
+    dt = time.perf_counter() - t0
+    return {"kind": "oracle", "sample": f"whole workload {name}, float64 numpy forward", "seconds": round(dt, 3),
+            "gflops": round(flops / dt / 1e9, 2), "pairs_per_s": round(pairs / dt, 1), "cores": threads,
+            "cpu": model}
+
+
+def cpu_baseline(inp, lo, hi, flops_all):
+    """The float64 oracle (as is) on this host, fwd+bwd over the whole workload."""
+    import oracle
+    from structured_sparse_attention_spattn_amd.inputs import as_f64
+    threads, model = _host_info()
+    q, k, v, do = (as_f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    t0 = time.perf_counter()
+    oracle.band_attention_bwd(q, k, v, do, lo, hi)  # includes the forward recompute
+    dt = time.perf_counter() - t0
     return {
         "value": round(flops_all / dt / 1e12, 5),
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
         "sample": "whole workload (B=8 H=16 N=4096 d=128), float64 numpy, fwd+bwd",
         "seconds": round(dt, 2),

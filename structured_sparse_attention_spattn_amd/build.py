@@ -63,5 +63,25 @@ def build(verbose=False, extra_flags=(), build_dir=None, lib_path=None):
     return LIB
 
 
+PROBE_SRC = os.path.join(HERE, "probe", "probe.hip")
+PROBE_LIB = os.path.join(HERE, "libspattn_probe.so")
+
+
+def build_probe(verbose=False):
+    """The microbenchmark library libspattn_probe.so (measured MFMA and HBM
+    denominators for the benchmark), one source, one hipcc call."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *COMMON_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        print(r.stdout.decode(errors="replace"), file=sys.stderr)
+        raise RuntimeError("build of libspattn_probe.so failed")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))

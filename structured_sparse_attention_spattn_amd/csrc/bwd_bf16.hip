@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles, true);
   if (!wi.valid) return;  // padding pair
   const int t = wi.t;
   const int h = wi.h;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles, false);
   if (!wi.valid) return;  // padding pair
   const int ut = wi.t;
   const int h = wi.h;

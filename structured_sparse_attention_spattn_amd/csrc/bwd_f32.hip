@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * W, D == 64 ? 2 : 1) void bwd_f32_dq_kernel(F32
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles, true);
   if (!wi.valid) return;  // padding pair
   const int t = wi.t;
   const int h = wi.h;
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(64 * W, D == 64 ? 2 : 1) void bwd_f32_dkdv_kernel(F
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles, false);
   if (!wi.valid) return;  // padding pair
   const int t = wi.t;
   const int h = wi.h;
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void bwd_f32_dq_split_kernel(F32B
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles, true);
   if (!wi.valid) return;  // padding pair
   const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, wi.b, wi.h);
   const int N = sh.n;
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void bwd_f32_dkdv_split_kernel(F3
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_tiles, false);
   if (!wi.valid) return;  // padding pair
   const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, wi.b, wi.h);
   const int N = sh.n;
@@ -722,8 +722,8 @@ int launch_bwd_dq_f32(const void* q, const void* k, const void* v, const void* o
                       void* dq, int B, int H, int N, int d, const Bands& bands, int local_window, float scale,
                       float* dvec, const Packed& pk, hipStream_t stream) {
   const bool split = split_launch(B, H, N);
-  const F32BwdArgs a = make_f32_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, bands, local_window, scale,
-                                     dvec, pk, split ? kT : kW * kT);
+  F32BwdArgs a = make_f32_args(q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, N, bands, local_window, scale,
+                               dvec, pk, split ? kT : kW * kT);
   const long long total = work_grid(B, H, a.n_tiles);
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   const dim3 grid((unsigned)total), block(64 * kW);
@@ -743,8 +743,8 @@ int launch_bwd_dkdv_f32(const void* q, const void* k, const void* v, const float
                         void* dv, int B, int H, int N, int d, const Bands& bands, int local_window, float scale,
                         float* dvec, const Packed& pk, hipStream_t stream) {
   const bool split = split_launch(B, H, N);
-  const F32BwdArgs a = make_f32_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, bands, local_window,
-                                     scale, dvec, pk, split ? kT : kW * kT);
+  F32BwdArgs a = make_f32_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, N, bands, local_window,
+                               scale, dvec, pk, split ? kT : kW * kT);
   const long long total = work_grid(B, H, a.n_tiles);
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
   const dim3 grid((unsigned)total), block(64 * kW);

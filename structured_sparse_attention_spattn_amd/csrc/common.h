@@ -646,7 +646,7 @@ __host__ __device__ __forceinline__ bool set_full(int i_min, int i_max, int j_mi
 
 // Workgroup -> logical work item, so that consecutive logical items land on
 // the same XCD (the hardware deals workgroups to the 8 XCDs round-robin).
-__device__ __forceinline__ int xcd_remap(int pid, int total) {
+__host__ __device__ __forceinline__ int xcd_remap(int pid, int total) {
   constexpr int kXcd = 8;
   const int q = total / kXcd, r = total % kXcd;
   const int xcd = pid % kXcd, slot = pid / kXcd;
@@ -670,7 +670,14 @@ struct WorkItem {
 __host__ __device__ __forceinline__ long long work_grid(int B, int H, int n_tiles) {
   return 8LL * ((B * H + 7) / 8) * n_tiles;
 }
-__device__ __forceinline__ WorkItem work_item(int pid, int B, int H, int n_tiles) {
+// descending: the tiles of a pair are dispatched from the last to the first.
+// Query-major kernels ask for it: a head's first query tiles have no keys
+// and the next few only part of its distance set, so in descending order the
+// full-cost tiles start first and the cheap ones last, and the workgroups that
+// wait for a slot are cheap ones.  (Key-major kernels already have that order
+// ascending: their last key tiles have fewer queries or none.)
+__host__ __device__ __forceinline__ WorkItem work_item(int pid, int B, int H, int n_tiles,
+                                                     bool descending = false) {
   const int c = (B * H + 7) / 8;  // pairs per XCD
   const int item = xcd_remap(pid, 8 * c * n_tiles);
   const int m = item / n_tiles;
@@ -680,6 +687,7 @@ __device__ __forceinline__ WorkItem work_item(int pid, int B, int H, int n_tiles
   w.b = k % B;
   w.h = k / B;
   w.t = item % n_tiles;
+  if (descending) w.t = n_tiles - 1 - w.t;
   w.valid = k < B * H;
   return w;
 }

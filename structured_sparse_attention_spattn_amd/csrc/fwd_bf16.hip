@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_qt);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_qt, true);
   if (!wi.valid) return;  // padding pair
   const int t = wi.t;
   const int h = wi.h;
@@ -351,6 +351,154 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
   }
 }
 
+// Lean variant for small head sizes: one 32-key half at a time with a
+// single straight-line body (no software pipelining across halves, so the
+// state is one accumulator set and one score block) and a register budget of
+// 128 per lane, so four workgroups share a CU and the other waves of each
+// SIMD hide one wave's dependent MFMA / softmax chain.  Per half: scores
+// S^T = K Q^T, the element mask only where the half is PARTIAL for this
+// wave's rows, the reference update, P and its row sum, O^T += V^T P^T.
+template <int D, bool TWO>
+__global__ __launch_bounds__(kThreads, 4) void fwd_bf16_lean_kernel(FwdArgs p) {
+  constexpr int kTile = kBK * D;  // one K or V tile, bf16 elements
+  using Tile = AsyncTile<kBK, D, kThreads / 64>;
+  constexpr int kDT = D / 32;
+  constexpr int kKK = D / 16;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_qt, true);
+  if (!wi.valid) return;  // padding pair
+  const int t = wi.t;
+  const int h = wi.h;
+  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, wi.b, h);
+  const int N = sh.n;
+  if (t * kBQ >= N) return;  // past the end of a packed sequence
+  const DistSet dset = dist_set(sh.lo, sh.hi, TWO ? p.local_window : 0);
+  const int lo = dset.lo;
+  const int hi = dset.hi;
+  const size_t base = sh.row0 * D;
+  const bf16* __restrict__ qb = p.q + base;
+  const bf16* __restrict__ kb = p.k + base;
+  const bf16* __restrict__ vb = p.v + base;
+  bf16* __restrict__ ob = p.o + base;
+  float* __restrict__ lb = p.lse + sh.row0;
+  const float ninf = -__builtin_inff();
+
+  const int i_tile0 = t * kBQ;
+  const TileWalk walk = kernel_walk(kWalk, i_tile0, N, dset);
+  if (walk.n == 0) {
+    // No row of this tile has a key: output 0, LSE -inf.
+    constexpr int kCpr = D / 8;
+    for (int c = tid; c < kBQ * kCpr; c += kThreads) {
+      const int i = i_tile0 + c / kCpr;
+      if (i < N) *(u32x4*)(ob + (size_t)i * D + (c % kCpr) * 8) = u32x4{0, 0, 0, 0};
+    }
+    for (int r = tid; r < kBQ; r += kThreads)
+      if (i_tile0 + r < N) lb[i_tile0 + r] = ninf;
+    return;
+  }
+  const int iw0 = i_tile0 + 32 * wave;
+  const int iw1 = min(N - 1, iw0 + 31);
+  const bool wave_live = iw0 <= N - 1;
+  const int iq = iw0 + c32;
+
+  Tile::load(smem, kb, walk.at(0) * kBK, N, wave, lane);
+  Tile::load(smem + kTile, vb, walk.at(0) * kBK, N, wave, lane);
+
+  // Q^T operand: lane holds Q[iq][16kk + 8g .. +7].
+  bf16x8 qreg[kKK];
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk)
+    qreg[kk] = iq < N ? *(const bf16x8*)(qb + (size_t)iq * D + 16 * kk + 8 * g) : bf16x8{};
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) settle(qreg[kk]);
+  LaneOffsets<D> off(lane);
+
+  OnlineState<D> st;
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.acc[dt][i] = 0.f;
+  st.m_ref = ninf;
+  st.l_run = 0.f;
+  const float sl2 = p.scale_log2;
+
+  // One 32-key half M (compile-time) of the tile in stage S.
+  auto half = [&](auto stage, auto half_idx, int jb) {
+    constexpr int S = decltype(stage)::value;
+    constexpr int M = decltype(half_idx)::value;
+    const int j0 = jb + 32 * M;
+    bool meets, full;
+    if constexpr (TWO) {
+      meets = wave_live && set_meets(iw0, iw1, j0, j0 + 31, dset);
+      full = set_full(iw0, iw1, j0, j0 + 31, dset);
+    } else {
+      meets = wave_live && tile_meets(iw0, iw1, j0, j0 + 31, lo, hi);
+      full = tile_full(iw0, iw1, j0, j0 + 31, lo, hi);
+    }
+    if (!meets) return;
+    const bf16* ks = smem + S * 2 * kTile;
+    const bf16* vs = ks + kTile;
+    bf16x8 ka[kKK];
+    load_ka<D>(ka, ks, off, 32 * M);
+    const f32x16 sc = mfma_ksum<kKK, 1>(ka, qreg);
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = sc[i];
+    if (!full) {
+      const int rb = iq - j0 - 8 * g;
+      if constexpr (TWO)
+        band_mask2(x, rb - lo, hi - lo, rb - dset.nlo, dset.nhi - dset.nlo);
+      else
+        band_mask(x, rb - lo, hi - lo);
+    }
+    float alpha, nms;
+    bool moved;
+    reference_update(x, st.m_ref, sl2, alpha, moved, nms);
+    bf16x8 p0, p1;
+    st.l_run = st.l_run * alpha + probs(x, sl2, nms, p0, p1);
+    if (moved) rescale<D>(st, alpha);
+    bf16x8 va[2 * kDT];
+    load_va<D>(va, vs, off, 32 * M);
+    pv<D>(st, va, p0, p1);
+  };
+  auto step = [&](auto stage, int v) {
+    constexpr int S = decltype(stage)::value;
+    wait_vmcnt<0>();  // this wave's part of the tile has landed
+    __syncthreads();  // ... everyone's, and everyone is done with the previous tile
+    if (v + 1 < walk.n) {
+      bf16* nxt = smem + (S ^ 1) * 2 * kTile;
+      const int un = walk.at(v + 1);
+      Tile::load(nxt, kb, un * kBK, N, wave, lane);
+      Tile::load(nxt + kTile, vb, un * kBK, N, wave, lane);
+    }
+    off.refresh();
+    const int jb = walk.at(v) * kBK;
+    half(stage, std::integral_constant<int, 0>{}, jb);
+    half(stage, std::integral_constant<int, 1>{}, jb);
+  };
+  for (int v = 0; v < walk.n; v += 2) {
+    step(std::integral_constant<int, 0>{}, v);
+    if (v + 1 < walk.n) step(std::integral_constant<int, 1>{}, v + 1);
+  }
+
+  const float l_tot = pair_sum(st.l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (iq < N && g == 0) lb[iq] = l_tot > 0.f ? (st.m_ref * sl2 + fast_log2(l_tot)) * kLn2 : ninf;
+  __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
+  if (wave_live) {
+    float* stg = (float*)smem + wave * 32 * D;
+    stage_transposed<D>(stg, st.acc, inv, lane);
+    store_staged<D>(stg, p.o, sh.row0 + iw0, min(32, N - iw0), false, lane);
+  }
+}
+
 }  // namespace
 
 int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -381,9 +529,9 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   else if (d == 128)
     hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
   else if (d == 64 && !two)
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_lean_kernel<64, false>), grid, block, 0, stream, a);
   else if (d == 64)
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_lean_kernel<64, true>), grid, block, 0, stream, a);
   else
     return SPATTN_E_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;

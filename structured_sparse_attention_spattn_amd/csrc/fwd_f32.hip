@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_f32_kernel(FwdF32Args p) {
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_qt);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_qt, true);
   if (!wi.valid) return;  // padding pair
   const int t = wi.t;
   const int h = wi.h;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_split_kernel(FwdF32Args p) {
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_qt);
+  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_qt, true);
   if (!wi.valid) return;  // padding pair
   const int t = wi.t;
   const int h = wi.h;

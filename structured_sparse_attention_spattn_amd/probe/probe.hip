@@ -1,0 +1,73 @@
+// Microbenchmarks for the measured denominators (declared in spattn_probe.h):
+// matrix-core throughput of the two MFMA shapes the kernels use, and the HBM
+// read bandwidth of plain 16-byte loads.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spattn_probe.h"
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+// Four independent accumulator chains per wave, operands from registers.
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* sink) {
+  const int lane = threadIdx.x & 63;
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  if constexpr (KIND == 0) {
+    bf16x8 a, b;
+    for (int j = 0; j < 8; ++j) {
+      a[j] = (__bf16)(1e-3f * (float)(lane + j));
+      b[j] = (__bf16)(1e-3f * (float)(lane - j));
+    }
+    for (int i = 0; i < iters; ++i) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+  } else {
+    const float a = 1e-3f * (float)lane, b = 1e-3f * (float)(64 - lane);
+    for (int i = 0; i < iters; ++i) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c3, 0, 0, 0);
+    }
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  sink[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const f32x4* __restrict__ src, size_t n, float* sink) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) acc += src[i];
+  sink[blockIdx.x * 256 + threadIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
+}
+
+}  // namespace
+
+extern "C" {
+
+int spattn_probe_mfma(int32_t kind, int32_t blocks, int32_t iters, float* sink, void* stream) {
+  if (blocks < 1 || iters < 1 || sink == nullptr || (kind != 0 && kind != 1)) return 1;
+  if (kind == 0)
+    hipLaunchKernelGGL(mfma_probe_kernel<0>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+  else
+    hipLaunchKernelGGL(mfma_probe_kernel<1>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int spattn_probe_read(const void* src, size_t bytes, int32_t blocks, float* sink, void* stream) {
+  if (src == nullptr || sink == nullptr || blocks < 1 || bytes % 16 != 0 || ((uintptr_t)src & 15u) != 0) return 1;
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const f32x4*)src,
+                     bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+}  // extern "C"

@@ -8,7 +8,9 @@ run against it:
   over a sweep of sizes, workspace sizing, status strings and the argument
   checks of every entry point (each fails before any launch);
 * tests/c/seq_view_host.cpp: the packed-sequence view every kernel indexes
-  with stays inside the tensors for malformed offset arrays.
+  with stays inside the tensors for malformed offset arrays;
+* tests/c/schedule_host.cpp: the workgroup -> work item mapping of the band
+  kernels covers every tile exactly once.
 A sanitizer report makes the program exit non-zero.
 """
 import os
@@ -68,3 +70,16 @@ def test_packed_sequence_view_under_sanitizers(tmp_path):
     assert r.returncode == 0, r.stderr[-4000:]
     out = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=_env())
     assert out.returncode == 0 and out.stdout.strip() == "violations 0", (out.stdout, out.stderr[-4000:])
+
+
+def test_dispatch_order_under_sanitizers(tmp_path):
+    """Every (sequence, head, tile) is run by exactly one workgroup under the
+    kernels' workgroup -> work item mapping (tests/c/schedule_host.cpp)."""
+    exe = str(tmp_path / "schedule_san")
+    cmd = [os.path.join(ROCM, "bin", "hipcc"), "--offload-arch=gfx950", "-std=c++17", "-g", "-O1", *SAN_HOST,
+           "-I", os.path.join(ROOT, "structured_sparse_attention_spattn_amd", "csrc"),
+           "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c", "schedule_host.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=_env())
+    assert out.returncode == 0 and out.stdout.strip().endswith("violations 0"), (out.stdout[-2000:], out.stderr[-4000:])
