@@ -306,8 +306,9 @@ int spattn_tile_list(int32_t N, int32_t lo, int32_t hi, int32_t BQ, int32_t BK,
  * Test export of a kernel's actual tile walk: for one band [lo, hi] (with
  * the shared local window as in spattn_fwd_local) of a length-N sequence,
  * runs on the device the walk builder and tile test the chosen kernel runs,
- * for the launch that B sequences of H heads would make (the float32 kernels
- * pick their tile shape by launch size).  Output in CSR form over the tiles
+ * for the launch that B sequences of H heads with head size d would make (the
+ * float32 kernels pick their tile shape by launch size, the bfloat16 forward
+ * by head size).  Output in CSR form over the tiles
  * the kernel owns (query tiles for SPATTN_KERNEL_FWD and _BWD_DQ, key tiles
  * for SPATTN_KERNEL_BWD_DKDV):
  *   ptr    device int32 [ceil(N / own_rows) + 1]
@@ -324,10 +325,10 @@ int spattn_tile_list(int32_t N, int32_t lo, int32_t hi, int32_t BQ, int32_t BK,
  * (i, j), j <= i < N, has i - j in the head's set.  If the list is longer
  * than cap, n_out holds the full count and the first cap entries are written.
  * Errors: SPATTN_E_ARG (unknown kernel, null pointers, B, H or N < 1, band
- * outside [0, N-1], local_window < 0), SPATTN_E_UNSUPPORTED (dtype),
- * SPATTN_E_HIP.
+ * outside [0, N-1], local_window < 0), SPATTN_E_UNSUPPORTED (dtype, d not
+ * 64 / 128), SPATTN_E_HIP.
  */
-int spattn_tile_walk(int32_t kernel, int32_t dtype, int32_t B, int32_t H, int32_t N,
+int spattn_tile_walk(int32_t kernel, int32_t d, int32_t dtype, int32_t B, int32_t H, int32_t N,
                      int32_t lo, int32_t hi, int32_t local_window, int32_t* ptr,
                      int32_t* tiles, uint8_t* kind, int32_t cap, int32_t* n_out,
                      int32_t* own_rows, int32_t* tile_rows, void* stream);

@@ -51,8 +51,8 @@ def load():
     lib.spattn_band_table.restype = ctypes.c_int
     lib.spattn_band_table_pattern.argtypes = [_i32, _i32, _i32, _i32, _pi32, _pi32]
     lib.spattn_band_table_pattern.restype = ctypes.c_int
-    lib.spattn_tile_walk.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _pi32,
-                                     _pi32, _p]
+    lib.spattn_tile_walk.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p,
+                                     _pi32, _pi32, _p]
     lib.spattn_tile_walk.restype = ctypes.c_int
     lib.spattn_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32,
                                ctypes.c_float, _p]

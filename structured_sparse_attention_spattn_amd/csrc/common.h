@@ -402,33 +402,41 @@ __device__ __forceinline__ int stage_off(int r, int col) {
 }
 // Accumulators of a transposed product X^T (column l % 32 = row of X,
 // register i of block dt = column 32 dt + 8 (i / 4) + 4 g + i % 4 of X),
-// times `mul`, into the staging tile.
-template <int D>
+// times `mul`, into the staging tile.  A staging tile may hold only the NC
+// columns C0 .. C0 + NC - 1 of X (a 32 x NC tile), so that a kernel whose
+// LDS is smaller than 32 x D floats per wave writes its result in D / NC
+// passes.
+template <int D, int NC = D, int C0 = 0>
 __device__ __forceinline__ void stage_transposed(float* st, const f32x16* acc, float mul, int lane) {
+  static_assert(NC % 32 == 0 && C0 % 32 == 0 && C0 + NC <= D, "staged column range");
   const int g = lane >> 5, r = lane & 31;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < NC / 32; ++dt)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      *(f32x4*)&st[stage_off<D>(r, 32 * dt + 8 * a + 4 * g)] =
-          f32x4{acc[dt][4 * a] * mul, acc[dt][4 * a + 1] * mul, acc[dt][4 * a + 2] * mul, acc[dt][4 * a + 3] * mul};
+    for (int a = 0; a < 4; ++a) {
+      const f32x16& x = acc[C0 / 32 + dt];
+      *(f32x4*)&st[stage_off<NC>(r, 32 * dt + 8 * a + 4 * g)] =
+          f32x4{x[4 * a] * mul, x[4 * a + 1] * mul, x[4 * a + 2] * mul, x[4 * a + 3] * mul};
+    }
 }
-// Rows 0 .. nrows - 1 of the staging tile to dst + row0 * D (row-major,
-// bfloat16 or float32): every lane moves 8 consecutive values of one row, so
-// one store instruction covers 512 / D whole rows.
-template <int D>
-__device__ __forceinline__ void store_staged(const float* st, void* dst, size_t row0, int nrows, bool f32, int lane) {
-  constexpr int kLpr = D / 8;      // lanes per row
+// Rows 0 .. nrows - 1 of a 32 x NC staging tile to columns col0 .. col0 +
+// NC - 1 of dst + row0 * D (row-major, bfloat16 or float32): every lane
+// moves 8 consecutive values of one row, so one store instruction covers
+// 512 / NC whole rows.
+template <int D, int NC = D>
+__device__ __forceinline__ void store_staged(const float* st, void* dst, size_t row0, int nrows, bool f32, int lane,
+                                             int col0 = 0) {
+  constexpr int kLpr = NC / 8;     // lanes per row
   constexpr int kRpp = 64 / kLpr;  // rows per pass
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging writes have landed
 #pragma unroll
   for (int pass = 0; pass < 32 / kRpp; ++pass) {
     const int r = pass * kRpp + lane / kLpr;
     const int c = 8 * (lane % kLpr);
-    const f32x4 a = *(const f32x4*)&st[stage_off<D>(r, c)];
-    const f32x4 b = *(const f32x4*)&st[stage_off<D>(r, c + 4)];
+    const f32x4 a = *(const f32x4*)&st[stage_off<NC>(r, c)];
+    const f32x4 b = *(const f32x4*)&st[stage_off<NC>(r, c + 4)];
     if (r < nrows) {
-      const size_t idx = (row0 + r) * D + c;
+      const size_t idx = (row0 + r) * D + col0 + c;
       if (f32) {
         *(f32x4*)((float*)dst + idx) = a;
         *(f32x4*)((float*)dst + idx + 4) = b;

@@ -8,15 +8,16 @@
 //
 // Work decomposition
 //   one workgroup = (batch b, head h, query tile of BQ = 128 rows), 4 waves,
-//   each wave owns 32 query rows; two workgroups share a CU.  K and V tiles
-//   stream into a double-buffered LDS ring with direct global -> LDS loads
-//   (no register staging); tile u + 1 is in flight while tile u is used.  The workgroup
-//   visits only the key tiles (BK = 64 rows) that intersect the diagonal strip
-//   [i - hi_h, i - lo_h] of its rows; inside a tile each wave skips the 32-key
-//   halves that miss its own 32-row strip, and masks element-wise only where
-//   a half is PARTIAL (a wave-uniform branch).  Workgroups are remapped so
-//   consecutive query tiles of one (b, h) run on the same XCD and share the
-//   K/V strip through that XCD's L2.
+//   each wave owns 32 query rows.  K and V tiles (BKT = 64 keys at d = 64,
+//   32 at d = 128) stream into a ring of LDS stages with direct global -> LDS
+//   loads (no register staging), one or two tiles ahead of the one in use.
+//   The workgroup visits only the key tiles that intersect the diagonal
+//   strip [i - hi_h, i - lo_h] of its rows; inside a tile each wave skips
+//   the 32-key halves that miss its own 32-row strip, and masks element-wise
+//   only where a half is PARTIAL (a wave-uniform branch).  Workgroups are
+//   remapped so consecutive query tiles of one (b, h) run on the same XCD
+//   and share the K/V strip through that XCD's L2, and the costliest query
+//   tiles (the last ones of a sequence) are dispatched first.
 // Products (transposed so no register shuffles are needed between them)
 //   S^T (keys x queries) = K Q^T    A = K rows from LDS, B = Q in registers
 //   O^T (d x queries)   += V^T P^T  A = V^T read from the row-major V tile
@@ -32,11 +33,8 @@
 namespace spattn {
 namespace {
 
-constexpr int kBQ = 128;
-constexpr int kBK = 64;
+constexpr int kBQ = 128;  // query rows per workgroup (4 waves of 32)
 constexpr int kThreads = 256;
-// query-major: 128 rows own 64-key tiles, a single run rotated (align_walk)
-constexpr WalkShape kWalk{kBQ, kBK, false, true};
 
 struct FwdArgs {
   const bf16* q;
@@ -54,20 +52,6 @@ struct FwdArgs {
   Bands bands;
 };
 
-// Element mask of a tile for query iq against key block kb:
-// base = iq - kb - 8 g - lo, width = hi - lo, and the same for the second
-// distance range when there is one.
-struct MaskArgs {
-  int base, width, base2, width2;
-};
-template <bool TWO>
-__device__ __forceinline__ void apply_mask(float* x, const MaskArgs& m, int shift) {
-  if constexpr (TWO)
-    band_mask2(x, m.base - shift, m.width, m.base2 - shift, m.width2);
-  else
-    band_mask(x, m.base - shift, m.width);
-}
-
 // Online-softmax state of one wave: O^T accumulator blocks, the reference
 // maximum of every query column (raw score units) and this lane's share of
 // the row sum, all relative to that reference.
@@ -84,10 +68,6 @@ struct OnlineState {
 // denominator share the reference, so the result is the same softmax.  Most
 // tiles then skip the rescale of the O accumulator entirely.
 constexpr float kRescaleLog2 = 8.0f;
-
-// Independent accumulator chains of the score product: one chain needs no
-// adds afterwards, and the interleaved softmax work covers its latency.
-constexpr int kChains = 1;
 
 // Row maximum of one 32-key half, new reference, correction factor for the
 // state accumulated so far (1 when the reference is kept) and the exponent
@@ -136,235 +116,41 @@ __device__ __forceinline__ void pv(OnlineState<D>& st, const bf16x8* va, bf16x8 
   }
 }
 
-// Both 32-key halves of a tile meet the wave's rows.  Software-pipelined so
-// the exponentials of half 0 issue between the score MFMAs of half 1 and
-// those of half 1 between the PV MFMAs of half 0.  When `masked` (a
-// wave-uniform flag) the band mask is applied to both halves; the mask sits
-// between phases, so its branch does not split an interleaved phase.
-template <int D, bool TWO>
-__device__ __forceinline__ void tile_pair(OnlineState<D>& st, const bf16* ks, const bf16* vs,
-                                          const LaneOffsets<D>& off, const bf16x8* qreg, float sl2, bool masked,
-                                          const MaskArgs& mk) {
-  constexpr int kKK = D / 16, kDT = D / 32;
-  // Phase boundaries are pinned (sched_barrier) so that operand reads of a
-  // later phase are not hoisted into an earlier one, where they would only
-  // lengthen register lifetimes.
-  bf16x8 ka[kKK];
-  load_ka<D>(ka, ks, off, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  const f32x16 s0 = mfma_ksum<kKK, kChains>(ka, qreg);
-  __builtin_amdgcn_sched_barrier(0);
-  load_ka<D>(ka, ks, off, 32);
-  float x0[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x0[i] = s0[i];
-  if (masked) apply_mask<TWO>(x0, mk, 0);
-  float alpha0, nms0;
-  bool moved0;
-  reference_update(x0, st.m_ref, sl2, alpha0, moved0, nms0);
-  __builtin_amdgcn_sched_barrier(0);
+// The forward kernel: one 32-key half at a time with a single straight-line
+// body (no software pipelining across halves, so the state is one
+// accumulator set and one score block) and a register budget for OCC
+// workgroups per CU, so the other waves of each SIMD hide one wave's
+// dependent MFMA / softmax chain.  K / V arrive in tiles of BKT keys (32 or
+// 64: one or two halves) through a ring of STAGES LDS stages, STAGES - 1
+// tiles ahead.  Per half: scores S^T = K Q^T, the element mask only where
+// the half is PARTIAL for this wave's rows, the reference update, P and its
+// row sum, O^T += V^T P^T.
+template <int D, int BKT, int STAGES, int OCC>
+struct FwdCfg {
+  static constexpr int kD = D, kBKT = BKT, kStages = STAGES, kOcc = OCC;
+  // query-major: 128 rows own BKT-key tiles, a single run rotated (align_walk)
+  static constexpr WalkShape walk{kBQ, BKT, false, true};
+};
+// d = 64: 64-key tiles, two stages (32 KB of LDS), 112 VGPRs: four
+// workgroups per CU.  d = 128: 32-key tiles, three stages (48 KB), 164
+// VGPRs: three workgroups per CU (measured against 64-key tiles at two per
+// CU and a four-stage ring at two per CU: 115 vs 122 and 125 us at
+// B8 H16 N4096; and against a cross-half pipelined kernel at two per CU:
+// 124 us).
+using Fwd64 = FwdCfg<64, 64, 2, 4>;
+using Fwd128 = FwdCfg<128, 32, 3, 3>;
 
-  // scores of half 1 || probabilities of half 0
-  const f32x16 s1 = mfma_ksum<kKK, kChains>(ka, qreg);
-  bf16x8 pa0, pa1;
-  st.l_run = st.l_run * alpha0 + probs(x0, sl2, nms0, pa0, pa1);
-  keep_here(pa0);
-  keep_here(pa1);
-  interleave_mfma_valu<kKK, 16 / kKK, 48 / kKK>();
-  __builtin_amdgcn_sched_barrier(0);
-  bf16x8 va[2 * kDT];
-  load_va<D>(va, vs, off, 0);  // in flight during the half-1 row maximum
-
-  float x1[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x1[i] = s1[i];
-  if (masked) apply_mask<TWO>(x1, mk, 32);
-  float alpha1, nms1;
-  bool moved1;
-  reference_update(x1, st.m_ref, sl2, alpha1, moved1, nms1);
-  if (moved0) rescale<D>(st, alpha0);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // PV of half 0 || probabilities of half 1
-  pv<D>(st, va, pa0, pa1);
-  bf16x8 pb0, pb1;
-  st.l_run = st.l_run * alpha1 + probs(x1, sl2, nms1, pb0, pb1);
-  keep_here(pb0);
-  keep_here(pb1);
-  interleave_mfma_valu<2 * kDT, 8 / kDT, 24 / kDT>();
-  __builtin_amdgcn_sched_barrier(0);
-  load_va<D>(va, vs, off, 32);
-  if (moved1) rescale<D>(st, alpha1);
-  __builtin_amdgcn_sched_barrier(0);
-  pv<D>(st, va, pb0, pb1);
-}
-
-// Only half m of the tile meets the wave's rows (always masked).
-template <int D, bool TWO>
-__device__ __forceinline__ void tile_half(OnlineState<D>& st, const bf16* ks, const bf16* vs,
-                                          const LaneOffsets<D>& off, const bf16x8* qreg, float sl2, int m,
-                                          const MaskArgs& mk) {
-  constexpr int kKK = D / 16, kDT = D / 32;
-  bf16x8 ka[kKK];
-  load_ka<D>(ka, ks, off, 32 * m);
-  __builtin_amdgcn_sched_barrier(0);
-  const f32x16 s = mfma_ksum<kKK, kChains>(ka, qreg);
-  __builtin_amdgcn_sched_barrier(0);
-  bf16x8 va[2 * kDT];
-  load_va<D>(va, vs, off, 32 * m);
-  float x[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = s[i];
-  apply_mask<TWO>(x, mk, 32 * m);
-  float alpha, nms;
-  bool moved;
-  reference_update(x, st.m_ref, sl2, alpha, moved, nms);
-  bf16x8 p0, p1;
-  st.l_run = st.l_run * alpha + probs(x, sl2, nms, p0, p1);
-  if (moved) rescale<D>(st, alpha);
-  pv<D>(st, va, p0, p1);
-}
-
-template <int D, bool TWO>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p) {
-  constexpr int kTile = kBK * D;  // one K or V tile, bf16 elements
-  using Tile = AsyncTile<kBK, D, kThreads / 64>;
-  constexpr int kDT = D / 32;      // 32-row output blocks of O^T
-  constexpr int kKK = D / 16;      // k-steps of the score product
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5;
-  const int c32 = lane & 31;
-
-  const WorkItem wi = work_item(blockIdx.x, p.B, p.H, p.n_qt, true);
-  if (!wi.valid) return;  // padding pair
-  const int t = wi.t;
-  const int h = wi.h;
-  const SeqHead sh = seq_head(p.cu, p.T, p.own_bdp, p.H, p.N, p.bands, wi.b, h);
-  const int N = sh.n;
-  if (t * kBQ >= N) return;  // past the end of a packed sequence
-  // the head's distance set: its band, joined with the local window if any
-  const DistSet dset = dist_set(sh.lo, sh.hi, TWO ? p.local_window : 0);
-  const int lo = dset.lo;
-  const int hi = dset.hi;
-  const size_t base = sh.row0 * D;
-  const bf16* __restrict__ qb = p.q + base;
-  const bf16* __restrict__ kb = p.k + base;
-  const bf16* __restrict__ vb = p.v + base;
-  bf16* __restrict__ ob = p.o + base;
-  float* __restrict__ lb = p.lse + sh.row0;
-  const float ninf = -__builtin_inff();
-
-  const int i_tile0 = t * kBQ;
-  const TileWalk walk = kernel_walk(kWalk, i_tile0, N, dset);
-  if (walk.n == 0) {
-    // No row of this tile has a key: output 0, LSE -inf.
-    constexpr int kCpr = D / 8;
-    for (int c = tid; c < kBQ * kCpr; c += kThreads) {
-      const int i = i_tile0 + c / kCpr;
-      if (i < N) *(u32x4*)(ob + (size_t)i * D + (c % kCpr) * 8) = u32x4{0, 0, 0, 0};
-    }
-    for (int r = tid; r < kBQ; r += kThreads)
-      if (i_tile0 + r < N) lb[i_tile0 + r] = ninf;
-    return;
-  }
-  const int iw0 = i_tile0 + 32 * wave;
-  const int iw1 = min(N - 1, iw0 + 31);
-  const bool wave_live = iw0 <= N - 1;
-  const int iq = iw0 + c32;
-
-  // First K / V tile before the Q loads: the two round trips overlap (the
-  // wait for Q covers both).
-  Tile::load(smem, kb, walk.at(0) * kBK, N, wave, lane);
-  Tile::load(smem + kTile, vb, walk.at(0) * kBK, N, wave, lane);
-
-  // Q^T operand: lane holds Q[iq][16kk + 8g .. +7].
-  bf16x8 qreg[kKK];
-#pragma unroll
-  for (int kk = 0; kk < kKK; ++kk)
-    qreg[kk] = iq < N ? *(const bf16x8*)(qb + (size_t)iq * D + 16 * kk + 8 * g) : bf16x8{};
-#pragma unroll
-  for (int kk = 0; kk < kKK; ++kk) settle(qreg[kk]);
-  LaneOffsets<D> off(lane);
-
-  OnlineState<D> st;
-#pragma unroll
-  for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.acc[dt][i] = 0.f;
-  st.m_ref = ninf;
-  st.l_run = 0.f;
-  const float sl2 = p.scale_log2;
-
-  // One tile from LDS stage S (a compile-time constant, so every LDS offset
-  // is an immediate).
-  auto step = [&](auto stage, int v) {
-    constexpr int S = decltype(stage)::value;
-    const int u = walk.at(v);
-    wait_vmcnt<0>();  // this wave's part of tile u has landed
-    __syncthreads();  // ... everyone's, and everyone is done with the previous tile
-    if (v + 1 < walk.n) {
-      bf16* nxt = smem + (S ^ 1) * 2 * kTile;
-      const int un = walk.at(v + 1);
-      Tile::load(nxt, kb, un * kBK, N, wave, lane);
-      Tile::load(nxt + kTile, vb, un * kBK, N, wave, lane);
-    }
-    const bf16* ks = smem + S * 2 * kTile;
-    const bf16* vs = ks + kTile;
-    off.refresh();
-    const int jb = u * kBK;
-    bool a0, a1, full;
-    if constexpr (TWO) {
-      a0 = wave_live && set_meets(iw0, iw1, jb, jb + 31, dset);
-      a1 = wave_live && set_meets(iw0, iw1, jb + 32, jb + 63, dset);
-      full = set_full(iw0, iw1, jb, jb + 63, dset);
-    } else {
-      a0 = wave_live && tile_meets(iw0, iw1, jb, jb + 31, lo, hi);
-      a1 = wave_live && tile_meets(iw0, iw1, jb + 32, jb + 63, lo, hi);
-      full = tile_full(iw0, iw1, jb, jb + 63, lo, hi);
-    }
-    const int rb = iq - jb - 8 * g;
-    const MaskArgs mk{rb - lo, hi - lo, rb - dset.nlo, dset.nhi - dset.nlo};
-    if (a0 && a1) {
-      tile_pair<D, TWO>(st, ks, vs, off, qreg, sl2, !full, mk);
-    } else if (a0 || a1) {
-      tile_half<D, TWO>(st, ks, vs, off, qreg, sl2, a0 ? 0 : 1, mk);
-    }
-  };
-  for (int v = 0; v < walk.n; v += 2) {
-    step(std::integral_constant<int, 0>{}, v);
-    if (v + 1 < walk.n) step(std::integral_constant<int, 1>{}, v + 1);
-  }
-
-  // ---- epilogue: O = acc / l, LSE = scale * m + ln(sum)
-  const float l_tot = pair_sum(st.l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (iq < N && g == 0) lb[iq] = l_tot > 0.f ? (st.m_ref * sl2 + fast_log2(l_tot)) * kLn2 : ninf;
-  __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
-  if (wave_live) {
-    float* stg = (float*)smem + wave * 32 * D;
-    stage_transposed<D>(stg, st.acc, inv, lane);
-    store_staged<D>(stg, p.o, sh.row0 + iw0, min(32, N - iw0), false, lane);
-  }
-}
-
-// Lean variant for small head sizes: one 32-key half at a time with a
-// single straight-line body (no software pipelining across halves, so the
-// state is one accumulator set and one score block) and a register budget of
-// 128 per lane, so four workgroups share a CU and the other waves of each
-// SIMD hide one wave's dependent MFMA / softmax chain.  Per half: scores
-// S^T = K Q^T, the element mask only where the half is PARTIAL for this
-// wave's rows, the reference update, P and its row sum, O^T += V^T P^T.
-template <int D, bool TWO>
-__global__ __launch_bounds__(kThreads, 4) void fwd_bf16_lean_kernel(FwdArgs p) {
-  constexpr int kTile = kBK * D;  // one K or V tile, bf16 elements
-  using Tile = AsyncTile<kBK, D, kThreads / 64>;
+template <typename C, bool TWO>
+__global__ __launch_bounds__(kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs p) {
+  constexpr int D = C::kD;
+  constexpr int BKT = C::kBKT;
+  constexpr int STAGES = C::kStages;
+  constexpr int kTile = BKT * D;  // one K or V tile, bf16 elements
+  using Tile = AsyncTile<BKT, D, kThreads / 64>;
+  constexpr int kL = 2 * Tile::kPer;  // loads per wave per tile (K and V)
   constexpr int kDT = D / 32;
   constexpr int kKK = D / 16;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];
+  __shared__ __attribute__((aligned(16))) bf16 smem[STAGES * 2 * kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -391,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 4) void fwd_bf16_lean_kernel(FwdArgs p) {
   const float ninf = -__builtin_inff();
 
   const int i_tile0 = t * kBQ;
-  const TileWalk walk = kernel_walk(kWalk, i_tile0, N, dset);
+  const TileWalk walk = kernel_walk(C::walk, i_tile0, N, dset);
   if (walk.n == 0) {
     // No row of this tile has a key: output 0, LSE -inf.
     constexpr int kCpr = D / 8;
@@ -408,8 +194,16 @@ __global__ __launch_bounds__(kThreads, 4) void fwd_bf16_lean_kernel(FwdArgs p) {
   const bool wave_live = iw0 <= N - 1;
   const int iq = iw0 + c32;
 
-  Tile::load(smem, kb, walk.at(0) * kBK, N, wave, lane);
-  Tile::load(smem + kTile, vb, walk.at(0) * kBK, N, wave, lane);
+  auto issue = [&](int v) {
+    bf16* st = smem + (v % STAGES) * 2 * kTile;
+    const int u = walk.at(v);
+    Tile::load(st, kb, u * BKT, N, wave, lane);
+    Tile::load(st + kTile, vb, u * BKT, N, wave, lane);
+  };
+  // the ring prefill before the Q loads: the round trips overlap
+#pragma unroll
+  for (int i = 0; i < STAGES - 1; ++i)
+    if (i < walk.n) issue(i);
 
   // Q^T operand: lane holds Q[iq][16kk + 8g .. +7].
   bf16x8 qreg[kKK];
@@ -470,32 +264,54 @@ __global__ __launch_bounds__(kThreads, 4) void fwd_bf16_lean_kernel(FwdArgs p) {
   };
   auto step = [&](auto stage, int v) {
     constexpr int S = decltype(stage)::value;
-    wait_vmcnt<0>();  // this wave's part of the tile has landed
-    __syncthreads();  // ... everyone's, and everyone is done with the previous tile
-    if (v + 1 < walk.n) {
-      bf16* nxt = smem + (S ^ 1) * 2 * kTile;
-      const int un = walk.at(v + 1);
-      Tile::load(nxt, kb, un * kBK, N, wave, lane);
-      Tile::load(nxt + kTile, vb, un * kBK, N, wave, lane);
-    }
+    // this wave's loads of tile v have landed: the ones still allowed in
+    // flight belong to the tiles after v that are already issued
+    const int ahead = min(STAGES - 2, walk.n - 1 - v);
+    if (STAGES >= 4 && ahead >= 2)
+      wait_vmcnt<2 * kL>();
+    else if (STAGES >= 3 && ahead >= 1)
+      wait_vmcnt<kL>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // ... everyone's, and everyone is done with tile v - 1
+    if (v + STAGES - 1 < walk.n) issue(v + STAGES - 1);  // into the stage tile v - 1 used
     off.refresh();
-    const int jb = walk.at(v) * kBK;
+    const int jb = walk.at(v) * BKT;
     half(stage, std::integral_constant<int, 0>{}, jb);
-    half(stage, std::integral_constant<int, 1>{}, jb);
+    if constexpr (BKT == 64) half(stage, std::integral_constant<int, 1>{}, jb);
   };
-  for (int v = 0; v < walk.n; v += 2) {
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  int v = 0;
+  for (; v + STAGES <= walk.n; v += STAGES) {
     step(std::integral_constant<int, 0>{}, v);
-    if (v + 1 < walk.n) step(std::integral_constant<int, 1>{}, v + 1);
+    step(std::integral_constant<int, 1>{}, v + 1);
+    if constexpr (STAGES >= 3) step(std::integral_constant<int, 2>{}, v + 2);
+    if constexpr (STAGES >= 4) step(std::integral_constant<int, 3>{}, v + 3);
   }
+  if (v < walk.n) step(std::integral_constant<int, 0>{}, v);
+  if (v + 1 < walk.n) step(std::integral_constant<int, 1>{}, v + 1);
+  if constexpr (STAGES >= 3)
+    if (v + 2 < walk.n) step(std::integral_constant<int, 2>{}, v + 2);
 
   const float l_tot = pair_sum(st.l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (iq < N && g == 0) lb[iq] = l_tot > 0.f ? (st.m_ref * sl2 + fast_log2(l_tot)) * kLn2 : ninf;
   __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
   if (wave_live) {
-    float* stg = (float*)smem + wave * 32 * D;
-    stage_transposed<D>(stg, st.acc, inv, lane);
-    store_staged<D>(stg, p.o, sh.row0 + iw0, min(32, N - iw0), false, lane);
+    // 32 x 64 floats per wave fit every ring here; d = 128 is written in two
+    // column passes (one wave's LDS operations complete in order, so the
+    // second pass's writes follow the first pass's reads)
+    constexpr int kNC = D < 64 ? D : 64;
+    static_assert(4 * 32 * kNC * 4 <= (int)sizeof(smem), "output staging fits the K / V ring");
+    float* stg = (float*)smem + wave * 32 * kNC;
+    const int nrows = min(32, N - iw0);
+    stage_transposed<D, kNC, 0>(stg, st.acc, inv, lane);
+    store_staged<D, kNC>(stg, p.o, sh.row0 + iw0, nrows, false, lane, 0);
+    if constexpr (D > kNC) {
+      static_assert(D == 2 * kNC, "two passes");
+      stage_transposed<D, kNC, kNC>(stg, st.acc, inv, lane);
+      store_staged<D, kNC>(stg, p.o, sh.row0 + iw0, nrows, false, lane, kNC);
+    }
   }
 }
 
@@ -525,23 +341,26 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   dim3 grid((unsigned)total), block(kThreads);
   const bool two = local_window > 0;
   if (d == 128 && !two)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<Fwd128, false>), grid, block, 0, stream, a);
   else if (d == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<Fwd128, true>), grid, block, 0, stream, a);
   else if (d == 64 && !two)
-    hipLaunchKernelGGL((fwd_bf16_lean_kernel<64, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<Fwd64, false>), grid, block, 0, stream, a);
   else if (d == 64)
-    hipLaunchKernelGGL((fwd_bf16_lean_kernel<64, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<Fwd64, true>), grid, block, 0, stream, a);
   else
     return SPATTN_E_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
 }
 
-void fwd_bf16_tiles(int* BQ, int* BK) {
-  *BQ = kBQ;
-  *BK = kBK;
+WalkShape fwd_bf16_walk(int d);
+
+void fwd_bf16_tiles(int d, int* BQ, int* BK) {
+  const WalkShape w = fwd_bf16_walk(d);
+  *BQ = w.own;
+  *BK = w.tile;
 }
 
-WalkShape fwd_bf16_walk() { return kWalk; }
+WalkShape fwd_bf16_walk(int d) { return d == 64 ? Fwd64::walk : Fwd128::walk; }
 
 }  // namespace spattn

@@ -16,9 +16,9 @@ int launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
 int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* lengths, int B,
                   int H, int Nmax, int d, int dtype, const Bands& bands, int local_window, float scale,
                   hipStream_t stream);
-void fwd_bf16_tiles(int* BQ, int* BK);
+void fwd_bf16_tiles(int d, int* BQ, int* BK);
 void fwd_f32_tiles(int* BQ, int* BK);
-WalkShape fwd_bf16_walk();
+WalkShape fwd_bf16_walk(int d);
 WalkShape bwd_bf16_dq_walk();
 WalkShape bwd_bf16_dkdv_walk();
 WalkShape fwd_f32_walk(int B, int H, int N);
@@ -449,7 +449,7 @@ int spattn_kernel_tiles(int32_t d, int32_t dtype, int32_t* BQ, int32_t* BK) {
   if (d != 64 && d != 128) return SPATTN_E_UNSUPPORTED;
   int bq, bk;
   if (dtype == SPATTN_BF16)
-    fwd_bf16_tiles(&bq, &bk);
+    fwd_bf16_tiles(d, &bq, &bk);
   else if (dtype == SPATTN_F32)
     fwd_f32_tiles(&bq, &bk);
   else
@@ -466,24 +466,25 @@ int spattn_tile_list(int32_t N, int32_t lo, int32_t hi, int32_t BQ, int32_t BK, 
   if (lo < 0 || hi > N - 1 || lo > hi + 1) return SPATTN_E_ARG;
   if (BQ == 0 || BK == 0) {
     if (BQ != BK) return SPATTN_E_ARG;
-    fwd_bf16_tiles(&BQ, &BK);
+    fwd_bf16_tiles(128, &BQ, &BK);
   }
   hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, N, lo, hi, BQ, BK, row_ptr,
                      tiles, kind, cap, n_out);
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
 }
 
-int spattn_tile_walk(int32_t kernel, int32_t dtype, int32_t B, int32_t H, int32_t N, int32_t lo, int32_t hi,
-                     int32_t local_window, int32_t* ptr, int32_t* tiles, uint8_t* kind, int32_t cap,
+int spattn_tile_walk(int32_t kernel, int32_t d, int32_t dtype, int32_t B, int32_t H, int32_t N, int32_t lo,
+                     int32_t hi, int32_t local_window, int32_t* ptr, int32_t* tiles, uint8_t* kind, int32_t cap,
                      int32_t* n_out, int32_t* own_rows, int32_t* tile_rows, void* stream) {
   if (B < 1 || H < 1 || N < 1 || cap < 0 || local_window < 0 || !ptr || !n_out ||
       (cap > 0 && (!tiles || !kind)))
     return SPATTN_E_ARG;
+  if (d != 64 && d != 128) return SPATTN_E_UNSUPPORTED;
   if (lo < 0 || hi > N - 1 || lo > hi + 1) return SPATTN_E_ARG;
   WalkShape ws;
   if (dtype == SPATTN_BF16) {
     if (kernel == SPATTN_KERNEL_FWD)
-      ws = fwd_bf16_walk();
+      ws = fwd_bf16_walk(d);
     else if (kernel == SPATTN_KERNEL_BWD_DQ)
       ws = bwd_bf16_dq_walk();
     else if (kernel == SPATTN_KERNEL_BWD_DKDV)

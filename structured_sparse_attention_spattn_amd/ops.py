@@ -329,7 +329,7 @@ def tile_list(N, lo, hi, BQ=0, BK=0, device="cuda"):
     return row_ptr.cpu().numpy(), tiles[:n].cpu().numpy(), kind[:n].cpu().numpy()
 
 
-def tile_walk(kernel, N, lo, hi, dtype=torch.bfloat16, B=1, H=1, local_window=0, device="cuda"):
+def tile_walk(kernel, N, lo, hi, dtype=torch.bfloat16, B=1, H=1, local_window=0, d=128, device="cuda"):
     """A kernel's actual tile walk for one band (spattn_tile_walk), as numpy
     (ptr, tiles, kind, own_rows, tile_rows): owned tile t visits
     tiles[ptr[t]:ptr[t + 1]] in that order."""
@@ -338,8 +338,8 @@ def tile_walk(kernel, N, lo, hi, dtype=torch.bfloat16, B=1, H=1, local_window=0,
     n_out = torch.zeros(1, dtype=torch.int32, device=device)
     # sizes first (cap 0 writes only ptr and the count)
     probe = torch.zeros(N + 1, dtype=torch.int32, device=device)
-    st = lib.spattn_tile_walk(int(kernel), _DT[dtype], B, H, N, lo, hi, int(local_window), _ptr(probe), None, None,
-                              0, _ptr(n_out), ctypes.byref(own), ctypes.byref(tile), _stream_handle(probe.device))
+    st = lib.spattn_tile_walk(int(kernel), int(d), _DT[dtype], B, H, N, lo, hi, int(local_window), _ptr(probe), None,
+                              None, 0, _ptr(n_out), ctypes.byref(own), ctypes.byref(tile), _stream_handle(probe.device))
     _lib.check(st, "spattn_tile_walk")
     torch.cuda.current_stream(probe.device).synchronize()
     n = int(n_out.item())
@@ -347,8 +347,8 @@ def tile_walk(kernel, N, lo, hi, dtype=torch.bfloat16, B=1, H=1, local_window=0,
     ptr = torch.zeros(n_own + 1, dtype=torch.int32, device=device)
     tiles = torch.zeros(max(n, 1), dtype=torch.int32, device=device)
     kind = torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
-    st = lib.spattn_tile_walk(int(kernel), _DT[dtype], B, H, N, lo, hi, int(local_window), _ptr(ptr), _ptr(tiles),
-                              _ptr(kind), n, _ptr(n_out), None, None, _stream_handle(ptr.device))
+    st = lib.spattn_tile_walk(int(kernel), int(d), _DT[dtype], B, H, N, lo, hi, int(local_window), _ptr(ptr),
+                              _ptr(tiles), _ptr(kind), n, _ptr(n_out), None, None, _stream_handle(ptr.device))
     _lib.check(st, "spattn_tile_walk")
     torch.cuda.current_stream(ptr.device).synchronize()
     return (ptr.cpu().numpy(), tiles[:n].cpu().numpy(), kind[:n].cpu().numpy(), own.value, tile.value)

@@ -82,8 +82,8 @@ int main(void) {
                                              SPATTN_BF16, NULL, NULL, 0, 0.0f, a, 16, NULL));
   printf("decode_dtype %d\n", spattn_decode(a, a, a, a, fa, NULL, 2, 4, 64, 128, 9, NULL, NULL, 0, 0.0f, NULL));
   int32_t n_out = 0;
-  printf("walk_kernel %d\n", spattn_tile_walk(5, SPATTN_BF16, 1, 1, 10, 0, 5, 0, &n_out, NULL, NULL, 0, &n_out, NULL,
-                                              NULL, NULL));
+  printf("walk_kernel %d\n", spattn_tile_walk(5, 128, SPATTN_BF16, 1, 1, 10, 0, 5, 0, &n_out, NULL, NULL, 0, &n_out,
+                                              NULL, NULL, NULL));
   printf("tile_list_band %d\n", spattn_tile_list(10, 0, 10, 64, 64, &n_out, NULL, NULL, 0, &n_out, NULL));
   printf("status %s|%s\n", spattn_status_string(SPATTN_E_WORKSPACE), spattn_status_string(-5));
   return 0;

@@ -190,8 +190,8 @@ def test_tile_walk_validation():
     lib = _lib.load()
     p = ctypes.c_void_p(1)
 
-    def walk(kernel=0, dtype=_lib.BF16, B=1, H=1, N=10, lo=0, hi=5, w=0, ptr=p, cap=4):
-        return lib.spattn_tile_walk(kernel, dtype, B, H, N, lo, hi, w, ptr, p, p, cap, p, None, None, None)
+    def walk(kernel=0, dtype=_lib.BF16, B=1, H=1, N=10, lo=0, hi=5, w=0, ptr=p, cap=4, d=128):
+        return lib.spattn_tile_walk(kernel, d, dtype, B, H, N, lo, hi, w, ptr, p, p, cap, p, None, None, None)
     assert walk(kernel=3) == _lib.E_ARG
     assert walk(kernel=-1) == _lib.E_ARG
     assert walk(dtype=4) == _lib.E_UNSUPPORTED
@@ -202,6 +202,7 @@ def test_tile_walk_validation():
     assert walk(w=-1) == _lib.E_ARG
     assert walk(ptr=None) == _lib.E_ARG
     assert walk(cap=-1) == _lib.E_ARG
+    assert walk(d=96) == _lib.E_UNSUPPORTED
 
 
 def test_decode_validation_before_launch():

@@ -159,14 +159,15 @@ def _walk_cases():
     for idx, w in WORKLOADS.items():
         lo, hi = oracle.band_table(w["N"], w["H"])
         for h in range(w["H"]):
-            cases.append((w["B"], w["H"], w["N"], int(lo[h]), int(hi[h]), 0))
-        cases.append((w["B"], w["H"], w["N"], int(lo[-1]), int(hi[-1]), 64))
-        cases.append((w["B"], w["H"], w["N"], int(lo[1]), int(hi[1]), int(lo[1])))  # window touching the band
+            cases.append((w["B"], w["H"], w["N"], int(lo[h]), int(hi[h]), 0, w["d"]))
+        cases.append((w["B"], w["H"], w["N"], int(lo[-1]), int(hi[-1]), 64, w["d"]))
+        cases.append((w["B"], w["H"], w["N"], int(lo[1]), int(hi[1]), int(lo[1]), w["d"]))  # window touching the band
     for N in (1, 5, 64, 129, 300, 1000):
         for (lo_, hi_) in [(0, N - 1), (0, 0), (N - 1, N - 1), (N // 3, N // 2), (N, N - 1)]:
             for w in (0, 1, 17, N // 2 + 3):
-                cases.append((1, 1, N, lo_, hi_, w))
-                cases.append((8, 16, N, lo_, hi_, w))  # float32: the larger launches' tiles
+                for d in (64, 128):
+                    cases.append((1, 1, N, lo_, hi_, w, d))
+                    cases.append((8, 16, N, lo_, hi_, w, d))  # float32: the larger launches' tiles
     return cases
 
 
@@ -182,8 +183,8 @@ def test_tile_walks_are_the_canonical_lists(kernel, dtype):
     key_major = kernel == 2
     cases = _walk_cases()
     _say(f"tile walks kernel={kernel} {dtype}: {len(cases)} cases")
-    for B, H, N, lo_, hi_, w in cases:
-        ptr, tl, kd, own, tile = ops.tile_walk(kernel, N, lo_, hi_, dtype=dtype, B=B, H=H, local_window=w)
+    for B, H, N, lo_, hi_, w, d in cases:
+        ptr, tl, kd, own, tile = ops.tile_walk(kernel, N, lo_, hi_, dtype=dtype, B=B, H=H, local_window=w, d=d)
         if key_major:
             optr, otl, okd = oracle.key_tile_list(N, lo_, hi_, tile, own, local_window=w)
         else:
