@@ -465,8 +465,9 @@ def variants_and_decode(q, k, v, do, o, lse, ws, grads, lo, hi, steps, dev):
 def measured_peaks(dev):
     """Measured denominators from libspattn_probe.so (spattn_probe.h): bf16
     and fp32 MFMA throughput (4 independent chains per wave, 16 waves per
-    CU, registers only) and the read bandwidth of a 4 GiB buffer; the best
-    of 3 launches each.  None where the probe library is not built."""
+    CU, registers only), LDS read bandwidth of the two read forms the kernels
+    use, and the read bandwidth of a 4 GiB buffer; the best of 3 launches
+    each.  None where the probe library is not built."""
     import torch
     path = os.path.join(ROOT, "structured_sparse_attention_spattn_amd", "libspattn_probe.so")
     if not os.path.exists(path):
@@ -494,11 +495,21 @@ def measured_peaks(dev):
         return min(ts)
 
     res = {"method": "libspattn_probe.so: 4 independent MFMA chains per wave, 4 workgroups x 4 waves per CU; "
+                     "conflict-free LDS reads, 4 workgroups x 4 waves per CU; "
                      "16-byte grid-stride reads of a 4 GiB buffer; best of 3 launches"}
     for kind, name, flop in ((0, "bf16_mfma_tflops", 32768), (1, "fp32_mfma_tflops", 4096)):
         iters = 2048 if kind == 0 else 1024
         ms = best_ms(lambda: lib.spattn_probe_mfma(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()), stream))
         res[name] = round(blocks * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12, 1)
+    lib.spattn_probe_lds.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    for kind, name in ((0, "lds_read_b128"), (1, "lds_read_b64_tr_b16")):
+        iters = 4096
+        ms = best_ms(lambda: lib.spattn_probe_lds(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()), stream))
+        tbs = blocks * 4 * iters * 8192 / (ms * 1e-3) / 1e12
+        # bytes per clock per CU at the 2.4 GHz peak engine clock
+        res[name + "_tbs"] = round(tbs, 1)
+        res[name + "_bytes_per_clk_cu"] = round(tbs * 1e12 / (256 * 2.4e9), 1)
     buf = torch.ones(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB
     nbytes = buf.numel() * 4
     ms = best_ms(lambda: lib.spattn_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, 256 * 8,

@@ -34,6 +34,15 @@ int spattn_probe_mfma(int32_t kind, int32_t blocks, int32_t iters, float* sink, 
  */
 int spattn_probe_read(const void* src, size_t bytes, int32_t blocks, float* sink, void* stream);
 
+/*
+ * LDS read bandwidth: `blocks` workgroups of 4 waves with a 32 KB LDS
+ * buffer each; every wave reads 8 KB per iteration for `iters` iterations in
+ * conflict-free 16-byte (kind 0: ds_read_b128) or 8-byte (kind 1: the
+ * transposing ds_read_b64_tr_b16) lane reads, and one float32 per lane goes
+ * to sink[blocks * 256].  Bytes of the launch: blocks * 4 * iters * 8192.
+ */
+int spattn_probe_lds(int32_t kind, int32_t blocks, int32_t iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,6 @@
 namespace spattn {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kZeroGroup = 4;  // query tiles without keys zeroed by one dQ workgroup
 
 struct BwdArgs {
@@ -55,18 +54,21 @@ struct BwdArgs {
 };
 
 // =====================================================================  dQ
-constexpr int kDqBQ = 128;    // query rows per workgroup
+constexpr int kDqWaves = 4;   // waves per workgroup, 32 query rows each
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqBQ = 32 * kDqWaves;  // query rows per workgroup
 constexpr int kDqBK = 32;     // key rows per stage
 constexpr int kDqStages = 4;  // LDS ring depth: tiles u+1 .. u+3 load while u is used
-// query-major: 128 rows own 32-key tiles, a single run rotated (align_walk)
+constexpr int kDqOcc = 2;     // waves per SIMD the register budget allows
+// query-major: the workgroup's rows own 32-key tiles, a single run rotated (align_walk)
 constexpr WalkShape kDqWalk{kDqBQ, kDqBK, false, true};
 
 template <int D, bool TWO>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
+__global__ __launch_bounds__(kDqThreads, kDqOcc) void bwd_dq_kernel(BwdArgs p) {
   constexpr int kTile = kDqBK * D;
   constexpr int kKK = D / 16;
   constexpr int kDT = D / 32;
-  using Tile = AsyncTile<kDqBK, D, kThreads / 64>;
+  using Tile = AsyncTile<kDqBK, D, kDqWaves>;
   constexpr int kL = 2 * Tile::kPer;  // loads per wave per stage
   __shared__ __attribute__((aligned(16))) bf16 smem[kDqStages * 2 * kTile];  // [stage][K, V]
 
@@ -200,10 +202,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   if (n_visit > 0) {
     LaneOffsets<D> off(lane);
     for (int v = 0; v < n_visit; ++v) {
-      const int ahead = n_visit - 1 - v;  // visits issued after v and possibly in flight
-      if (ahead >= 2)
+      // visits issued after v and possibly in flight
+      const int ahead = min(kDqStages - 2, n_visit - 1 - v);
+      if (kDqStages >= 4 && ahead >= 2)
         wait_vmcnt<2 * kL>();
-      else if (ahead == 1)
+      else if (kDqStages >= 3 && ahead >= 1)
         wait_vmcnt<kL>();
       else
         wait_vmcnt<0>();
@@ -283,9 +286,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs p) {
   }
   __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
   if (wave_live) {
-    float* stg = (float*)smem + wave * 32 * D;
-    stage_transposed<D>(stg, acc, scl, lane);  // dQ = scale sum dS K
-    store_staged<D>(stg, p.dq, sh.row0 + iw0, min(32, N - iw0), p.grad_f32 != 0, lane);
+    // dQ = scale sum dS K; 32 x 64 floats per wave fit the ring at any depth
+    constexpr int kNC = kDqWaves * 32 * D * 4 <= (int)sizeof(smem) ? D : D / 2;
+    static_assert(kDqWaves * 32 * kNC * 4 <= (int)sizeof(smem), "output staging fits the K / V ring");
+    store_result<D, kNC>((float*)smem + wave * 32 * kNC, acc, scl, p.dq, sh.row0 + iw0, min(32, N - iw0),
+                         p.grad_f32 != 0, lane);
   }
 }
 
@@ -706,7 +711,7 @@ int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* 
   a.local_window = local_window;
   const long long total = work_grid(B, H, a.n_tiles);
   if (total > 0x7fffffffLL) return SPATTN_E_ARG;
-  const dim3 grid((unsigned)total), block(kThreads);
+  const dim3 grid((unsigned)total), block(kDqThreads);
   const bool two = local_window > 0;
   if (d == 128 && !two)
     hipLaunchKernelGGL((bwd_dq_kernel<128, false>), grid, block, 0, stream, a);

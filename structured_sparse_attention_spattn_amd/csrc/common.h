@@ -448,6 +448,23 @@ __device__ __forceinline__ void store_staged(const float* st, void* dst, size_t 
   }
 }
 
+// A wave's 32 x D transposed result (accumulators times `mul`) to rows
+// row0 .. row0 + nrows - 1 of dst, through a staging area of 32 x NC floats
+// in one pass (NC = D) or two column passes (NC = D / 2; one wave's LDS
+// operations complete in order, so the second pass's writes follow the first
+// pass's reads).
+template <int D, int NC>
+__device__ __forceinline__ void store_result(float* stg, const f32x16* acc, float mul, void* dst, size_t row0,
+                                             int nrows, bool f32, int lane) {
+  static_assert(NC == D || 2 * NC == D, "one or two column passes");
+  stage_transposed<D, NC, 0>(stg, acc, mul, lane);
+  store_staged<D, NC>(stg, dst, row0, nrows, f32, lane, 0);
+  if constexpr (NC < D) {
+    stage_transposed<D, NC, NC>(stg, acc, mul, lane);
+    store_staged<D, NC>(stg, dst, row0, nrows, f32, lane, NC);
+  }
+}
+
 // Zero rows 0 .. nrows - 1 of dst + row0 * D, in the store pattern of
 // store_staged (no staging needed for a tile that received no products).
 template <int D>

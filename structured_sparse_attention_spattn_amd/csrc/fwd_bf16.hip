@@ -33,8 +33,6 @@
 namespace spattn {
 namespace {
 
-constexpr int kBQ = 128;  // query rows per workgroup (4 waves of 32)
-constexpr int kThreads = 256;
 
 struct FwdArgs {
   const bf16* q;
@@ -125,10 +123,12 @@ __device__ __forceinline__ void pv(OnlineState<D>& st, const bf16x8* va, bf16x8 
 // tiles ahead.  Per half: scores S^T = K Q^T, the element mask only where
 // the half is PARTIAL for this wave's rows, the reference update, P and its
 // row sum, O^T += V^T P^T.
-template <int D, int BKT, int STAGES, int OCC>
+template <int D, int BKT, int STAGES, int OCC, int WAVES = 4>
 struct FwdCfg {
-  static constexpr int kD = D, kBKT = BKT, kStages = STAGES, kOcc = OCC;
-  // query-major: 128 rows own BKT-key tiles, a single run rotated (align_walk)
+  static constexpr int kD = D, kBKT = BKT, kStages = STAGES, kOcc = OCC, kWaves = WAVES;
+  static constexpr int kBQ = 32 * WAVES;  // query rows per workgroup (32 per wave)
+  static constexpr int kThreads = 64 * WAVES;
+  // query-major: the workgroup's rows own BKT-key tiles, a single run rotated (align_walk)
   static constexpr WalkShape walk{kBQ, BKT, false, true};
 };
 // d = 64: 64-key tiles, two stages (32 KB of LDS), 112 VGPRs: four
@@ -141,12 +141,14 @@ using Fwd64 = FwdCfg<64, 64, 2, 4>;
 using Fwd128 = FwdCfg<128, 32, 3, 3>;
 
 template <typename C, bool TWO>
-__global__ __launch_bounds__(kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs p) {
+__global__ __launch_bounds__(C::kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs p) {
   constexpr int D = C::kD;
   constexpr int BKT = C::kBKT;
   constexpr int STAGES = C::kStages;
   constexpr int kTile = BKT * D;  // one K or V tile, bf16 elements
-  using Tile = AsyncTile<BKT, D, kThreads / 64>;
+  constexpr int kBQ = C::kBQ;
+  constexpr int kThreads = C::kThreads;
+  using Tile = AsyncTile<BKT, D, C::kWaves>;
   constexpr int kL = 2 * Tile::kPer;  // loads per wave per tile (K and V)
   constexpr int kDT = D / 32;
   constexpr int kKK = D / 16;
@@ -298,24 +300,28 @@ __global__ __launch_bounds__(kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs p) 
   if (iq < N && g == 0) lb[iq] = l_tot > 0.f ? (st.m_ref * sl2 + fast_log2(l_tot)) * kLn2 : ninf;
   __syncthreads();  // every wave is done with the K / V ring: it becomes the output staging area
   if (wave_live) {
-    // 32 x 64 floats per wave fit every ring here; d = 128 is written in two
-    // column passes (one wave's LDS operations complete in order, so the
-    // second pass's writes follow the first pass's reads)
+    // 32 x 64 floats per wave fit every ring here (d = 128: two passes)
     constexpr int kNC = D < 64 ? D : 64;
-    static_assert(4 * 32 * kNC * 4 <= (int)sizeof(smem), "output staging fits the K / V ring");
-    float* stg = (float*)smem + wave * 32 * kNC;
-    const int nrows = min(32, N - iw0);
-    stage_transposed<D, kNC, 0>(stg, st.acc, inv, lane);
-    store_staged<D, kNC>(stg, p.o, sh.row0 + iw0, nrows, false, lane, 0);
-    if constexpr (D > kNC) {
-      static_assert(D == 2 * kNC, "two passes");
-      stage_transposed<D, kNC, kNC>(stg, st.acc, inv, lane);
-      store_staged<D, kNC>(stg, p.o, sh.row0 + iw0, nrows, false, lane, kNC);
-    }
+    static_assert(C::kWaves * 32 * kNC * 4 <= (int)sizeof(smem), "output staging fits the K / V ring");
+    store_result<D, kNC>((float*)smem + wave * 32 * kNC, st.acc, inv, p.o, sh.row0 + iw0, min(32, N - iw0), false,
+                         lane);
   }
 }
 
 }  // namespace
+
+template <typename C>
+static int launch_cfg(FwdArgs a, bool two, hipStream_t stream) {
+  a.n_qt = (a.N + C::kBQ - 1) / C::kBQ;
+  const long long total = work_grid(a.B, a.H, a.n_qt);
+  if (total > 0x7fffffffLL) return SPATTN_E_ARG;
+  const dim3 grid((unsigned)total), block(C::kThreads);
+  if (two)
+    hipLaunchKernelGGL((fwd_bf16_kernel<C, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<C, false>), grid, block, 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
+}
 
 int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                     int N, int d, const Bands& bands, int local_window, float scale, const Packed& pk,
@@ -329,28 +335,16 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   a.B = B;
   a.H = H;
   a.N = N;
-  a.n_qt = (N + kBQ - 1) / kBQ;
   a.cu = pk.cu;
   a.T = pk.T;
   a.own_bdp = pk.own_bdp;
   a.local_window = local_window;
   a.scale_log2 = scale * kLog2e;
   a.bands = bands;
-  const long long total = work_grid(B, H, a.n_qt);
-  if (total > 0x7fffffffLL) return SPATTN_E_ARG;
-  dim3 grid((unsigned)total), block(kThreads);
   const bool two = local_window > 0;
-  if (d == 128 && !two)
-    hipLaunchKernelGGL((fwd_bf16_kernel<Fwd128, false>), grid, block, 0, stream, a);
-  else if (d == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<Fwd128, true>), grid, block, 0, stream, a);
-  else if (d == 64 && !two)
-    hipLaunchKernelGGL((fwd_bf16_kernel<Fwd64, false>), grid, block, 0, stream, a);
-  else if (d == 64)
-    hipLaunchKernelGGL((fwd_bf16_kernel<Fwd64, true>), grid, block, 0, stream, a);
-  else
-    return SPATTN_E_UNSUPPORTED;
-  return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_E_HIP;
+  if (d == 128) return launch_cfg<Fwd128>(a, two, stream);
+  if (d == 64) return launch_cfg<Fwd64>(a, two, stream);
+  return SPATTN_E_UNSUPPORTED;
 }
 
 WalkShape fwd_bf16_walk(int d);

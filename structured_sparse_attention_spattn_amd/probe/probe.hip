@@ -1,6 +1,7 @@
 // Microbenchmarks for the measured denominators (declared in spattn_probe.h):
-// matrix-core throughput of the two MFMA shapes the kernels use, and the HBM
-// read bandwidth of plain 16-byte loads.
+// matrix-core throughput of the two MFMA shapes the kernels use, the HBM
+// read bandwidth of plain 16-byte loads, and the LDS read bandwidth of the
+// two LDS read forms the kernels use.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,6 +51,43 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const f32x4* __restrict
   sink[blockIdx.x * 256 + threadIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+// LDS reads from a 32 KB workgroup buffer: every wave reads 8 KB per
+// iteration, each read instruction a contiguous 1 KB (KIND 0: ds_read_b128)
+// or 512 B (KIND 1: ds_read_b64_tr_b16) block, so no bank conflicts.  The
+// block offset moves with the iteration so no read is loop-invariant.
+template <int KIND>
+__global__ __launch_bounds__(256) void lds_probe_kernel(int iters, float* sink) {
+  __shared__ __attribute__((aligned(16))) uint32_t buf[8192];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < 8192; i += 256) buf[i] = (uint32_t)(i * 2654435761u);
+  __syncthreads();
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it) {
+    const int base = ((it * 7 + wave * 3) & 3) * 8192;  // byte offset of an 8 KB quarter
+    if constexpr (KIND == 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const u32x4 v = *(const u32x4*)((const char*)buf + ((base + k * 1024 + lane * 16) & 32767));
+        acc ^= v[0] + v[1] + v[2] + v[3];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const char* ptr = (const char*)buf + ((base + k * 512 + lane * 8) & 32767);
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)ptr);
+        acc ^= (uint32_t)(v[0] + v[1] + v[2] + v[3]);
+      }
+    }
+  }
+  sink[blockIdx.x * 256 + tid] = (float)acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -67,6 +105,15 @@ int spattn_probe_read(const void* src, size_t bytes, int32_t blocks, float* sink
   if (src == nullptr || sink == nullptr || blocks < 1 || bytes % 16 != 0 || ((uintptr_t)src & 15u) != 0) return 1;
   hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const f32x4*)src,
                      bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int spattn_probe_lds(int32_t kind, int32_t blocks, int32_t iters, float* sink, void* stream) {
+  if (blocks < 1 || iters < 1 || sink == nullptr || (kind != 0 && kind != 1)) return 1;
+  if (kind == 0)
+    hipLaunchKernelGGL(lds_probe_kernel<0>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+  else
+    hipLaunchKernelGGL(lds_probe_kernel<1>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

@@ -36,6 +36,30 @@ def test_library_exports_every_declared_symbol():
     assert set(_declared_functions()) <= exported
 
 
+def test_probe_library_exports_every_declared_symbol():
+    """libspattn_probe.so (the measured-denominator microbenchmarks) exports
+    what include/spattn_probe.h declares and rejects bad arguments on the host."""
+    path = os.path.join(ROOT, "structured_sparse_attention_spattn_amd", "libspattn_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libspattn_probe.so not built")
+    text = open(os.path.join(ROOT, "include", "spattn_probe.h")).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(spattn_probe_\w+)\s*\(", text, flags=re.M)))
+    assert names == ["spattn_probe_lds", "spattn_probe_mfma", "spattn_probe_read"]
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    assert set(names) <= set(re.findall(r"\bT (spattn_probe_\w+)", out))
+    lib = ctypes.CDLL(path)
+    sink = ctypes.c_void_p(16)  # never dereferenced: every call below fails its argument check
+    assert lib.spattn_probe_mfma(2, 1, 1, sink, None) == 1
+    assert lib.spattn_probe_mfma(0, 0, 1, sink, None) == 1
+    assert lib.spattn_probe_lds(2, 1, 1, sink, None) == 1
+    assert lib.spattn_probe_lds(0, 1, 0, sink, None) == 1
+    assert lib.spattn_probe_lds(0, 1, 1, None, None) == 1
+    lib.spattn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    assert lib.spattn_probe_read(sink, 15, 1, sink, None) == 1
+
+
 @pytest.mark.parametrize("N", range(1, 65))
 def test_band_table_bit_exact_vs_oracle(N):
     for H in range(1, 17):
