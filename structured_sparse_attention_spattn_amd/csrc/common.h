@@ -277,6 +277,33 @@ struct AsyncTile {
       lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr(tile + rb * D)), src + (size_t)grow * D + c * 8);
     }
   }
+  // The per-lane source offsets of a wave's pieces relative to the tile's
+  // first row (element units): fixed for the whole walk, so a tile that lies
+  // inside the rows [0, N) costs one address add per piece.
+  struct Offsets {
+    int e[kPer];
+    __device__ __forceinline__ Offsets(int wave, int lane) {
+      const int lr = lane / (D / 8), p = lane % (D / 8);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int r = ((wave + WAVES * i) % kPieces) * kRpi + lr;
+        e[i] = r * D + (p ^ swz<D>(r)) * 8;
+      }
+    }
+  };
+  __device__ __forceinline__ static void load(bf16* tile, const bf16* __restrict__ src, int row0, int N,
+                                              const Offsets& o, int wave, int lane) {
+    if (row0 + ROWS > N) {  // the sequence's last tile: clamped rows
+      load(tile, src, row0, N, wave, lane);
+      return;
+    }
+    const bf16* base = src + (size_t)row0 * D;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int rb = ((wave + WAVES * i) % kPieces) * kRpi;
+      lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr(tile + rb * D)), base + o.e[i]);
+    }
+  }
 };
 
 // Make the compiler complete the load that produced x here (it inserts the

@@ -196,11 +196,12 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs 
   const bool wave_live = iw0 <= N - 1;
   const int iq = iw0 + c32;
 
+  const typename Tile::Offsets toff(wave, lane);
   auto issue = [&](int v) {
     bf16* st = smem + (v % STAGES) * 2 * kTile;
     const int u = walk.at(v);
-    Tile::load(st, kb, u * BKT, N, wave, lane);
-    Tile::load(st + kTile, vb, u * BKT, N, wave, lane);
+    Tile::load(st, kb, u * BKT, N, toff, wave, lane);
+    Tile::load(st + kTile, vb, u * BKT, N, toff, wave, lane);
   };
   // the ring prefill before the Q loads: the round trips overlap
 #pragma unroll
