@@ -51,12 +51,15 @@ struct FwdArgs {
 };
 
 // Online-softmax state of one wave: O^T accumulator blocks, the reference
-// maximum of every query column (raw score units) and this lane's share of
-// the row sum, all relative to that reference.
+// maximum of every query column (raw score units) with its move threshold
+// and exponent offset, and this lane's share of the row sum, all relative to
+// that reference.
 template <int D>
 struct OnlineState {
   f32x16 acc[D / 32];
   float m_ref;
+  float m_thr;  // m_ref + 2^kRescaleLog2 in score units (-inf while m_ref is)
+  float nms;    // exponent offset of the probabilities: -m_ref log2(e) scale (0 while m_ref is -inf)
   float l_run;
 };
 
@@ -66,6 +69,7 @@ struct OnlineState {
 // denominator share the reference, so the result is the same softmax.  Most
 // tiles then skip the rescale of the O accumulator entirely.
 constexpr float kRescaleLog2 = 8.0f;
+
 
 // Row maximum of one 32-key half, new reference, correction factor for the
 // state accumulated so far (1 when the reference is kept) and the exponent
@@ -223,6 +227,8 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs 
 #pragma unroll
     for (int i = 0; i < 16; ++i) st.acc[dt][i] = 0.f;
   st.m_ref = ninf;
+  st.m_thr = ninf;
+  st.nms = 0.f;
   st.l_run = 0.f;
   const float sl2 = p.scale_log2;
 
@@ -255,11 +261,22 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs 
       else
         band_mask(x, rb - lo, hi - lo);
     }
-    float alpha, nms;
-    bool moved;
-    reference_update(x, st.m_ref, sl2, alpha, moved, nms);
     bf16x8 p0, p1;
-    st.l_run = st.l_run * alpha + probs(x, sl2, nms, p0, p1);
+    // The reference moves only when some row's maximum passes it by more than
+    // 2^kRescaleLog2.  Each lane tests its own 16 scores against that
+    // threshold (no lane exchange); when no lane of the wave passes it and
+    // every row already has a reference, the reference update and its
+    // correction factor are skipped.
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+    float alpha = 1.f;
+    bool moved = false;
+    if (__ballot(!(mx <= st.m_thr)) != 0) {
+      reference_update(x, st.m_ref, sl2, alpha, moved, st.nms);
+      st.m_thr = st.m_ref == -__builtin_inff() ? -__builtin_inff() : st.m_ref + kRescaleLog2 / sl2;
+    }
+    st.l_run = st.l_run * alpha + probs(x, sl2, st.nms, p0, p1);
     if (moved) rescale<D>(st, alpha);
     bf16x8 va[2 * kDT];
     load_va<D>(va, vs, off, 32 * M);
