@@ -135,10 +135,10 @@ struct FwdCfg {
   // query-major: the workgroup's rows own BKT-key tiles, a single run rotated (align_walk)
   static constexpr WalkShape walk{kBQ, BKT, false, true};
 };
-// d = 64: 64-key tiles, two stages (32 KB of LDS), 112 VGPRs: four
-// workgroups per CU.  d = 128: 32-key tiles, three stages (48 KB), 164
-// VGPRs: three workgroups per CU (measured against 64-key tiles at two per
-// CU and a four-stage ring at two per CU: 115 vs 122 and 125 us at
+// d = 64: 64-key tiles, two stages (32 KB of LDS), at most 128 VGPRs: four
+// workgroups per CU.  d = 128: 32-key tiles, three stages (48 KB), at most
+// 168 VGPRs: three workgroups per CU (measured against 64-key tiles at two
+// per CU and a four-stage ring at two per CU: 115 vs 122 and 125 us at
 // B8 H16 N4096; and against a cross-half pipelined kernel at two per CU:
 // 124 us).
 using Fwd64 = FwdCfg<64, 64, 2, 4>;
