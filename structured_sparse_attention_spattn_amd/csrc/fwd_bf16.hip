@@ -51,29 +51,37 @@ struct FwdArgs {
 };
 
 // Online-softmax state of one wave: O^T accumulator blocks, the reference
-// maximum of every query column (raw score units) with its move threshold
-// and exponent offset, and this lane's share of the row sum, all relative to
-// that reference.
+// maximum of every query column (raw score units) with the exponent offset of
+// its probabilities, and this lane's share of the row sum relative to that
+// reference; plus what each of the two tests below keeps.
 template <int D>
 struct OnlineState {
   f32x16 acc[D / 32];
   float m_ref;
-  float m_thr;  // m_ref + 2^kRescaleLog2 in score units (-inf while m_ref is)
   float nms;    // exponent offset of the probabilities: -m_ref log2(e) scale (0 while m_ref is -inf)
   float l_run;
+  float m_thr;  // maximum test: m_ref + kProbBoundLog2 / (log2(e) scale), -inf while m_ref is
+  bool ready;   // sum test: no row of the wave has m_ref = -inf (wave-uniform)
 };
 
-// A new reference maximum is taken only when some row's maximum has grown by
-// more than 2^kRescaleLog2 over its reference (wave-uniform decision): until
-// then probabilities are exp2 of at most kRescaleLog2, and numerator and
-// denominator share the reference, so the result is the same softmax.  Most
-// tiles then skip the rescale of the O accumulator entirely.
-constexpr float kRescaleLog2 = 8.0f;
+// The reference of a row is moved (to the row's running maximum, rescaling
+// what was accumulated) only when one of its probabilities could pass
+// 2^kProbBoundLog2; until then numerator and denominator share the reference,
+// so the result is the same softmax.  The decision is wave-uniform, and with
+// scores of moderate range only a row's first half takes it.  Two tests:
+//   maximum test: each lane compares the maximum of its 16 scores with m_thr;
+//   sum test: once every row of the wave has a reference, the probabilities
+//     are taken against it first; when the 16 of a lane sum to at most
+//     2^kProbBoundLog2 each of them is at most that and the reference stays,
+//     so the other halves never form a row maximum.  Otherwise the wave
+//     recomputes the half's scores and moves the reference.
+constexpr float kProbBoundLog2 = 8.0f;
+constexpr float kProbBound = 256.0f;  // 2^kProbBoundLog2
 
-
-// Row maximum of one 32-key half, new reference, correction factor for the
-// state accumulated so far (1 when the reference is kept) and the exponent
-// offset -m_ref * scale_log2 of the probabilities.
+// Row maximum of one 32-key half, the new reference (the running maximum),
+// the correction factor of the state accumulated so far (1 where the
+// reference stays, 0 where there was none) and the exponent offset
+// -m_ref * scale_log2 of the probabilities.
 __device__ __forceinline__ void reference_update(const float* x, float& m_ref, float sl2, float& alpha, bool& moved,
                                                  float& nms) {
   float mx = x[0];
@@ -81,18 +89,20 @@ __device__ __forceinline__ void reference_update(const float* x, float& m_ref, f
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
   mx = pair_max(mx);
   const float m_new = fmaxf(m_ref, mx);
-  moved = __ballot((m_new - m_ref) * sl2 > kRescaleLog2) != 0;  // -inf - -inf is NaN: false
-  const float m_next = moved ? m_new : m_ref;
-  alpha = m_next == m_ref ? 1.f : fast_exp2((m_ref - m_next) * sl2);
-  m_ref = m_next;
+  moved = __ballot(m_new > m_ref) != 0;
+  alpha = m_new == m_ref ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+  m_ref = m_new;
   nms = -(m_ref == -__builtin_inff() ? 0.f : m_ref) * sl2;
 }
 
-// Probabilities of one half (in place), their sum, packed as the P^T operand.
+// Probabilities of one half against the exponent offset nms (in place), their
+// float32 sum (the row sum, and through it the LSE, stays at float32
+// accuracy), packed as the P^T operand.
 __device__ __forceinline__ float probs(float* x, float sl2, float nms, bf16x8& p0, bf16x8& p1) {
-  float sum = 0.f;
+  x[0] = fast_exp2(__builtin_fmaf(x[0], sl2, nms));
+  float sum = x[0];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 1; i < 16; ++i) {
     x[i] = fast_exp2(__builtin_fmaf(x[i], sl2, nms));
     sum += x[i];
   }
@@ -127,22 +137,24 @@ __device__ __forceinline__ void pv(OnlineState<D>& st, const bf16x8* va, bf16x8 
 // tiles ahead.  Per half: scores S^T = K Q^T, the element mask only where
 // the half is PARTIAL for this wave's rows, the reference update, P and its
 // row sum, O^T += V^T P^T.
-template <int D, int BKT, int STAGES, int OCC, int WAVES = 4>
+template <int D, int BKT, int STAGES, int OCC, bool SUM_TEST, int WAVES = 4>
 struct FwdCfg {
   static constexpr int kD = D, kBKT = BKT, kStages = STAGES, kOcc = OCC, kWaves = WAVES;
+  static constexpr bool kSumTest = SUM_TEST;  // the sum test of the reference, else the maximum test
   static constexpr int kBQ = 32 * WAVES;  // query rows per workgroup (32 per wave)
   static constexpr int kThreads = 64 * WAVES;
   // query-major: the workgroup's rows own BKT-key tiles, a single run rotated (align_walk)
   static constexpr WalkShape walk{kBQ, BKT, false, true};
 };
 // d = 64: 64-key tiles, two stages (32 KB of LDS), at most 128 VGPRs: four
-// workgroups per CU.  d = 128: 32-key tiles, three stages (48 KB), at most
-// 168 VGPRs: three workgroups per CU (measured against 64-key tiles at two
-// per CU and a four-stage ring at two per CU: 115 vs 122 and 125 us at
-// B8 H16 N4096; and against a cross-half pipelined kernel at two per CU:
-// 124 us).
-using Fwd64 = FwdCfg<64, 64, 2, 4>;
-using Fwd128 = FwdCfg<128, 32, 3, 3>;
+// workgroups per CU; the sum test (its halves are VALU-bound: 4 % faster than
+// the maximum test at B2 H12 N10000).  d = 128: 32-key tiles, three stages
+// (48 KB), at most 168 VGPRs: three workgroups per CU (measured against 64-key
+// tiles at two per CU and a four-stage ring at two per CU: 115 vs 122 and
+// 125 us at B8 H16 N4096; and against a cross-half pipelined kernel at two per
+// CU: 124 us); the maximum test (the sum test's recompute path spills there).
+using Fwd64 = FwdCfg<64, 64, 2, 4, true>;
+using Fwd128 = FwdCfg<128, 32, 3, 3, false>;
 
 template <typename C, bool TWO>
 __global__ __launch_bounds__(C::kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs p) {
@@ -227,8 +239,9 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs 
 #pragma unroll
     for (int i = 0; i < 16; ++i) st.acc[dt][i] = 0.f;
   st.m_ref = ninf;
-  st.m_thr = ninf;
   st.nms = 0.f;
+  st.m_thr = ninf;
+  st.ready = false;
   st.l_run = 0.f;
   const float sl2 = p.scale_log2;
 
@@ -248,39 +261,66 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs 
     if (!meets) return;
     const bf16* ks = smem + S * 2 * kTile;
     const bf16* vs = ks + kTile;
-    bf16x8 ka[kKK];
-    load_ka<D>(ka, ks, off, 32 * M);
-    const f32x16 sc = mfma_ksum<kKK, 1>(ka, qreg);
-    float x[16];
+    // S^T of the half, masked to the distance set where the half is partial
+    // for this wave's rows
+    auto scores = [&](float* x, const LaneOffsets<D>& o) {
+      bf16x8 ka[kKK];
+      load_ka<D>(ka, ks, o, 32 * M);
+      const f32x16 sc = mfma_ksum<kKK, 1>(ka, qreg);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = sc[i];
-    if (!full) {
-      const int rb = iq - j0 - 8 * g;
-      if constexpr (TWO)
-        band_mask2(x, rb - lo, hi - lo, rb - dset.nlo, dset.nhi - dset.nlo);
-      else
-        band_mask(x, rb - lo, hi - lo);
-    }
-    bf16x8 p0, p1;
-    // The reference moves only when some row's maximum passes it by more than
-    // 2^kRescaleLog2.  Each lane tests its own 16 scores against that
-    // threshold (no lane exchange); when no lane of the wave passes it and
-    // every row already has a reference, the reference update and its
-    // correction factor are skipped.
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-    float alpha = 1.f;
-    bool moved = false;
-    if (__ballot(!(mx <= st.m_thr)) != 0) {
+      for (int i = 0; i < 16; ++i) x[i] = sc[i];
+      if (!full) {
+        const int rb = iq - j0 - 8 * g;
+        if constexpr (TWO)
+          band_mask2(x, rb - lo, hi - lo, rb - dset.nlo, dset.nhi - dset.nlo);
+        else
+          band_mask(x, rb - lo, hi - lo);
+      }
+    };
+    // new references for the wave's rows (wave-uniform)
+    auto take_reference = [&](const float* x) {
+      float alpha;
+      bool moved;
       reference_update(x, st.m_ref, sl2, alpha, moved, st.nms);
-      st.m_thr = st.m_ref == -__builtin_inff() ? -__builtin_inff() : st.m_ref + kRescaleLog2 / sl2;
+      st.ready = __ballot(st.m_ref == -__builtin_inff()) == 0;
+      st.m_thr = st.m_ref == -__builtin_inff() ? -__builtin_inff() : st.m_ref + kProbBoundLog2 / sl2;
+      if (moved) {
+        rescale<D>(st, alpha);
+        st.l_run *= alpha;
+      }
+    };
+    // the row sum and O^T += V^T P^T
+    auto finish = [&](float s, bf16x8 p0, bf16x8 p1) {
+      st.l_run += s;
+      bf16x8 va[2 * kDT];
+      load_va<D>(va, vs, off, 32 * M);
+      pv<D>(st, va, p0, p1);
+    };
+    float x[16];
+    scores(x, off);
+    bf16x8 p0, p1;
+    if constexpr (C::kSumTest) {
+      if (st.ready) {
+        const float s = probs(x, sl2, st.nms, p0, p1);
+        if (__ballot(!(s <= kProbBound)) == 0) {
+          finish(s, p0, p1);
+          return;
+        }
+        // the scores again from the K tile, still in its stage (the empty
+        // asm with a memory clobber makes the compiler reload the operands
+        // instead of holding the first ones all along)
+        asm volatile("" ::: "memory");
+        scores(x, off);
+      }
+      take_reference(x);
+    } else {
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      if (__ballot(!(mx <= st.m_thr)) != 0) take_reference(x);
     }
-    st.l_run = st.l_run * alpha + probs(x, sl2, st.nms, p0, p1);
-    if (moved) rescale<D>(st, alpha);
-    bf16x8 va[2 * kDT];
-    load_va<D>(va, vs, off, 32 * M);
-    pv<D>(st, va, p0, p1);
+    const float s = probs(x, sl2, st.nms, p0, p1);
+    finish(s, p0, p1);
   };
   auto step = [&](auto stage, int v) {
     constexpr int S = decltype(stage)::value;
