@@ -466,8 +466,9 @@ def measured_peaks(dev):
     """Measured denominators from libspattn_probe.so (spattn_probe.h): bf16
     and fp32 MFMA throughput (4 independent chains per wave, 16 waves per
     CU, registers only), LDS read bandwidth of the two read forms the kernels
-    use, and the read bandwidth of a 4 GiB buffer; the best of 3 launches
-    each.  None where the probe library is not built."""
+    use, float32 atomic-add throughput into 256 MiB and 1 MiB, and the read
+    bandwidth of a 4 GiB buffer; the best of 3 launches each.  None where the
+    probe library is not built."""
     import torch
     path = os.path.join(ROOT, "structured_sparse_attention_spattn_amd", "libspattn_probe.so")
     if not os.path.exists(path):
@@ -496,6 +497,7 @@ def measured_peaks(dev):
 
     res = {"method": "libspattn_probe.so: 4 independent MFMA chains per wave, 4 workgroups x 4 waves per CU; "
                      "conflict-free LDS reads, 4 workgroups x 4 waves per CU; "
+                     "float32 atomic adds without return, 256 B per wave instruction, 4 workgroups per CU; "
                      "16-byte grid-stride reads of a 4 GiB buffer; best of 3 launches"}
     for kind, name, flop in ((0, "bf16_mfma_tflops", 32768), (1, "fp32_mfma_tflops", 4096)):
         iters = 2048 if kind == 0 else 1024
@@ -510,6 +512,16 @@ def measured_peaks(dev):
         # bytes per clock per CU at the 2.4 GHz peak engine clock
         res[name + "_tbs"] = round(tbs, 1)
         res[name + "_bytes_per_clk_cu"] = round(tbs * 1e12 / (256 * 2.4e9), 1)
+    # float32 atomic adds (no return) into a buffer the size of an fp32 dQ
+    # accumulator at B=8 H=16 N=4096 d=128 (256 MiB) and into 1 MiB (L2)
+    lib.spattn_probe_atomic.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p]
+    for nfl, name in ((1 << 26, "atomic_add_f32_256mib_gbs"), (1 << 18, "atomic_add_f32_1mib_gbs")):
+        abuf = torch.zeros(nfl, dtype=torch.float32, device=dev)
+        iters = 1024
+        ms = best_ms(lambda: lib.spattn_probe_atomic(ctypes.c_void_p(abuf.data_ptr()), nfl, blocks, iters, stream))
+        res[name] = round(blocks * 256 * iters * 4 / (ms * 1e-3) / 1e9, 1)
+        del abuf
     buf = torch.ones(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB
     nbytes = buf.numel() * 4
     ms = best_ms(lambda: lib.spattn_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, 256 * 8,

@@ -43,6 +43,17 @@ int spattn_probe_read(const void* src, size_t bytes, int32_t blocks, float* sink
  */
 int spattn_probe_lds(int32_t kind, int32_t blocks, int32_t iters, float* sink, void* stream);
 
+/*
+ * float32 atomic-add throughput: `blocks` workgroups of 256 lanes each issue
+ * `iters` atomic adds of 1.0 without return (global_atomic_add_f32) into the
+ * device buffer dst of n_floats floats (a power of two, at least 256; dst
+ * 256-byte aligned), lane l of the launch at float (l + k * blocks * 256) mod
+ * n_floats in its k-th add, so every wave instruction covers 256 contiguous
+ * bytes.
+ * dst is modified.  Bytes added by the launch: blocks * 256 * iters * 4.
+ */
+int spattn_probe_atomic(float* dst, size_t n_floats, int32_t blocks, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,7 +1,8 @@
 // Microbenchmarks for the measured denominators (declared in spattn_probe.h):
 // matrix-core throughput of the two MFMA shapes the kernels use, the HBM
-// read bandwidth of plain 16-byte loads, and the LDS read bandwidth of the
-// two LDS read forms the kernels use.
+// read bandwidth of plain 16-byte loads, the LDS read bandwidth of the two
+// LDS read forms the kernels use, and the throughput of float32 atomic adds
+// into device memory (what a backward accumulating dQ with atomics needs).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -88,6 +89,19 @@ __global__ __launch_bounds__(256) void lds_probe_kernel(int iters, float* sink) 
   sink[blockIdx.x * 256 + tid] = (float)acc;
 }
 
+// float32 atomic adds without return (global_atomic_add_f32), each wave
+// adding to 64 consecutive floats (256 B) per instruction, the lanes of the
+// launch covering the buffer in a grid-stride pattern that wraps around.
+// n is a power of two: the wrap is a mask.
+__global__ __launch_bounds__(256) void atomic_probe_kernel(float* dst, size_t n, int iters) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int it = 0; it < iters; ++it) {
+    unsafeAtomicAdd(dst + (i & (n - 1)), 1.0f);
+    i += stride;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,6 +128,14 @@ int spattn_probe_lds(int32_t kind, int32_t blocks, int32_t iters, float* sink, v
     hipLaunchKernelGGL(lds_probe_kernel<0>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
   else
     hipLaunchKernelGGL(lds_probe_kernel<1>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int spattn_probe_atomic(float* dst, size_t n_floats, int32_t blocks, int32_t iters, void* stream) {
+  if (dst == nullptr || n_floats < 256 || (n_floats & (n_floats - 1)) != 0 || blocks < 1 || iters < 1 ||
+      ((uintptr_t)dst & 255u) != 0)
+    return 1;
+  hipLaunchKernelGGL(atomic_probe_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, dst, n_floats, iters);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

@@ -44,7 +44,7 @@ def test_probe_library_exports_every_declared_symbol():
         pytest.skip("libspattn_probe.so not built")
     text = open(os.path.join(ROOT, "include", "spattn_probe.h")).read()
     names = sorted(set(re.findall(r"^\s*int\s+(spattn_probe_\w+)\s*\(", text, flags=re.M)))
-    assert names == ["spattn_probe_lds", "spattn_probe_mfma", "spattn_probe_read"]
+    assert names == ["spattn_probe_atomic", "spattn_probe_lds", "spattn_probe_mfma", "spattn_probe_read"]
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     assert set(names) <= set(re.findall(r"\bT (spattn_probe_\w+)", out))
@@ -58,6 +58,15 @@ def test_probe_library_exports_every_declared_symbol():
     lib.spattn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p]
     assert lib.spattn_probe_read(sink, 15, 1, sink, None) == 1
+    lib.spattn_probe_atomic.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p]
+    aligned = ctypes.c_void_p(256)  # never dereferenced either
+    assert lib.spattn_probe_atomic(None, 256, 1, 1, None) == 1
+    assert lib.spattn_probe_atomic(aligned, 384, 1, 1, None) == 1  # not a power of two
+    assert lib.spattn_probe_atomic(aligned, 128, 1, 1, None) == 1  # below 256
+    assert lib.spattn_probe_atomic(sink, 256, 1, 1, None) == 1     # not 256-byte aligned
+    assert lib.spattn_probe_atomic(aligned, 256, 0, 1, None) == 1
+    assert lib.spattn_probe_atomic(aligned, 256, 1, 0, None) == 1
 
 
 @pytest.mark.parametrize("N", range(1, 65))
