@@ -7,11 +7,16 @@ dK / dV), on B = 8, H = 16, N = 4096, d = 128, bfloat16 inputs resident in HBM.
 
 Prints ONE JSON line.  ``value`` is in-band TFLOP/s of fwd+bwd (14 d FLOP per
 attended pair; the heads together attend N(N+1)/2 pairs per sequence) with
-L2 and the MALL flushed before every timed step (a 512 MiB fill outside the
-events), so no input is served from cache; ``warm`` holds the same steps
-back to back.  Extra keys: per-kernel times and HBM fractions, the roofline
+L2 and the MALL evicted before every timed step (a 512 MiB read outside the
+events: the caches then hold only clean lines of an unrelated buffer), so
+every input comes from HBM and no step pays for writing back another
+buffer's dirty lines; the timed steps follow about 150 ms of untimed steps,
+so that they run at the clocks a continuous run holds.  ``fill_flushed``
+holds the same steps after a 512 MiB fill instead of the read, and
+``cold_start`` the steps of the first run (fill, no settle); ``warm`` holds
+the same steps back to back.  Extra keys: per-kernel times and HBM fractions, the roofline
 of the dominant kernel, the dense-causal kernel of the same library at the
-same shape, the forward of the other workloads (flushed) each next to the
+same shape, the forward of the other workloads (evicted) each next to the
 float64 CPU oracle timed on this host, the page's ablation patterns and the
 shared local window ("variants"), a decode step, the measured MFMA and HBM
 denominators next to the published ones, and the oracle's fwd+bwd time.
@@ -33,6 +38,27 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 FP32_PEAK_TFLOPS = 157.3  # fp32 matrix (and vector) peak
 FLUSH_BYTES = 512 << 20
+SETTLE_MS = 150.0  # untimed steps before the headline, for the clocks to settle
+
+
+class Evictor:
+    """Evicts L2 and the MALL before a timed launch.  "read" (the default)
+    reads a 512 MiB buffer (one reduction), which leaves only clean lines of
+    that buffer in the caches and writes back whatever was dirty there
+    before the timed region starts.  "fill" writes 512 MiB instead, which
+    leaves the caches full of dirty lines whose write-back then falls inside
+    the next timed launch."""
+
+    def __init__(self, dev):
+        import torch
+        self.rd = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.fill = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def __call__(self, how="read"):
+        if how == "fill":
+            self.fill.zero_()
+        else:
+            self.rd.sum()
 
 
 def kernel_source_hash():
@@ -156,16 +182,16 @@ def main():
     grads = tuple(torch.empty_like(q) for _ in range(3))
     ws = torch.empty(max(256, ops.bwd_workspace_bytes(B, H, N, D, torch.bfloat16, torch.bfloat16)),
                      dtype=torch.uint8, device=dev)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    evict = Evictor(dev)
 
     def step(bands=None):
         ops.fwd(q, k, v, bands=bands, out=o, lse=lse)
         ops.bwd(q, k, v, o, lse, do, bands=bands, workspace=ws, out=grads)
 
-    def timed(bands, steps, warmup, flushed):
+    def timed(bands, steps, warmup, flushed, how="read"):
         """`steps` full steps with HIP events around each kernel (recorded on
-        the stream the kernels are launched on).  flushed: a 512 MiB fill
-        before every step, outside the events, evicts L2 and the MALL.
+        the stream the kernels are launched on).  flushed: L2 and the MALL
+        evicted before every step, outside the events (`how`: Evictor).
         Returns the wall time and the per-kernel event times (ms)."""
         for _ in range(warmup):
             step(bands)
@@ -175,7 +201,7 @@ def main():
         t0 = time.perf_counter()
         for e0, e1, e2, e3 in ev:
             if flushed:
-                flush.zero_()
+                evict(how)
             e0.record()
             ops.fwd(q, k, v, bands=bands, out=o, lse=lse)
             e1.record()
@@ -190,7 +216,19 @@ def main():
         times["step"] = [e[0].elapsed_time(e[3]) for e in ev]
         return wall, times
 
-    # ---- headline: flushed steps
+    # ---- the first timed run as it falls, for comparison: fill flush, no settle
+    _, ct = timed(None, args.steps, args.warmup, flushed=True, how="fill")
+    # ---- settle: untimed evicted steps until SETTLE_MS of wall time has passed
+    # (the engine and memory clocks ramp over the first tens of milliseconds
+    # of a burst; a continuous run stays at the settled clocks)
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < SETTLE_MS:
+        for _ in range(10):
+            evict()
+            step()
+        torch.cuda.synchronize()
+        settle_steps += 10
+    # ---- headline: evicted steps
     _, ft = timed(None, args.steps, args.warmup, flushed=True)
     per = {nm: float(np.mean(t)) for nm, t in ft.items()}
     per_median = {nm: float(np.median(t)) for nm, t in ft.items()}
@@ -237,7 +275,7 @@ def main():
         "traffic": measured_traffic(kern_names[dom]),
         "avg_launch_ms": round(per[dom], 4),
         "algorithmic_bytes_per_launch": alg_bytes[dom],
-        "io": "minimal (rows outside every band are not read); caches flushed before each step",
+        "io": "minimal (rows outside every band are not read); caches evicted before each step",
         "achieved_full_io": round(alg_full[dom] / (per[dom] * 1e-3) / 1e9, 1),
         "frac_full_io": round(alg_full[dom] / (per[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_full_io": alg_full[dom],
@@ -258,7 +296,9 @@ def main():
         "data": "synthetic (iid N(0,1), seed 1005)",
         "config": {"workload": "band attention fwd+bwd, bf16, B=8 H=16 N=4096 d=128, BDP bands width 256",
                    "B": B, "H": H, "N": N, "d": D},
-        "timing": "HIP events per step, L2 and MALL flushed (512 MiB fill) before each step, outside the events",
+        "timing": (f"HIP events per step; {SETTLE_MS:.0f} ms of untimed steps, then {args.warmup} warm-up steps, "
+                   "first; L2 and MALL evicted (512 MiB read) before each step, outside the events"),
+        "settle": {"ms": SETTLE_MS, "steps": settle_steps},
         "pct_bf16_mfma_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "inband_pairs": pairs,
         "pairs_per_s": round(pairs / (ms_per_step * 1e-3), 1),
@@ -273,6 +313,16 @@ def main():
         "roofline": roofline,
     }
 
+    def summary(tt):
+        pm = {nm: float(np.mean(t)) for nm, t in tt.items()}
+        return {"ms_per_step": round(pm["step"], 4), "tflops_fwdbwd": round(fl_all / (pm["step"] * 1e-3) / 1e12, 2),
+                "kernel_ms": {kname: round(pm[kname], 4) for kname in kernels}}
+
+    # ---- the same steps after a 512 MiB fill (the caches left dirty), settled clocks
+    _, fft = timed(None, args.steps, 2, flushed=True, how="fill")
+    out["fill_flushed"] = summary(fft)
+    out["cold_start"] = dict(summary(ct), timing=f"the first timed run: {args.warmup} warm-up steps, 512 MiB fill "
+                                                 "before each step, clocks still ramping")
     # ---- the same steps back to back, caches warm
     wall, wt = timed(None, args.steps, 2, flushed=False)
     wper = {nm: float(np.mean(t)) for nm, t in wt.items()}
@@ -293,11 +343,11 @@ def main():
             "ms_per_step": round(dms, 4), "fwd_ms": round(dfwd, 4), "bwd_ms": round(dbwd, 4),
             "speedup_fwdbwd": round(dms / ms_per_step, 3), "speedup_fwd": round(dfwd / fwd_ms, 3),
             "dense_tflops_fwdbwd": round(14 * D * pairs_total(dlo, dhi) / (dms * 1e-3) / 1e12, 2),
-            "timing": "flushed, as the headline",
+            "timing": "evicted, as the headline",
         }
 
     if not args.no_configs:
-        out["configs"] = workload_forwards(dev, flush, with_cpu=not args.no_cpu)
+        out["configs"] = workload_forwards(dev, evict, with_cpu=not args.no_cpu)
 
     if not args.no_variants:
         out["variants"], out["decode"] = variants_and_decode(q, k, v, do, o, lse, ws, grads, lo, hi, args.steps, dev)
@@ -317,9 +367,9 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def workload_forwards(dev, flush, with_cpu, reps=20):
+def workload_forwards(dev, evict, with_cpu, reps=20):
     """Forward of workloads 1-4 on seeded inputs of their shapes: HIP events
-    around each launch with L2 and the MALL flushed before it (median), the
+    around each launch with L2 and the MALL evicted before it (median), the
     warm back-to-back mean, and the whole-workload float64 oracle forward
     timed on the host cores."""
     import numpy as np
@@ -340,7 +390,7 @@ def workload_forwards(dev, flush, with_cpu, reps=20):
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for e0, e1 in ev:
-            flush.zero_()
+            evict()
             e0.record()
             ops.fwd(cq, ck, cv, out=co, lse=cl)
             e1.record()
@@ -364,7 +414,7 @@ def workload_forwards(dev, flush, with_cpu, reps=20):
             "pct_peak": round(100 * tf / peak, 2), "peak_tflops": peak,
             "hbm_frac_minimal_io": round(min_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "hbm_frac_full_io": round(full_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "timing": "median of flushed launches",
+            "timing": "median of evicted launches",
             "warm_fwd_us": round(warm_ms * 1e3, 2),
             "warm_tflops": round(4 * cd * cpairs / (warm_ms * 1e-3) / 1e12, 2),
         }
