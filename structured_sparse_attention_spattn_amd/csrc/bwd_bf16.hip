@@ -123,11 +123,12 @@ __global__ __launch_bounds__(kDqThreads, kDqOcc) void bwd_dq_kernel(BwdArgs p) {
   // key tiles to visit, in order; the ring holds visit v in stage v % kDqStages
   const TileWalk walk = kernel_walk(kDqWalk, i_tile0, N, dset);
   const int n_visit = walk.n;
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   auto issue = [&](int v) {
-    bf16* st = smem + (v % kDqStages) * 2 * kTile;
+    const uint32_t st = smem_lds + (uint32_t)((v % kDqStages) * 2 * kTile * 2);
     const int u = walk.at(v);
     Tile::load(st, kb, u * kDqBK, N, wave, lane);
-    Tile::load(st + kTile, vb, u * kDqBK, N, wave, lane);
+    Tile::load(st + 2 * kTile, vb, u * kDqBK, N, wave, lane);
   };
   // Ring prefill first: its round trip overlaps that of the row loads below
   // (the wait for those covers both).
@@ -407,15 +408,17 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs p) {
   const int voff = shifted && kw == 1 ? 1 : 0;
   if (n_visit > 0) {
     const float sl2 = p.scale_log2;
+    const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    const uint32_t rowv_lds = __builtin_amdgcn_readfirstlane(lds_addr(&rowv[0][0][0]));
     auto issue = [&](int v) {
       const int st = v % kKvStages;
       const int tq = walk.at(v);
-      bf16* t = smem + st * 2 * kTile;
+      const uint32_t t = smem_lds + (uint32_t)(st * 2 * kTile * 2);
       Tile::load(t, qb, tq * kKvQB, N, wave, lane);
-      Tile::load(t + kTile, dob, tq * kKvQB, N, wave, lane);
+      Tile::load(t + 2 * kTile, dob, tq * kKvQB, N, wave, lane);
       const int i = min(tq * kKvQB + (lane & 31), N - 1);
       const float* src = lane < 32 ? nl2b + i : ddb + i;
-      lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr(&rowv[st][wave][0])), src);
+      lds_dma4(rowv_lds + (uint32_t)((st * kWaves + wave) * 2 * kKvQB * 4), src);
     };
     // Ring prefill first: its round trip overlaps that of the row loads below.
 #pragma unroll

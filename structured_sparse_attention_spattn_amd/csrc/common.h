@@ -248,6 +248,10 @@ __device__ __forceinline__ void lds_dma4(uint32_t lds_base, const void* gaddr) {
       : "memory");
 }
 // LDS byte address of a __shared__ location.
+// LDS byte address of p, a pointer into a shared array.  The address-space
+// cast of a generic pointer carries a null check (two scalar instructions),
+// so the kernels take it once per shared array and add stage and piece
+// offsets to it as integers.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   typedef __attribute__((address_space(3))) const char lchar;
   return (uint32_t)(uintptr_t)(lchar*)p;
@@ -265,7 +269,8 @@ struct AsyncTile {
   static constexpr int kPieces = ROWS / kRpi;
   static constexpr int kPer = (kPieces + WAVES - 1) / WAVES;
   static_assert(kPieces * kRpi == ROWS && (kPieces % WAVES == 0 || kPieces < WAVES), "uneven tile split");
-  __device__ __forceinline__ static void load(bf16* tile, const bf16* __restrict__ src, int row0, int N, int wave,
+  // tile: the LDS byte address of the tile's first element
+  __device__ __forceinline__ static void load(uint32_t tile, const bf16* __restrict__ src, int row0, int N, int wave,
                                               int lane) {
     const int lr = lane / (D / 8), p = lane % (D / 8);
 #pragma unroll
@@ -274,7 +279,7 @@ struct AsyncTile {
       const int r = rb + lr;
       const int grow = min(row0 + r, N - 1);
       const int c = p ^ swz<D>(r);
-      lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr(tile + rb * D)), src + (size_t)grow * D + c * 8);
+      lds_dma16(__builtin_amdgcn_readfirstlane(tile + 2 * rb * D), src + (size_t)grow * D + c * 8);
     }
   }
   // The per-lane source offsets of a wave's pieces relative to the tile's
@@ -291,7 +296,7 @@ struct AsyncTile {
       }
     }
   };
-  __device__ __forceinline__ static void load(bf16* tile, const bf16* __restrict__ src, int row0, int N,
+  __device__ __forceinline__ static void load(uint32_t tile, const bf16* __restrict__ src, int row0, int N,
                                               const Offsets& o, int wave, int lane) {
     if (row0 + ROWS > N) {  // the sequence's last tile: clamped rows
       load(tile, src, row0, N, wave, lane);
@@ -301,7 +306,7 @@ struct AsyncTile {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int rb = ((wave + WAVES * i) % kPieces) * kRpi;
-      lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr(tile + rb * D)), base + o.e[i]);
+      lds_dma16(__builtin_amdgcn_readfirstlane(tile + 2 * rb * D), base + o.e[i]);
     }
   }
 };

@@ -213,11 +213,12 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void fwd_bf16_kernel(FwdArgs 
   const int iq = iw0 + c32;
 
   const typename Tile::Offsets toff(wave, lane);
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   auto issue = [&](int v) {
-    bf16* st = smem + (v % STAGES) * 2 * kTile;
+    const uint32_t st = smem_lds + (uint32_t)((v % STAGES) * 2 * kTile * 2);
     const int u = walk.at(v);
     Tile::load(st, kb, u * BKT, N, toff, wave, lane);
-    Tile::load(st + kTile, vb, u * BKT, N, toff, wave, lane);
+    Tile::load(st + 2 * kTile, vb, u * BKT, N, toff, wave, lane);
   };
   // the ring prefill before the Q loads: the round trips overlap
 #pragma unroll
