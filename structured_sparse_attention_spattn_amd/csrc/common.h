@@ -247,7 +247,6 @@ __device__ __forceinline__ void lds_dma4(uint32_t lds_base, const void* gaddr) {
       : "s"(lds_base), "v"(gaddr)
       : "memory");
 }
-// LDS byte address of a __shared__ location.
 // LDS byte address of p, a pointer into a shared array.  The address-space
 // cast of a generic pointer carries a null check (two scalar instructions),
 // so the kernels take it once per shared array and add stage and piece
