@@ -6,9 +6,11 @@ The forward keeps one reference maximum per query row and only moves it
 more than the rescale window; with N(0, 1) inputs that happens almost only on
 a row's first keys.  Here the key rows are scaled along the sequence so that
 the largest score of a row keeps growing from one 32-key half to the next
-(up), shrinks (down), or jumps at a few isolated keys (spike), which drives
-the move path, the correction factors and the rows that start with every key
-masked.  The masked-set softmax being checked is "Sparse Attention, Then and
+(up), shrinks (down), jumps at a few isolated keys (spike), or steps up at
+every 32-key boundary (staircase: most halves then fail the kept reference's
+bound and take the update, at d = 64 after recomputing their scores), which
+drives the move path, the correction factors and the rows that start with
+every key masked.  The masked-set softmax being checked is "Sparse Attention, Then and
 Now" section 1 over each head's band ("Making Every Head Count", Figure 1
 caption).  Bars as elsewhere: float32 within 1e-4 max-abs; bfloat16 within
 2e-2 max-abs and 1e-2 relative L2 (O) and 2e-2 max-abs (LSE); the positions
@@ -72,6 +74,8 @@ def _profile(kind, N):
         f = np.ones(N)
         f[np.arange(37, N, 211)] = 24.0
         return f
+    if kind == "staircase":
+        return 1.0 + 2.0 * (j // 32)
     raise ValueError(kind)
 
 
@@ -87,7 +91,7 @@ def _inputs(B, H, N, d, dtype, seed, kind):
     return inp
 
 
-@pytest.mark.parametrize("kind", ["up", "down", "spike"])
+@pytest.mark.parametrize("kind", ["up", "down", "spike", "staircase"])
 @pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
 @pytest.mark.parametrize("bands", ["bdp", "dense"])
 def test_reference_moves_mid_walk(kind, dtype, d, bands):
